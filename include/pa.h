@@ -1,0 +1,248 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The library implements the data-parallel hot path of PagedAttention as the
+ * explainer pages describe it: the K and V vectors of every cached token live
+ * in fixed-size blocks (16 tokens) scattered through one physical pool and are
+ * reached through a per-sequence block table ("vLLM 核心概念", sections
+ * "核心概念：块（Block）" and "逻辑视图与物理视图分离"); each decode step stores the
+ * new token's K/V and then attends over the whole cached history ("vLLM 核心概念",
+ * section "为什么需要 KV Cache？"; "PagedAttention 实战", section
+ * "Decode：逐 token 生成输出"); forked sequences share blocks and copy a block
+ * only when they diverge ("理解 vLLM PagedAttention", section 六).
+ *
+ * Conventions for every device entry point
+ *   - All tensors are caller-owned device memory (allocated by the caller, e.g.
+ *     with PyTorch); the library never allocates device memory, never frees it
+ *     and never synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL
+ *     means the default stream) and is asynchronous.
+ *   - Scalar arguments and shapes are validated on the host before anything is
+ *     enqueued; a rejected call enqueues nothing.  A launch failure returns
+ *     PA_ERR_HIP.  The detail of the last error on the calling thread is in
+ *     pa_last_error().
+ *   - Device-resident indices (slots, block tables, context lengths, copy
+ *     pairs) cannot be checked on the host.  The kernels check them and never
+ *     touch memory outside the pools because of them: an out-of-range slot or
+ *     copy pair is skipped, and a sequence whose context length or block ids
+ *     are out of range gets NaN in its output rows.
+ *
+ * Cache layout (the pages leave it open; chosen so that every decode load is a
+ * contiguous 16-byte lane load that lands directly in a matrix-core operand):
+ *   K pool: [num_blocks][num_kv_heads][head_dim/8][16][8]
+ *           token t, dim d of (block b, head h) at [b][h][d/8][t][d%8]
+ *   V pool: [num_blocks][num_kv_heads][4][head_dim][4]
+ *           token t, dim d of (block b, head h) at [b][h][t/4][d][t%4]
+ *   One (block, head) tile of K or V is 16*head_dim contiguous elements; one
+ *   physical block of a pool is num_kv_heads*16*head_dim contiguous elements.
+ * Slot encoding: slot = physical_block * 16 + position_in_block.
+ * Query-to-KV head map: query head h reads KV head h / (num_heads/num_kv_heads).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misaligned buffer, bad id   */
+  PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, dtype, group)   */
+  PA_ERR_OUT_OF_BLOCKS = 3, /* block manager: the free list cannot satisfy a call  */
+  PA_ERR_WORKSPACE = 4,     /* workspace smaller than pa_decode_workspace_size()    */
+  PA_ERR_HIP = 5,           /* a HIP runtime call failed                            */
+  PA_ERR_NOT_FOUND = 6      /* block manager: unknown sequence id                   */
+} pa_status;
+
+typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Block size of every pool (tokens per block); the pages' default. */
+#define PA_BLOCK_SIZE 16
+/* Tokens of context one decode workgroup covers before partitions are merged. */
+#define PA_PARTITION_TOKENS 512
+
+/* A KV pool pair.  k_cache and v_cache are device pointers in the layout above,
+ * 16-byte aligned, each num_blocks*num_kv_heads*16*head_dim elements of dtype.
+ * block_size must be 16; head_dim must be 64 or 128. */
+typedef struct pa_cache {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;            /* pa_dtype */
+} pa_cache;
+
+/* ---------------------------------------------------------------------------
+ * pa_cache_write -- slot-mapped store of new tokens' K and V.
+ * Defined by: the current token's key and value are cached so later steps
+ * reuse them ("vLLM 核心概念", section "为什么需要 KV Cache？"), in the block the
+ * table names for that position ("vLLM 核心概念", section "按需分配").
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] packed (no padding
+ *                 between tokens), cache dtype, 16-byte aligned.
+ *   slot_mapping  device, int64[num_tokens]; token i is stored at slot
+ *                 slot_mapping[i].  A negative slot skips the token; a slot at or
+ *                 beyond num_blocks*16 is skipped too.
+ *   num_tokens    >= 0; 0 enqueues nothing.
+ * Two tokens mapped to one slot in the same call: either may win.
+ * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+pa_status pa_cache_write(const pa_cache* cache, const void* k, const void* v,
+                         const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_copy_blocks -- copy-on-write block copy.
+ * Defined by: sequences that share a prompt point at the same physical blocks
+ * and a new block is taken only when later tokens diverge, as in copy-on-write
+ * ("理解 vLLM PagedAttention", section 六; "PagedAttention 实战", section
+ * "PagedAttention 的核心", item 3).  For every pair (src, dst) the whole K block
+ * and V block dst (all heads, all 16 positions) become bit-identical copies of
+ * block src.
+ *   pairs       device, int32[num_pairs][2] = (src, dst).
+ *   pairs_host  optional host copy of the same pairs (may be NULL).  When given,
+ *               it is checked: ids in [0, num_blocks), destinations distinct, no
+ *               destination also a source; a violation returns
+ *               PA_ERR_INVALID_ARG and enqueues nothing.  Without it these
+ *               preconditions are the caller's (the block manager's lists
+ *               always satisfy them); out-of-range pairs are skipped on device.
+ *   num_pairs   >= 0; 0 enqueues nothing.
+ * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs,
+                         const int32_t* pairs_host, int32_t num_pairs, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_workspace_size -- bytes of workspace pa_decode needs.
+ * Sequences longer than PA_PARTITION_TOKENS are split into partitions whose
+ * partial softmax states (max, sum, unnormalised output; float32) are kept in
+ * the workspace and merged by log-sum-exp.  Returns 0 when max_context_len <=
+ * PA_PARTITION_TOKENS (no merge) and for invalid arguments.
+ * ------------------------------------------------------------------------- */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode -- single-query paged decode attention (attention pass, then merge).
+ * Defined by: each decode step reads the cached K/V of all history tokens
+ * ("PagedAttention 实战", section "Decode：逐 token 生成输出"; "理解 vLLM
+ * PagedAttention", section 七) through the block table ("vLLM 核心概念", section
+ * "逻辑视图与物理视图分离").  For sequence b with context n_b = context_lens[b]
+ * and query head h (KV head g = h / (num_heads/num_kv_heads)):
+ *     s_t = scale * <q[b,h,:], K_b[t,g,:]>,  t = 0 .. n_b-1
+ *     out[b,h,:] = sum_t softmax(s)_t * V_b[t,g,:]
+ * where K_b[t] is token t % 16 of block block_tables[b][t / 16].  Scores,
+ * softmax and accumulation are float32; out is rounded to the cache dtype
+ * (round to nearest even).  The reduction order depends only on logical token
+ * positions, so the result is bit-identical for any placement of the blocks.
+ *   q, out              device, [num_seqs][num_heads][head_dim], cache dtype,
+ *                       16-byte aligned.
+ *   block_tables        device, int32[num_seqs][max_blocks_per_seq].
+ *   context_lens        device, int32[num_seqs], each in [1, max_context_len].
+ *   max_context_len     host bound on every context length, <= 16*max_blocks_per_seq.
+ *   num_heads           a multiple of num_kv_heads, at most 16 per KV head.
+ *   workspace           device, >= pa_decode_workspace_size(...) bytes (may be
+ *                       NULL when that size is 0).
+ * A sequence with context length outside [1, max_context_len] or a block id
+ * outside [0, num_blocks) gets NaN in its output rows.
+ * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int32_t num_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of pa_decode, for callers that time or schedule them apart.
+ * pa_decode_attention is the attention pass: one workgroup per (sequence, KV
+ * head, 512-token partition) walks its blocks with an online softmax.  For a
+ * sequence with one partition it writes out[] itself; otherwise it writes the
+ * partition's float32 state (max in log2 units of the scaled score, sum,
+ * unnormalised output) to the workspace.  pa_decode_merge combines those states
+ * by log-sum-exp ("PagedAttention 实战", section "2026 年的新变化": sequence split)
+ * and writes out[] for every sequence with more than one partition.  Same
+ * arguments and errors as pa_decode; pa_decode_merge is a no-op when
+ * max_context_len <= PA_PARTITION_TOKENS. */
+pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_seqs,
+                              int32_t num_heads, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t max_context_len, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_heads,
+                          const int32_t* context_lens, int32_t max_context_len, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Status name; never NULL. */
+const char* pa_status_string(pa_status status);
+/* Detail of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ===========================================================================
+ * Host block manager (pure host code, no device calls; not thread-safe).
+ * Defined by: blocks come from one global pool, a sequence appends blocks as it
+ * grows and returns them when it ends, and several sequences may point logical
+ * blocks at one physical block ("理解 vLLM PagedAttention", section 三); a block
+ * is taken exactly when the last one is full, the first token included
+ * ("vLLM 核心概念", section "按需分配"; "理解 vLLM PagedAttention", section 四);
+ * forked sequences share blocks and copy one only on divergence (same page,
+ * section 六).  Policies the pages leave open:
+ *   - the free list is a LIFO stack that starts as `free_order` (NULL = 0,1,2..)
+ *     and pops free_order[0] first; freed blocks are pushed on top;
+ *   - freeing a sequence drops one reference per block, last logical block
+ *     first, pushing each block whose count reaches zero;
+ *   - an append into a shared (refcount > 1), partially filled last block
+ *     takes a fresh block and reports (old, new) as a copy-on-write pair; the
+ *     old block loses a reference; the last sharer writes in place;
+ *   - a failing append or batch changes nothing.
+ * ======================================================================== */
+typedef struct pa_bm pa_bm;
+
+typedef struct pa_bm_stats {
+  int64_t num_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;      /* refcount > 0 */
+  int64_t shared_blocks;    /* refcount > 1 */
+  int64_t allocated_slots;  /* used_blocks * 16 */
+  int64_t occupied_slots;   /* per used block, the most tokens any sharer keeps in it */
+  double waste;             /* 1 - occupied/allocated (0 when nothing is allocated) */
+} pa_bm_stats;
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id);
+/* Reserve the slot of the next token of one sequence.  cow_src and cow_dst receive
+ * -1 unless this append copied a shared block. */
+pa_status pa_bm_append(pa_bm* bm, int64_t seq_id, int64_t* slot, int32_t* cow_src,
+                       int32_t* cow_dst);
+/* One token for each of n distinct sequences, in order, all or nothing.
+ * slots: int64[n].  cow_pairs: int32[cow_cap][2]; *n_cow receives the count
+ * (at most n; cow_cap >= n guarantees room, else PA_ERR_INVALID_ARG). */
+pa_status pa_bm_append_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slots,
+                             int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
+/* count tokens appended to one sequence (a prefill), each one an append;
+ * all or nothing.  slots: int64[count]; cow pairs as above (at most count). */
+pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t count, int64_t* slots,
+                              int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
+pa_status pa_bm_seq_len(const pa_bm* bm, int64_t seq_id, int64_t* len);
+/* Copy a sequence's table (logical order) to out[0..cap); *n = its length. */
+pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap,
+                            int32_t* n);
+/* Pack n sequences' tables into tables[n][max_blocks] (unused entries -1) and
+ * their lengths into ctx_lens[n]. */
+pa_status pa_bm_pack(const pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* tables,
+                     int32_t max_blocks, int32_t* ctx_lens);
+pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* out);
+/* Free blocks, next-to-pop first, into out[0..cap); *n = how many are free. */
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -117,7 +117,16 @@ class RefBlockManager:
         return slots, cows
 
     def append_tokens(self, sid: int, count: int) -> Tuple[List[int], List[Tuple[int, int]]]:
-        """``count`` tokens to one sequence (a prefill); each token is one append."""
+        """``count`` tokens to one sequence (a prefill), each token one append; all-or-nothing."""
+        if sid not in self._tables:
+            raise KeyError(f"no sequence {sid}")
+        n = self._lens[sid]
+        need = 0
+        if count and n % self.block_size and self._ref[self._tables[sid][-1]] > 1:
+            need += 1                       # the copy of the shared, partly filled last block
+        need += blocks_needed(n + count, self.block_size) - blocks_needed(n, self.block_size)
+        if need > len(self._free):
+            raise OutOfBlocks(f"{count} tokens need {need} blocks, {len(self._free)} free")
         slots, cows = [], []
         for _ in range(count):
             s, c = self.append(sid)

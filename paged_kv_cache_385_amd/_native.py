@@ -1,0 +1,109 @@
+"""ctypes binding of libpa.so (argument marshalling only).
+
+The library is built in-tree by ``paged_kv_cache_385_amd.build``.  Loading
+fails loudly when it is missing: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_OUT_OF_BLOCKS = 3
+PA_ERR_WORKSPACE = 4
+PA_ERR_HIP = 5
+PA_ERR_NOT_FOUND = 6
+PA_F16 = 0
+PA_BF16 = 1
+BLOCK_SIZE = 16
+PARTITION_TOKENS = 512
+
+
+class PaCache(C.Structure):
+    _fields_ = [("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("num_blocks", C.c_int32),
+                ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("dtype", C.c_int32)]
+
+
+class PaBmStats(C.Structure):
+    _fields_ = [("num_blocks", C.c_int64), ("free_blocks", C.c_int64), ("used_blocks", C.c_int64),
+                ("shared_blocks", C.c_int64), ("allocated_slots", C.c_int64),
+                ("occupied_slots", C.c_int64), ("waste", C.c_double)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {detail or status}")
+
+
+class OutOfBlocks(PaError):
+    pass
+
+
+_P = C.c_void_p
+_I32 = C.c_int32
+_I64 = C.c_int64
+_PI32 = C.POINTER(C.c_int32)
+_PI64 = C.POINTER(C.c_int64)
+
+# name -> (restype, argtypes); every symbol pa.h declares
+SIGNATURES = {
+    "pa_cache_write": (C.c_int, [C.POINTER(PaCache), _P, _P, _P, _I32, _P]),
+    "pa_copy_blocks": (C.c_int, [C.POINTER(PaCache), _P, _P, _I32, _P]),
+    "pa_decode_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32]),
+    "pa_decode": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32, C.c_float, _P,
+                            _P, C.c_size_t, _P]),
+    "pa_decode_attention": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,
+                                      C.c_float, _P, _P, C.c_size_t, _P]),
+    "pa_decode_merge": (C.c_int, [C.POINTER(PaCache), _I32, _I32, _P, _I32, _P, _P, C.c_size_t,
+                                  _P]),
+    "pa_status_string": (C.c_char_p, [C.c_int]),
+    "pa_last_error": (C.c_char_p, []),
+    "pa_bm_create": (C.c_int, [_I32, _I32, _P, C.POINTER(C.c_void_p)]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_add_seq": (C.c_int, [_P, _I64]),
+    "pa_bm_append": (C.c_int, [_P, _I64, _PI64, _PI32, _PI32]),
+    "pa_bm_append_batch": (C.c_int, [_P, _I32, _P, _P, _P, _I32, _PI32]),
+    "pa_bm_append_tokens": (C.c_int, [_P, _I64, _I32, _P, _P, _I32, _PI32]),
+    "pa_bm_fork": (C.c_int, [_P, _I64, _I64]),
+    "pa_bm_free_seq": (C.c_int, [_P, _I64]),
+    "pa_bm_seq_len": (C.c_int, [_P, _I64, _PI64]),
+    "pa_bm_block_table": (C.c_int, [_P, _I64, _P, _I32, _PI32]),
+    "pa_bm_pack": (C.c_int, [_P, _I32, _P, _P, _I32, _P]),
+    "pa_bm_refcount": (C.c_int, [_P, _I32, _PI32]),
+    "pa_bm_free_list": (C.c_int, [_P, _P, _I32, _PI32]),
+    "pa_bm_stats_get": (C.c_int, [_P, C.POINTER(PaBmStats)]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library; raises ImportError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m paged_kv_cache_385_amd.build` (no fallback exists)")
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int, fn: str) -> None:
+    if status == PA_OK:
+        return
+    detail = lib().pa_last_error().decode()
+    name = lib().pa_status_string(status).decode()
+    cls = OutOfBlocks if status == PA_ERR_OUT_OF_BLOCKS else PaError
+    raise cls(status, fn, f"{name}: {detail}")

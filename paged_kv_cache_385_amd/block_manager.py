@@ -1,0 +1,118 @@
+"""Python handle on the native host block manager (pa_bm_* in libpa.so)."""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _native as N
+
+
+def _ptr(a: np.ndarray) -> C.c_void_p:
+    return C.c_void_p(a.ctypes.data)
+
+
+class BlockManager:
+    """Free list, reference counts, fork and copy-on-write; see pa.h for the policies."""
+
+    def __init__(self, num_blocks: int, block_size: int = N.BLOCK_SIZE,
+                 free_order: Optional[Sequence[int]] = None):
+        self._lib = N.lib()
+        h = C.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+        N.check(self._lib.pa_bm_create(num_blocks, block_size,
+                                       None if order is None else _ptr(order), C.byref(h)),
+                "pa_bm_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pa_bm_destroy(h)
+            self._h = None
+
+    def add_seq(self, sid: int) -> None:
+        N.check(self._lib.pa_bm_add_seq(self._h, sid), "pa_bm_add_seq")
+
+    def append(self, sid: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        slot = C.c_int64()
+        s, d = C.c_int32(), C.c_int32()
+        N.check(self._lib.pa_bm_append(self._h, sid, C.byref(slot), C.byref(s), C.byref(d)),
+                "pa_bm_append")
+        return slot.value, ((s.value, d.value) if s.value >= 0 else None)
+
+    def append_batch(self, sids: Iterable[int], slots_out: Optional[np.ndarray] = None
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+        """One token for each sequence.  Returns (slots int64[n], cow pairs int32[k, 2])."""
+        ids = np.ascontiguousarray(np.asarray(list(sids) if not isinstance(sids, np.ndarray)
+                                              else sids, dtype=np.int64))
+        n = ids.shape[0]
+        slots = slots_out if slots_out is not None else np.empty(n, dtype=np.int64)
+        cows = np.empty((max(n, 1), 2), dtype=np.int32)
+        nc = C.c_int32()
+        N.check(self._lib.pa_bm_append_batch(self._h, n, _ptr(ids), _ptr(slots), _ptr(cows),
+                                             max(n, 1), C.byref(nc)), "pa_bm_append_batch")
+        return slots, cows[:nc.value]
+
+    def append_tokens(self, sid: int, count: int) -> Tuple[np.ndarray, np.ndarray]:
+        slots = np.empty(max(count, 1), dtype=np.int64)
+        cows = np.empty((max(count, 1), 2), dtype=np.int32)
+        nc = C.c_int32()
+        N.check(self._lib.pa_bm_append_tokens(self._h, sid, count, _ptr(slots), _ptr(cows),
+                                              max(count, 1), C.byref(nc)), "pa_bm_append_tokens")
+        return slots[:count], cows[:nc.value]
+
+    def fork(self, parent: int, child: int) -> None:
+        N.check(self._lib.pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def free_seq(self, sid: int) -> None:
+        N.check(self._lib.pa_bm_free_seq(self._h, sid), "pa_bm_free_seq")
+
+    def seq_len(self, sid: int) -> int:
+        n = C.c_int64()
+        N.check(self._lib.pa_bm_seq_len(self._h, sid, C.byref(n)), "pa_bm_seq_len")
+        return n.value
+
+    def block_table(self, sid: int) -> List[int]:
+        n = C.c_int32()
+        N.check(self._lib.pa_bm_block_table(self._h, sid, None, 0, C.byref(n)), "pa_bm_block_table")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        N.check(self._lib.pa_bm_block_table(self._h, sid, _ptr(out), n.value, C.byref(n)),
+                "pa_bm_block_table")
+        return out[:n.value].tolist()
+
+    def pack(self, sids: Sequence[int], max_blocks: int, tables_out: Optional[np.ndarray] = None,
+             ctx_out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Block tables int32[n, max_blocks] (unused -1) and context lengths int32[n]."""
+        ids = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
+        n = ids.shape[0]
+        tables = tables_out if tables_out is not None else np.empty((n, max_blocks), dtype=np.int32)
+        ctx = ctx_out if ctx_out is not None else np.empty(n, dtype=np.int32)
+        N.check(self._lib.pa_bm_pack(self._h, n, _ptr(ids), _ptr(tables), max_blocks, _ptr(ctx)),
+                "pa_bm_pack")
+        return tables, ctx
+
+    def refcount(self, blk: int) -> int:
+        r = C.c_int32()
+        N.check(self._lib.pa_bm_refcount(self._h, blk, C.byref(r)), "pa_bm_refcount")
+        return r.value
+
+    def free_list(self) -> List[int]:
+        n = C.c_int32()
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        N.check(self._lib.pa_bm_free_list(self._h, _ptr(out), self.num_blocks, C.byref(n)),
+                "pa_bm_free_list")
+        return out[:n.value].tolist()
+
+    def stats(self) -> dict:
+        st = N.PaBmStats()
+        N.check(self._lib.pa_bm_stats_get(self._h, C.byref(st)), "pa_bm_stats_get")
+        return {f: getattr(st, f) for f, _ in N.PaBmStats._fields_}

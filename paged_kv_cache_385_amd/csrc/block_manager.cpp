@@ -1,0 +1,365 @@
+// Host block manager: free list, reference counts, fork and copy-on-write.
+//
+// Follows "理解 vLLM PagedAttention" sections 三 (blocks taken from one global
+// pool, appended as a sequence grows, returned when it ends, shared by pointing
+// logical blocks of several sequences at one physical block), 四 (allocation on
+// demand; waste confined to the last block) and 六 (sharing with copy-on-write
+// on divergence), and "vLLM 核心概念" sections "按需分配" and "内存共享".
+// The policies the pages leave open are stated in pa.h next to the pa_bm_*
+// declarations.  Pure host code: no device calls.
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Seq {
+  std::vector<int32_t> table;  // logical block j -> physical block
+  int64_t len = 0;             // tokens stored
+};
+
+}  // namespace
+
+struct pa_bm {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // top = back()
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int32_t, int32_t> scratch_drop;  // reused by batch planning
+
+  Seq* find(int64_t id) {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+  const Seq* find(int64_t id) const {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+  int32_t pop_free() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    ref[b] = 1;
+    return b;
+  }
+  // One append whose block needs were already checked against the free list.
+  int64_t append_one(Seq& s, int32_t* cow_src, int32_t* cow_dst) {
+    const int32_t off = static_cast<int32_t>(s.len % block_size);
+    int32_t blk;
+    *cow_src = -1;
+    *cow_dst = -1;
+    if (off == 0) {
+      blk = pop_free();
+      s.table.push_back(blk);
+    } else {
+      const int32_t last = s.table.back();
+      if (ref[last] > 1) {
+        blk = pop_free();
+        ref[last] -= 1;
+        s.table.back() = blk;
+        *cow_src = last;
+        *cow_dst = blk;
+      } else {
+        blk = last;
+      }
+    }
+    s.len += 1;
+    return static_cast<int64_t>(blk) * block_size + off;
+  }
+};
+
+namespace pa {
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_bm** out) {
+  if (!out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks %d", num_blocks);
+  if (block_size != PA_BLOCK_SIZE)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only 16)", block_size);
+  pa_bm* bm = new (std::nothrow) pa_bm;
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->ref.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: free_order is not a permutation (entry %d = %d)", i, b);
+      }
+      seen[b] = 1;
+      bm->free_stack[num_blocks - 1 - i] = b;  // free_order[0] on top
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[num_blocks - 1 - i] = i;
+  }
+  *out = bm;
+  return PA_OK;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: bm is NULL");
+  if (bm->find(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
+  bm->seqs.emplace(seq_id, Seq{});
+  return PA_OK;
+}
+
+pa_status pa_bm_append_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slots,
+                             int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow) {
+  if (!bm || n < 0 || (n > 0 && (!seq_ids || !slots)) || !n_cow)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: bad arguments");
+  if (cow_cap < n || (n > 0 && !cow_pairs))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: cow_cap %d < n %d", cow_cap, n);
+  *n_cow = 0;
+  std::vector<Seq*> ptr(n);
+  for (int32_t i = 0; i < n; ++i) {
+    ptr[i] = bm->find(seq_ids[i]);
+    if (!ptr[i]) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_append_batch: no sequence %lld", (long long)seq_ids[i]);
+  }
+  // distinct ids
+  {
+    std::vector<int64_t> ids(seq_ids, seq_ids + n);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end())
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: a sequence appears twice");
+  }
+  // plan: count blocks taken, with the reference drops earlier copies make
+  auto& drop = bm->scratch_drop;
+  drop.clear();
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = *ptr[i];
+    if (s.len % bm->block_size == 0) {
+      ++need;
+    } else {
+      const int32_t last = s.table.back();
+      auto it = drop.find(last);
+      const int32_t pending = it == drop.end() ? 0 : it->second;
+      if (bm->ref[last] - pending > 1) {
+        ++need;
+        drop[last] = pending + 1;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_batch: needs %lld blocks, %zu free",
+                    (long long)need, bm->free_stack.size());
+  int32_t nc = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src, dst;
+    slots[i] = bm->append_one(*ptr[i], &src, &dst);
+    if (src >= 0) {
+      cow_pairs[2 * nc] = src;
+      cow_pairs[2 * nc + 1] = dst;
+      ++nc;
+    }
+  }
+  *n_cow = nc;
+  return PA_OK;
+}
+
+pa_status pa_bm_append(pa_bm* bm, int64_t seq_id, int64_t* slot, int32_t* cow_src,
+                       int32_t* cow_dst) {
+  if (!slot || !cow_src || !cow_dst) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append: NULL output");
+  int32_t pair[2] = {-1, -1};
+  int32_t nc = 0;
+  pa_status st = pa_bm_append_batch(bm, 1, &seq_id, slot, pair, 1, &nc);
+  if (st != PA_OK) return st;
+  *cow_src = nc ? pair[0] : -1;
+  *cow_dst = nc ? pair[1] : -1;
+  return PA_OK;
+}
+
+pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t count, int64_t* slots,
+                              int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow) {
+  if (!bm || count < 0 || (count > 0 && !slots) || !n_cow)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: bad arguments");
+  if (cow_cap < count || (count > 0 && !cow_pairs))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: cow_cap %d < count %d", cow_cap, count);
+  *n_cow = 0;
+  Seq* s = bm->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_append_tokens: no sequence %lld", (long long)seq_id);
+  if (count == 0) return PA_OK;
+  // blocks taken: a copy of a shared partial last block (first token only),
+  // plus one block per block boundary crossed
+  const int64_t len = s->len;
+  const int64_t bs = bm->block_size;
+  int64_t need = 0;
+  if (len % bs != 0 && bm->ref[s->table.back()] > 1) need += 1;
+  const int64_t first_new_block = (len + bs - 1) / bs;       // blocks held now
+  const int64_t blocks_after = (len + count + bs - 1) / bs;
+  need += blocks_after - first_new_block;
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_tokens: needs %lld blocks, %zu free",
+                    (long long)need, bm->free_stack.size());
+  int32_t nc = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    int32_t src, dst;
+    slots[i] = bm->append_one(*s, &src, &dst);
+    if (src >= 0) {
+      cow_pairs[2 * nc] = src;
+      cow_pairs[2 * nc + 1] = dst;
+      ++nc;
+    }
+  }
+  *n_cow = nc;
+  return PA_OK;
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: bm is NULL");
+  const Seq* p = bm->find(parent);
+  if (!p) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_fork: no sequence %lld", (long long)parent);
+  if (bm->find(child)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: sequence %lld exists", (long long)child);
+  Seq c = *p;
+  for (int32_t b : c.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: bm is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_free_seq: no sequence %lld", (long long)seq_id);
+  const std::vector<int32_t>& t = it->second.table;
+  for (auto r = t.rbegin(); r != t.rend(); ++r) {
+    if (--bm->ref[*r] == 0) bm->free_stack.push_back(*r);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_seq_len(const pa_bm* bm, int64_t seq_id, int64_t* len) {
+  if (!bm || !len) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_seq_len: NULL argument");
+  const Seq* s = bm->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_seq_len: no sequence %lld", (long long)seq_id);
+  *len = s->len;
+  return PA_OK;
+}
+
+pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap,
+                            int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_block_table: bad arguments");
+  const Seq* s = bm->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_block_table: no sequence %lld", (long long)seq_id);
+  const int32_t m = static_cast<int32_t>(s->table.size());
+  std::memcpy(out, s->table.data(), sizeof(int32_t) * std::min(m, cap));
+  *n = m;
+  return PA_OK;
+}
+
+pa_status pa_bm_pack(const pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* tables,
+                     int32_t max_blocks, int32_t* ctx_lens) {
+  if (!bm || n < 0 || max_blocks <= 0 || (n > 0 && (!seq_ids || !tables || !ctx_lens)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_pack: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = bm->find(seq_ids[i]);
+    if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_pack: no sequence %lld", (long long)seq_ids[i]);
+    const int32_t m = static_cast<int32_t>(s->table.size());
+    if (m > max_blocks || s->len > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_pack: sequence %lld holds %d blocks > %d",
+                      (long long)seq_ids[i], m, max_blocks);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = bm->find(seq_ids[i]);
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    const int32_t m = static_cast<int32_t>(s->table.size());
+    std::memcpy(row, s->table.data(), sizeof(int32_t) * m);
+    std::fill(row + m, row + max_blocks, -1);
+    ctx_lens[i] = static_cast<int32_t>(s->len);
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* out) {
+  if (!bm || !out || block < 0 || block >= bm->num_blocks)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: bad arguments");
+  *out = bm->ref[block];
+  return PA_OK;
+}
+
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_list: bad arguments");
+  const int32_t m = static_cast<int32_t>(bm->free_stack.size());
+  const int32_t k = std::min(m, cap);
+  for (int32_t i = 0; i < k; ++i) out[i] = bm->free_stack[m - 1 - i];
+  *n = m;
+  return PA_OK;
+}
+
+pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_stats_get: NULL argument");
+  std::vector<int32_t> occupied(bm->num_blocks, 0);
+  const int64_t bs = bm->block_size;
+  for (const auto& kv : bm->seqs) {
+    const Seq& s = kv.second;
+    for (size_t j = 0; j < s.table.size(); ++j) {
+      const int64_t fill = std::min<int64_t>(bs, s.len - static_cast<int64_t>(j) * bs);
+      int32_t& o = occupied[s.table[j]];
+      o = std::max<int32_t>(o, static_cast<int32_t>(fill));
+    }
+  }
+  int64_t used = 0, shared = 0, occ = 0;
+  for (int32_t b = 0; b < bm->num_blocks; ++b) {
+    used += bm->ref[b] > 0;
+    shared += bm->ref[b] > 1;
+    occ += occupied[b];
+  }
+  out->num_blocks = bm->num_blocks;
+  out->free_blocks = static_cast<int64_t>(bm->free_stack.size());
+  out->used_blocks = used;
+  out->shared_blocks = shared;
+  out->allocated_slots = used * bs;
+  out->occupied_slots = occ;
+  out->waste = used ? 1.0 - static_cast<double>(occ) / static_cast<double>(used * bs) : 0.0;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,679 @@
+// Paged KV-cache kernels for gfx950 (CDNA4) and their C-ABI entry points.
+//
+//   cache_write_kernel   slot-mapped store of new tokens' K/V ("vLLM 核心概念",
+//                        sections "为什么需要 KV Cache？" and "按需分配")
+//   copy_blocks_kernel   copy-on-write block copy ("理解 vLLM PagedAttention", section 六)
+//   decode_attn_kernel   single-query attention over a block-paged context
+//                        ("PagedAttention 实战", section "Decode：逐 token 生成输出";
+//                        "vLLM 核心概念", section "逻辑视图与物理视图分离")
+//   decode_merge_kernel  log-sum-exp merge of context partitions ("PagedAttention 实战",
+//                        section "2026 年的新变化": sequence split)
+//
+// Layout of the pools (see pa.h): K [NB][Hkv][D/8][16][8], V [NB][Hkv][4][D][4].
+// With that layout one (block, head) tile is 16*D contiguous elements and each
+// wave reads it with one 16-byte load per lane per 1 KiB; every loaded vector is
+// already a matrix-core operand:
+//   q.K^T : v_mfma_f32_16x16x32_{f16,bf16}, A = K tile (16 tokens x 32 dims),
+//           B = q^T (32 dims x 16 query heads of one KV-head group, zero-padded),
+//           C = S^T (16 tokens x 16 heads); lane l holds tokens 4(l/16)..+3 of head l%16.
+//   P.V   : v_mfma_f32_16x16x16_{f16,bf16}, A = V^T (16 dims x 16 tokens),
+//           B = P^T (16 tokens x 16 heads) -- exactly the S^T register layout, so the
+//           softmax output feeds the second product without any data movement,
+//           C = out^T; lane l accumulates head l%16, so the online-softmax rescale
+//           is lane-local.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = PA_BLOCK_SIZE;                       // tokens per block
+constexpr int kPartTokens = PA_PARTITION_TOKENS;            // tokens per workgroup
+constexpr int kPartBlocks = kPartTokens / kBlock;           // 32
+constexpr int kWaves = 4;                                   // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxParts = 1024;                             // merge LDS bound
+
+// ---- element traits --------------------------------------------------------------
+struct F16 {
+  using T = _Float16;
+  static constexpr uint16_t kNaN = 0x7E00;
+  __device__ static f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 mfma_pv(u16x4 a, u16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+  __device__ static float to_float(uint16_t x) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, x));
+  }
+};
+
+struct BF16 {
+  using T = __bf16;
+  static constexpr uint16_t kNaN = 0x7FC0;
+  __device__ static f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 mfma_pv(u16x4 a, u16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  __device__ static uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+  __device__ static float to_float(uint16_t x) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
+  }
+};
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cache write -----------------------------------------------------------------
+// One thread per (token, KV head, 8-dim chunk): a 16-byte K store, eight 2-byte V stores.
+template <int D>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, int32_t num_tokens, int32_t hkv, int64_t num_slots) {
+  constexpr int kChunks = D / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = static_cast<int64_t>(hkv) * kChunks;
+  if (idx >= static_cast<int64_t>(num_tokens) * per_token) return;
+  const int64_t t = idx / per_token;
+  const int32_t rem = static_cast<int32_t>(idx - t * per_token);
+  const int32_t h = rem / kChunks;
+  const int32_t c = rem - h * kChunks;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int32_t off = static_cast<int32_t>(slot & 15);
+  const int64_t src = (t * hkv + h) * D + 8 * c;
+  const int64_t tile = (blk * hkv + h) * (kBlock * D);
+  store16(k_cache + tile + (static_cast<int64_t>(c) * kBlock + off) * 8, load16(k + src));
+  const u16x8 vv = __builtin_bit_cast(u16x8, load16(v + src));
+  uint16_t* vdst = v_cache + tile + (static_cast<int64_t>(off >> 2) * D + 8 * c) * 4 + (off & 3);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vdst[4 * i] = vv[i];
+}
+
+// ---- block copy ------------------------------------------------------------------
+// grid.y = pair, grid.x strides over the 16-byte vectors of one block in both pools.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    const int32_t* __restrict__ pairs, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+    int64_t vecs_per_block, int32_t num_blocks) {
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const u32x4* ks = k_cache + src * vecs_per_block;
+  const u32x4* vs = v_cache + src * vecs_per_block;
+  u32x4* kd = k_cache + dst * vecs_per_block;
+  u32x4* vd = v_cache + dst * vecs_per_block;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs_per_block;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const u32x4 a = ks[i];
+    const u32x4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+// ---- decode: attention pass --------------------------------------------------------
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  float2* ws_ml;     // [B][H][P] (max in log2 units, sum)
+  float* ws_acc;     // [B][H][P][D] unnormalised output
+  int32_t num_seqs, num_heads, num_kv_heads, group;
+  int32_t max_blocks, max_ctx, num_blocks, max_parts;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Workgroup id -> logical work index.  Consecutive workgroup ids go round-robin
+// to the 8 XCDs; this permutation gives each XCD eight consecutive logical
+// indices, i.e. eight consecutive sequences of one (KV head, partition), so
+// sequences that alias prefix blocks meet in one XCD's L2.
+__device__ __forceinline__ int32_t xcd_swizzle(int32_t wg, int32_t n) {
+  const int32_t full = n & ~63;
+  if (wg >= full) return wg;
+  return (wg & ~63) | ((wg & 7) << 3) | ((wg >> 3) & 7);
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
+  constexpr int KK = D / 32;        // 16x16x32 steps for q.K^T; also 16-byte V loads per lane
+  constexpr int MT = D / 16;        // output tiles of 16 dims
+  constexpr int kLdsStride = D + 4; // floats per head row in LDS (staggers banks)
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][16 * kLdsStride];
+
+  const int32_t lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int32_t b = lin % a.num_seqs;
+  const int32_t rest = lin / a.num_seqs;
+  const int32_t kvh = rest % a.num_kv_heads;
+  const int32_t p = rest / a.num_kv_heads;
+  const int32_t G = a.group;
+
+  const int32_t ctx = a.ctx_lens[b];
+  const bool bad_ctx = ctx < 1 || ctx > a.max_ctx;
+  const int32_t nparts = bad_ctx ? 1 : (ctx + kPartTokens - 1) / kPartTokens;
+  if (p >= nparts) return;
+
+  const int32_t tid = threadIdx.x;
+  const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t lane = tid & 63;
+  const int32_t n = lane & 15;       // query head within the group (MFMA column)
+  const int32_t g4 = lane >> 4;      // token quad within a block (MFMA row group)
+  const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G) * D;
+
+  if (bad_ctx) {
+    for (int32_t i = tid; i < G * D; i += kThreads) a.out[q_row0 + i] = E::kNaN;
+    return;
+  }
+
+  // q fragments: B operand of q.K^T, dims 32kk + 8*g4 .. +7 of head n (zero for n >= G)
+  u32x4 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = (n < G) ? load16(a.q + q_row0 + static_cast<int64_t>(n) * D + 32 * kk + 8 * g4)
+                     : u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  const int32_t j0 = p * kPartBlocks + w;
+  const int32_t jend = min(nblk, (p + 1) * kPartBlocks);
+  const int32_t nw = j0 < jend ? (jend - j0 + kWaves - 1) / kWaves : 0;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  bool bad_blk = false;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 kb[2][KK], vb[2][KK];
+
+  auto load_block = [&](int buf, int32_t j) {
+    int32_t phys = bt[j];
+    if (phys < 0 || phys >= a.num_blocks) {
+      bad_blk = true;
+      phys = 0;
+    }
+    const uint16_t* kt = a.k_cache + phys * blk_stride + head_off;
+    const uint16_t* vt = a.v_cache + phys * blk_stride + head_off;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load16(kt + (kk * 64 + lane) * 8);
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2) vb[buf][j2] = load16(vt + ((g4 * D) + 32 * j2 + 2 * n) * 4);
+  };
+
+  auto compute_block = [&](int buf, int32_t j) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
+    const int32_t valid = ctx - j * kBlock;   // >= 1; tokens of this block inside the context
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = s[r] * a.scale_log2;
+      if (valid < kBlock && 4 * g4 + r >= valid) sv[r] = -INFINITY;
+    }
+    float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(m_run, bmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    u16x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = E::from_float(fast_exp2(sv[r] - m_new));
+      psum += E::to_float(pb[r]);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] *= alpha;
+    if (valid < kBlock) {
+      // positions past the context may hold anything (NaN included): zero their V
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2) {
+        u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (4 * g4 + (e & 3) >= valid) vv[e] = 0;
+        vb[buf][j2] = __builtin_bit_cast(u32x4, vv);
+      }
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2) {
+      const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+      const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
+      const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
+      acc[2 * j2] = E::mfma_pv(lo, pb, acc[2 * j2]);
+      acc[2 * j2 + 1] = E::mfma_pv(hi, pb, acc[2 * j2 + 1]);
+    }
+  };
+
+  if (nw > 0) {
+    load_block(0, j0);
+    for (int32_t i = 0; i < nw; i += 2) {
+      const int32_t ja = j0 + i * kWaves;
+      if (i + 1 < nw) load_block(1, ja + kWaves);
+      compute_block(0, ja);
+      if (i + 1 >= nw) break;
+      if (i + 2 < nw) load_block(0, ja + 2 * kWaves);
+      compute_block(1, ja + kWaves);
+    }
+  }
+
+  // ---- combine the four waves of the workgroup in LDS ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (g4 == 0) {
+    s_m[w][n] = m_run;
+    s_l[w][n] = l_run;
+  }
+  // any wave that met an out-of-range block id poisons the whole result
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (bad_blk) s_bad = 1;
+  float mw[kWaves];
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    mw[u] = s_m[u][n];
+    M = fmaxf(M, mw[u]);
+  }
+  const float wscale = fast_exp2(m_run - M);   // 0 for a wave that saw no block
+  if (n < G) {
+    float* row = &s_acc[w][n * kLdsStride];
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2) {
+      const f32x4 e = acc[2 * j2] * wscale;
+      const f32x4 o = acc[2 * j2 + 1] * wscale;
+      float* dst = row + 32 * j2 + 8 * g4;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], o[0], e[1], o[1]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[2], o[2], e[3], o[3]};
+    }
+  }
+  __syncthreads();
+  const bool poisoned = s_bad != 0;
+
+  // each thread finishes 4 consecutive dims of one head
+  for (int32_t i4 = tid; i4 < G * (D / 4); i4 += kThreads) {
+    const int32_t hh = i4 / (D / 4);
+    const int32_t d = (i4 - hh * (D / 4)) * 4;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) Mh = fmaxf(Mh, s_m[u][hh]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      L += s_l[u][hh] * fast_exp2(s_m[u][hh] - Mh);
+      o += *reinterpret_cast<const f32x4*>(&s_acc[u][hh * kLdsStride + d]);
+    }
+    const int64_t row = q_row0 + static_cast<int64_t>(hh) * D;
+    if (nparts == 1) {
+      u16x4 ov;
+      if (poisoned) {
+        ov = u16x4{E::kNaN, E::kNaN, E::kNaN, E::kNaN};
+      } else {
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+      }
+      *reinterpret_cast<u16x4*>(a.out + row + d) = ov;
+    } else {
+      const int64_t st = (static_cast<int64_t>(b) * a.num_heads + kvh * G + hh) * a.max_parts + p;
+      if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
+      *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
+      if (d == 0) a.ws_ml[st] = poisoned ? float2{0.f, NAN} : float2{Mh, L};
+    }
+  }
+}
+
+// ---- decode: log-sum-exp merge -----------------------------------------------------
+struct MergeArgs {
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  const float2* ws_ml;
+  const float* ws_acc;
+  int32_t num_seqs, num_heads, max_ctx, max_parts;
+};
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+  constexpr int C4 = D / 4;              // float4 columns
+  constexpr int GROUPS = 256 / C4;       // partition groups
+  __shared__ float s_w[kMaxParts];
+  __shared__ float s_red[256];
+  __shared__ __attribute__((aligned(16))) f32x4 s_part[GROUPS][C4];
+
+  const int32_t b = blockIdx.x / a.num_heads;
+  const int32_t h = blockIdx.x - b * a.num_heads;
+  const int32_t ctx = a.ctx_lens[b];
+  if (ctx < 1 || ctx > a.max_ctx) return;                 // attention pass wrote NaN
+  const int32_t nparts = (ctx + kPartTokens - 1) / kPartTokens;
+  if (nparts <= 1) return;                                // attention pass wrote out
+  const int64_t st0 = (static_cast<int64_t>(b) * a.num_heads + h) * a.max_parts;
+  const int32_t tid = threadIdx.x;
+
+  float mx = -INFINITY;
+  for (int32_t i = tid; i < nparts; i += 256) mx = fmaxf(mx, a.ws_ml[st0 + i].x);
+  s_red[tid] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) s_red[tid] = fmaxf(s_red[tid], s_red[tid + s]);
+    __syncthreads();
+  }
+  const float M = s_red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int32_t i = tid; i < nparts; i += 256) {
+    const float2 ml = a.ws_ml[st0 + i];
+    const float wgt = fast_exp2(ml.x - M);
+    s_w[i] = wgt;
+    lsum += wgt * ml.y;
+  }
+  s_red[tid] = lsum;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) s_red[tid] += s_red[tid + s];
+    __syncthreads();
+  }
+  const float L = s_red[0];
+
+  const int32_t col = tid % C4;
+  const int32_t grp = tid / C4;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  const f32x4* acc4 = reinterpret_cast<const f32x4*>(a.ws_acc) + st0 * C4 + col;
+  for (int32_t i = grp; i < nparts; i += GROUPS) o += s_w[i] * acc4[static_cast<int64_t>(i) * C4];
+  s_part[grp][col] = o;
+  __syncthreads();
+  if (tid < C4) {
+    f32x4 t = s_part[0][tid];
+#pragma unroll
+    for (int g = 1; g < GROUPS; ++g) t += s_part[g][tid];
+    const float inv = 1.f / L;
+    u16x4 ov;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ov[r] = E::from_float(t[r] * inv);
+    *reinterpret_cast<u16x4*>(a.out + (static_cast<int64_t>(b) * a.num_heads + h) * D + 4 * tid) = ov;
+  }
+}
+
+// ---- host-side helpers -------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_cache(const pa_cache* c, const char* fn) {
+  if (!c) return pa::fail(PA_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (!c->k_cache || !c->v_cache) return pa::fail(PA_ERR_INVALID_ARG, "%s: cache pointers are NULL", fn);
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: cache pointers must be 16-byte aligned", fn);
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: num_blocks %d, num_kv_heads %d", fn, c->num_blocks, c->num_kv_heads);
+  if (c->block_size != kBlock)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16)", fn, c->block_size);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, c->head_dim);
+  if (c->dtype != PA_F16 && c->dtype != PA_BF16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, c->dtype);
+  return PA_OK;
+}
+
+pa_status launch_status(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t parts_for(int32_t max_ctx) { return (max_ctx + kPartTokens - 1) / kPartTokens; }
+
+size_t ws_ml_bytes(int64_t rows) { return (static_cast<size_t>(rows) * sizeof(float2) + 255) & ~size_t(255); }
+
+struct DecodeSetup {
+  DecodeArgs args;
+  int64_t grid;
+};
+
+pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                         int32_t num_heads, const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* ctx_lens, int32_t max_ctx, float scale, void* out,
+                         void* workspace, size_t workspace_bytes, bool need_q, DecodeSetup* su) {
+  pa_status st = check_cache(cache, fn);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
+  if (num_heads <= 0 || num_heads % cache->num_kv_heads)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: num_heads %d not a multiple of num_kv_heads %d", fn,
+                    num_heads, cache->num_kv_heads);
+  const int32_t G = num_heads / cache->num_kv_heads;
+  if (G > 16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", fn, G);
+  if (max_ctx < 1) return pa::fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d", fn, max_ctx);
+  if (need_q) {
+    if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * kBlock < max_ctx)
+      return pa::fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq %d cannot hold %d tokens", fn,
+                      max_blocks, max_ctx);
+    if (num_seqs > 0 && (!q || !block_tables || !aligned16(q)))
+      return pa::fail(PA_ERR_INVALID_ARG, "%s: q / block_tables NULL or q misaligned", fn);
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  }
+  if (num_seqs > 0 && (!ctx_lens || !out || !aligned16(out)))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: context_lens / out NULL or out misaligned", fn);
+  const int32_t P = parts_for(max_ctx);
+  if (P > kMaxParts) return pa::fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d too long", fn, max_ctx);
+  const size_t need = pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return pa::fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
+  const int64_t grid = static_cast<int64_t>(P) * cache->num_kv_heads * num_seqs;
+  if (grid > INT32_MAX) return pa::fail(PA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  DecodeArgs& a = su->args;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t*>(cache->v_cache);
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.out = static_cast<uint16_t*>(out);
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * P;
+  a.ws_ml = need ? static_cast<float2*>(workspace) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_ml_bytes(rows)) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = G;
+  a.max_blocks = max_blocks;
+  a.max_ctx = max_ctx;
+  a.num_blocks = cache->num_blocks;
+  a.max_parts = P;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  su->grid = grid;
+  return PA_OK;
+}
+
+template <class E>
+void launch_attn(const DecodeSetup& su, int d, hipStream_t s) {
+  if (d == 64)
+    decode_attn_kernel<E, 64><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+  else
+    decode_attn_kernel<E, 128><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+}
+
+template <class E>
+void launch_merge(const MergeArgs& m, int64_t grid, int d, hipStream_t s) {
+  if (d == 64)
+    decode_merge_kernel<E, 64><<<dim3(grid), dim3(256), 0, s>>>(m);
+  else
+    decode_merge_kernel<E, 128><<<dim3(grid), dim3(256), 0, s>>>(m);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_cache_write(const pa_cache* cache, const void* k, const void* v,
+                         const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  pa::clear_error();
+  pa_status st = check_cache(cache, "pa_cache_write");
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_cache_write: num_tokens %d", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_cache_write: k / v / slot_mapping NULL or misaligned");
+  const int D = cache->head_dim;
+  const int64_t threads = static_cast<int64_t>(num_tokens) * cache->num_kv_heads * (D / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return pa::fail(PA_ERR_UNSUPPORTED, "pa_cache_write: too many tokens");
+  const int64_t num_slots = static_cast<int64_t>(cache->num_blocks) * kBlock;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto kp = static_cast<const uint16_t*>(k);
+  auto vp = static_cast<const uint16_t*>(v);
+  auto kc = static_cast<uint16_t*>(cache->k_cache);
+  auto vc = static_cast<uint16_t*>(cache->v_cache);
+  if (D == 64)
+    cache_write_kernel<64><<<dim3(grid), dim3(256), 0, s>>>(kp, vp, slot_mapping, kc, vc, num_tokens,
+                                                           cache->num_kv_heads, num_slots);
+  else
+    cache_write_kernel<128><<<dim3(grid), dim3(256), 0, s>>>(kp, vp, slot_mapping, kc, vc, num_tokens,
+                                                            cache->num_kv_heads, num_slots);
+  return launch_status("pa_cache_write");
+}
+
+pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, const int32_t* pairs_host,
+                         int32_t num_pairs, void* stream) {
+  pa::clear_error();
+  pa_status st = check_cache(cache, "pa_copy_blocks");
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: num_pairs %d", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pairs is NULL");
+  if (num_pairs > 65535) return pa::fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: more than 65535 pairs");
+  if (pairs_host) {
+    // destinations distinct, none also a source, all ids in range
+    const int32_t nb = cache->num_blocks;
+    std::vector<uint8_t> role(nb, 0);   // bit 0: source, bit 1: destination
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t s = pairs_host[2 * i], d = pairs_host[2 * i + 1];
+      if (s < 0 || s >= nb || d < 0 || d >= nb)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pair %d (%d, %d) out of range", i, s, d);
+      if (role[d] & 2) return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: destination %d repeated", d);
+      role[s] |= 1;
+      role[d] |= 2;
+    }
+    for (int32_t b = 0; b < nb; ++b)
+      if (role[b] == 3) return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: block %d is source and destination", b);
+  }
+  const int64_t vecs = static_cast<int64_t>(cache->num_kv_heads) * kBlock * cache->head_dim * 2 / 16;
+  const int64_t gx = std::min<int64_t>((vecs + 255) / 256, 64);
+  copy_blocks_kernel<<<dim3(gx, num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      pairs, static_cast<u32x4*>(cache->k_cache), static_cast<u32x4*>(cache->v_cache), vecs,
+      cache->num_blocks);
+  return launch_status("pa_copy_blocks");
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= kPartTokens) return 0;
+  const int64_t P = parts_for(max_context_len);
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * P;
+  return ws_ml_bytes(rows) + static_cast<size_t>(rows) * head_dim * sizeof(float);
+}
+
+pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_seqs,
+                              int32_t num_heads, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t max_context_len, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  DecodeSetup su;
+  pa_status st = prepare_decode("pa_decode_attention", cache, q, num_seqs, num_heads, block_tables,
+                                max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                                workspace, workspace_bytes, true, &su);
+  if (st != PA_OK || num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == PA_F16)
+    launch_attn<F16>(su, cache->head_dim, s);
+  else
+    launch_attn<BF16>(su, cache->head_dim, s);
+  return launch_status("pa_decode_attention");
+}
+
+pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_heads,
+                          const int32_t* context_lens, int32_t max_context_len, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  DecodeSetup su;
+  pa_status st = prepare_decode("pa_decode_merge", cache, nullptr, num_seqs, num_heads, nullptr, 0,
+                                context_lens, max_context_len, 1.f, out, workspace,
+                                workspace_bytes, false, &su);
+  if (st != PA_OK || num_seqs == 0 || parts_for(max_context_len) <= 1) return st;
+  MergeArgs m;
+  m.ctx_lens = context_lens;
+  m.out = static_cast<uint16_t*>(out);
+  m.ws_ml = su.args.ws_ml;
+  m.ws_acc = su.args.ws_acc;
+  m.num_seqs = num_seqs;
+  m.num_heads = num_heads;
+  m.max_ctx = max_context_len;
+  m.max_parts = su.args.max_parts;
+  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads;
+  if (grid > INT32_MAX) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode_merge: grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == PA_F16)
+    launch_merge<F16>(m, grid, cache->head_dim, s);
+  else
+    launch_merge<BF16>(m, grid, cache->head_dim, s);
+  return launch_status("pa_decode_merge");
+}
+
+pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int32_t num_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = pa_decode_attention(cache, q, num_seqs, num_heads, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                                     workspace, workspace_bytes, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_merge(cache, num_seqs, num_heads, context_lens, max_context_len, out, workspace,
+                         workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+"""Torch-facing wrappers of the C-ABI calls (marshalling only; every step runs in libpa).
+
+Tensors must be contiguous, on one HIP device, in the dtypes and shapes pa.h
+states.  Work is enqueued on the current torch stream unless ``stream`` is
+given (a ``torch.cuda.Stream``).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+_DT = {torch.float16: N.PA_F16, torch.bfloat16: N.PA_BF16}
+
+
+def k_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int) -> Tuple[int, ...]:
+    return (num_blocks, num_kv_heads, head_dim // 8, N.BLOCK_SIZE, 8)
+
+
+def v_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int) -> Tuple[int, ...]:
+    return (num_blocks, num_kv_heads, N.BLOCK_SIZE // 4, head_dim, 4)
+
+
+def alloc_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+               device="cuda", fill_bits: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V pools in the library layout; ``fill_bits`` fills every element with a 16-bit pattern."""
+    k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=dtype, device=device)
+    v = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=dtype, device=device)
+    if fill_bits is not None:
+        val = int(np.int16(np.uint16(fill_bits)))
+        k.view(torch.int16).fill_(val)
+        v.view(torch.int16).fill_(val)
+    return k, v
+
+
+def _stream_ptr(stream, device) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> N.PaCache:
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DT:
+        raise TypeError("pools must both be float16 or both bfloat16")
+    if not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous device tensors")
+    nb, hkv, dc, bs, eight = k_cache.shape
+    if eight != 8 or bs != N.BLOCK_SIZE or tuple(v_cache.shape) != v_pool_shape(nb, hkv, dc * 8):
+        raise ValueError(f"pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} do not match the layout")
+    return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, dc * 8, _DT[k_cache.dtype])
+
+
+def _need(t: torch.Tensor, dtype, device, name, shape=None):
+    if t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous {dtype} tensor on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def cache_write(k_cache, v_cache, k, v, slot_mapping, stream=None) -> None:
+    desc = cache_desc(k_cache, v_cache)
+    T = k.shape[0]
+    shp = (T, desc.num_kv_heads, desc.head_dim)
+    _need(k, k_cache.dtype, k_cache.device, "k", shp)
+    _need(v, k_cache.dtype, k_cache.device, "v", shp)
+    _need(slot_mapping, torch.int64, k_cache.device, "slot_mapping", (T,))
+    N.check(N.lib().pa_cache_write(C.byref(desc), k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                   T, _stream_ptr(stream, k_cache.device)), "pa_cache_write")
+
+
+def copy_blocks(k_cache, v_cache, pairs, pairs_host: Optional[np.ndarray] = None, stream=None) -> None:
+    desc = cache_desc(k_cache, v_cache)
+    n = pairs.shape[0]
+    _need(pairs, torch.int32, k_cache.device, "pairs", (n, 2))
+    host = None
+    if pairs_host is not None:
+        pairs_host = np.ascontiguousarray(pairs_host, dtype=np.int32)
+        if pairs_host.shape != (n, 2):
+            raise ValueError("pairs_host must match pairs")
+        host = C.c_void_p(pairs_host.ctypes.data)
+    N.check(N.lib().pa_copy_blocks(C.byref(desc), pairs.data_ptr(), host, n,
+                                   _stream_ptr(stream, k_cache.device)), "pa_copy_blocks")
+
+
+def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(N.lib().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len))
+
+
+def alloc_workspace(num_seqs, num_heads, head_dim, max_context_len, device="cuda") -> torch.Tensor:
+    n = workspace_size(num_seqs, num_heads, head_dim, max_context_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace):
+    desc = cache_desc(k_cache, v_cache)
+    B, H, D = q.shape
+    _need(q, k_cache.dtype, k_cache.device, "q")
+    if D != desc.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    _need(block_tables, torch.int32, k_cache.device, "block_tables")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _need(context_lens, torch.int32, k_cache.device, "context_lens", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, k_cache.dtype, k_cache.device, "out", (B, H, D))
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    return desc, B, H, out, ws_ptr, ws_bytes
+
+
+def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int, scale: float,
+           out=None, workspace=None, stream=None) -> torch.Tensor:
+    """pa_decode: attention pass then log-sum-exp merge; returns out [B, H, D]."""
+    desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
+                                            workspace)
+    N.check(N.lib().pa_decode(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
+                              block_tables.shape[1], context_lens.data_ptr(), max_context_len,
+                              scale, out.data_ptr(), ws, wsb, _stream_ptr(stream, q.device)),
+            "pa_decode")
+    return out
+
+
+def decode_attention(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
+                     scale: float, out=None, workspace=None, stream=None) -> torch.Tensor:
+    desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
+                                            workspace)
+    N.check(N.lib().pa_decode_attention(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
+                                        block_tables.shape[1], context_lens.data_ptr(),
+                                        max_context_len, scale, out.data_ptr(), ws, wsb,
+                                        _stream_ptr(stream, q.device)), "pa_decode_attention")
+    return out
+
+
+def decode_merge(k_cache, v_cache, context_lens, max_context_len: int, out, workspace=None,
+                 stream=None) -> torch.Tensor:
+    desc = cache_desc(k_cache, v_cache)
+    B, H, D = out.shape
+    _need(context_lens, torch.int32, k_cache.device, "context_lens", (B,))
+    ws, wsb = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                   workspace.numel() * workspace.element_size())
+    N.check(N.lib().pa_decode_merge(C.byref(desc), B, H, context_lens.data_ptr(), max_context_len,
+                                    out.data_ptr(), ws, wsb, _stream_ptr(stream, out.device)),
+            "pa_decode_merge")
+    return out

@@ -1,0 +1,127 @@
+"""Shared set-up for the GPU tests: build a workload's cache on the device
+through the library, and compute the oracle's expectations on the CPU."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as OA
+from oracle import block_manager as OB
+from oracle import cache as OC
+from oracle import layout as OL
+
+POISON = {torch.float16: 0x7E00, torch.bfloat16: 0x7FC0}   # quiet NaN patterns
+TOL = {torch.float16: 2e-3, torch.bfloat16: 1e-2}
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+class SegCache(dict):
+    def __init__(self, wl):
+        super().__init__()
+        self.wl = wl
+
+    def get_seg(self, seg):
+        if seg not in self:
+            self[seg] = self.wl.segment_kv(seg)
+        return self[seg]
+
+    def tokens(self, seg, start, n):
+        k, v = self.get_seg(seg)
+        return k[start:start + n].contiguous(), v[start:start + n].contiguous()
+
+
+def build_device(wl, poison=True, free_order=None, device="cuda"):
+    """Cache after the workload's set-up trace, replayed through the library."""
+    from paged_kv_cache_385_amd import PagedKVCache
+    segs = SegCache(wl)
+    cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, device,
+                         free_order=wl.free_order if free_order is None else free_order,
+                         fill_bits=POISON[wl.dtype] if poison else 0)
+    cache.apply_trace(wl.setup, segs.tokens)
+    return cache, segs
+
+
+def run_step(wl, cache, segs, max_blocks=None):
+    """The workload's decode step through DecodeBatch; returns (out, batch)."""
+    from paged_kv_cache_385_amd import DecodeBatch
+    sids = [op[1] for op in wl.step]
+    if max_blocks is None:
+        max_blocks = -(-int(wl.ctx_lens.max()) // 16)
+    batch = DecodeBatch(cache, sids, wl.num_heads, wl.scale, max_blocks)
+    ks, vs = zip(*(segs.tokens(op[2], op[3], 1) for op in wl.step))
+    k_new = torch.cat(ks).to(cache.device)
+    v_new = torch.cat(vs).to(cache.device)
+    q = wl.q().to(cache.device)
+    out = batch.step(k_new, v_new, q)
+    torch.cuda.synchronize()
+    return out, batch
+
+
+def oracle_out(wl, segs, seqs=None) -> np.ndarray:
+    return OA.decode_batch(wl.q(), lambda b: wl.seq_kv(b, segs), wl.ctx_lens, wl.scale, seqs)
+
+
+def oracle_pools(wl, segs, with_step=True, fill=None):
+    """Expected logical pools (uint16 bits) from the oracle's block manager and cache ops."""
+    bm = OB.RefBlockManager(wl.num_blocks, 16, wl.free_order)
+    fill = POISON[wl.dtype] if fill is None else fill
+    kp, vp = OC.empty_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, fill=fill)
+    ops = list(wl.setup)
+    for op in ops:
+        if op[0] == "add":
+            bm.add_seq(op[1])
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        else:
+            slots, cows = bm.append_tokens(op[1], op[4])
+            OC.copy_blocks(kp, vp, cows, inplace=True)
+            k, v = segs.tokens(op[2], op[3], op[4])
+            OC.cache_write(kp, vp, k, v, slots, inplace=True)
+    step = None
+    if with_step:
+        sids = [op[1] for op in wl.step]
+        slots, cows = bm.append_batch(sids)
+        OC.copy_blocks(kp, vp, cows, inplace=True)
+        ks, vs = zip(*(segs.tokens(op[2], op[3], 1) for op in wl.step))
+        OC.cache_write(kp, vp, torch.cat(ks), torch.cat(vs), slots, inplace=True)
+        step = (slots, cows)
+    return kp, vp, bm, step
+
+
+def oracle_step_tables(wl):
+    """The oracle block manager's tables, slots and pairs for the workload's step."""
+    bm = OB.RefBlockManager(wl.num_blocks, 16, wl.free_order)
+    for op in wl.setup:
+        if op[0] == "add":
+            bm.add_seq(op[1])
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        else:
+            bm.append_tokens(op[1], op[4])
+    slots, cows = bm.append_batch([op[1] for op in wl.step])
+    return bm, slots, cows
+
+
+def device_pools_logical(cache):
+    k = cache.k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    v = cache.v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    return OL.k_to_logical(k), OL.v_to_logical(v)
+
+
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype, rows=None, label=""):
+    g = got.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.isfinite(g).all(), f"{label}: non-finite output"
+    err = np.abs(g - ref)
+    worst = float(err.max())
+    say(f"{label}: max|err| = {worst:.3e} (tol {TOL[dtype]:.0e}), max|out| = {np.abs(ref).max():.3f}")
+    assert worst <= TOL[dtype], f"{label}: max abs error {worst} > {TOL[dtype]}"
+    return worst

@@ -1,0 +1,243 @@
+"""Host-side checks of libpa.so that need no GPU.
+
+* the library loads and exports every function include/pa.h declares;
+* argument validation rejects bad calls before anything is enqueued;
+* the native block manager matches the oracle's pure-Python one bit for bit
+  (slots, copy-on-write pairs, tables, refcounts, free lists, statistics and
+  the points where the pool runs out) on seeded random traces and on the five
+  workloads' traces.
+"""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block_manager as REF
+from tests.conftest import ROOT
+from workloads import CONFIG_IDS, make_workload
+
+N = pytest.importorskip("paged_kv_cache_385_amd._native")
+from paged_kv_cache_385_amd.block_manager import BlockManager  # noqa: E402
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 20
+    lib = N.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(N.SIGNATURES), set(names) ^ set(N.SIGNATURES)
+    assert lib.pa_status_string(N.PA_ERR_WORKSPACE) == b"PA_ERR_WORKSPACE"
+
+
+# ---- argument validation (fake device pointers never reach a kernel) ------------------
+no_device = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="fake-pointer validation runs only where no device exists")
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+
+
+def _cache(**kw):
+    d = dict(k_cache=FAKE, v_cache=FAKE, num_blocks=8, block_size=16, num_kv_heads=2,
+             head_dim=128, dtype=N.PA_F16)
+    d.update(kw)
+    return N.PaCache(**d)
+
+
+@no_device
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=32), N.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), N.PA_ERR_UNSUPPORTED),
+    (dict(dtype=7), N.PA_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), N.PA_ERR_INVALID_ARG),
+    (dict(k_cache=FAKE + 2), N.PA_ERR_INVALID_ARG),
+    (dict(v_cache=None), N.PA_ERR_INVALID_ARG),
+])
+def test_cache_descriptor_validation(kw, status):
+    lib = N.lib()
+    c = _cache(**kw)
+    assert lib.pa_cache_write(C.byref(c), FAKE, FAKE, FAKE, 4, None) == status
+    assert lib.pa_copy_blocks(C.byref(c), FAKE, None, 1, None) == status
+    assert lib.pa_decode(C.byref(c), FAKE, 1, 2, FAKE, 1, FAKE, 16, 0.1, FAKE, None, 0, None) == status
+    assert lib.pa_last_error()
+
+
+@no_device
+def test_call_validation():
+    lib = N.lib()
+    c = _cache()
+    assert lib.pa_cache_write(C.byref(c), FAKE, FAKE, FAKE, 0, None) == N.PA_OK      # nothing to do
+    assert lib.pa_cache_write(C.byref(c), FAKE, FAKE, FAKE, -1, None) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_cache_write(C.byref(c), FAKE + 8, FAKE, FAKE, 1, None) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_cache_write(None, FAKE, FAKE, FAKE, 1, None) == N.PA_ERR_INVALID_ARG
+    # copy pairs checked on the host copy
+    for bad in ([[0, 8]], [[0, 1], [2, 1]], [[0, 1], [1, 2]], [[-1, 3]]):
+        h = np.ascontiguousarray(bad, dtype=np.int32)
+        assert lib.pa_copy_blocks(C.byref(c), FAKE, h.ctypes.data, len(h), None) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(C.byref(c), FAKE, None, 0, None) == N.PA_OK
+    dec = lambda **k: lib.pa_decode(  # noqa: E731
+        C.byref(c), k.get("q", FAKE), k.get("B", 2), k.get("H", 4), FAKE, k.get("mb", 64), FAKE,
+        k.get("mc", 1000), k.get("scale", 0.1), k.get("out", FAKE), k.get("ws", None),
+        k.get("wsb", 0), None)
+    assert dec() == N.PA_ERR_WORKSPACE                       # 1000 tokens need a merge workspace
+    assert dec(H=3) == N.PA_ERR_INVALID_ARG                  # not a multiple of num_kv_heads
+    assert dec(H=34) == N.PA_ERR_UNSUPPORTED                 # 17 query heads per KV head
+    assert dec(mb=8) == N.PA_ERR_INVALID_ARG                 # 8 blocks cannot hold 1000 tokens
+    assert dec(mc=0) == N.PA_ERR_INVALID_ARG
+    assert dec(scale=float("nan")) == N.PA_ERR_INVALID_ARG
+    assert dec(q=FAKE + 4) == N.PA_ERR_INVALID_ARG
+    assert dec(out=None) == N.PA_ERR_INVALID_ARG
+    need = lib.pa_decode_workspace_size(2, 4, 128, 1000)
+    assert dec(ws=FAKE, wsb=need - 1) == N.PA_ERR_WORKSPACE
+    assert lib.pa_decode_merge(C.byref(c), 2, 4, FAKE, 1000, FAKE, None, 0, None) == N.PA_ERR_WORKSPACE
+
+
+def test_workspace_size():
+    lib = N.lib()
+    assert lib.pa_decode_workspace_size(8, 32, 128, 512) == 0          # one partition: no merge
+    assert lib.pa_decode_workspace_size(0, 32, 128, 4096) == 0
+    for B, H, D, mc in ((8, 32, 128, 131072), (128, 64, 128, 4096), (3, 5, 64, 513)):
+        P = -(-mc // 512)
+        n = lib.pa_decode_workspace_size(B, H, D, mc)
+        assert n >= B * H * P * (D + 2) * 4                          # states fit
+        assert n < B * H * P * (D + 2) * 4 + 512
+
+
+# ---- native block manager vs the oracle's -------------------------------------------------
+def _same_state(nat, ref, sids):
+    assert nat.free_list() == ref.free_list()
+    for s in sids:
+        assert nat.block_table(s) == ref.block_table(s)
+        assert nat.seq_len(s) == ref.seq_len(s)
+    assert [nat.refcount(b) for b in range(ref.num_blocks)] == \
+           [ref.refcount(b) for b in range(ref.num_blocks)]
+    a, b = nat.stats(), ref.stats()
+    for k in ("free_blocks", "used_blocks", "shared_blocks", "allocated_slots", "occupied_slots"):
+        assert a[k] == b[k], k
+    assert a["waste"] == pytest.approx(b["waste"], abs=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_native_matches_reference_on_random_traces(seed):
+    rng = np.random.default_rng(seed)
+    nb = int(rng.integers(8, 200))
+    order = rng.permutation(nb)
+    nat, ref = BlockManager(nb, 16, order), REF.RefBlockManager(nb, 16, order)
+    live, next_id = [], 0
+    for step in range(500):
+        r = rng.random()
+        if r < 0.12 or not live:
+            nat.add_seq(next_id)
+            ref.add_seq(next_id)
+            live.append(next_id)
+            next_id += 1
+        elif r < 0.22:
+            p = live[int(rng.integers(len(live)))]
+            nat.fork(p, next_id)
+            ref.fork(p, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif r < 0.30:
+            s = live.pop(int(rng.integers(len(live))))
+            nat.free_seq(s)
+            ref.free_seq(s)
+        elif r < 0.45:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 40))
+            try:
+                s_ref, c_ref = ref.append_tokens(s, n)
+            except REF.OutOfBlocks:
+                with pytest.raises(N.OutOfBlocks):
+                    nat.append_tokens(s, n)
+            else:
+                s_nat, c_nat = nat.append_tokens(s, n)
+                assert s_nat.tolist() == s_ref
+                assert [tuple(p) for p in c_nat.tolist()] == c_ref
+        else:
+            k = int(rng.integers(1, min(len(live), 8) + 1))
+            batch = rng.choice(live, size=k, replace=False).tolist()
+            try:
+                s_ref, c_ref = ref.append_batch(batch)
+            except REF.OutOfBlocks:
+                with pytest.raises(N.OutOfBlocks):
+                    nat.append_batch(batch)
+            else:
+                s_nat, c_nat = nat.append_batch(batch)
+                assert s_nat.tolist() == s_ref
+                assert [tuple(p) for p in c_nat.tolist()] == c_ref
+        _same_state(nat, ref, live)
+
+
+def test_errors_and_atomicity():
+    nat = BlockManager(4, 16)
+    nat.add_seq(0)
+    with pytest.raises(N.PaError):
+        nat.add_seq(0)
+    with pytest.raises(N.PaError):
+        nat.fork(5, 6)
+    with pytest.raises(N.PaError):
+        nat.append(9)
+    nat.append_tokens(0, 64)
+    before = (nat.free_list(), nat.block_table(0), nat.seq_len(0))
+    with pytest.raises(N.OutOfBlocks):
+        nat.append(0)
+    with pytest.raises(N.OutOfBlocks):
+        nat.append_tokens(0, 3)
+    assert (nat.free_list(), nat.block_table(0), nat.seq_len(0)) == before
+    with pytest.raises(N.PaError):
+        nat.append_batch([0, 0])
+    with pytest.raises(N.PaError):
+        BlockManager(4, 16, [0, 1, 1, 2])
+    with pytest.raises(N.PaError):
+        BlockManager(4, 32)
+
+
+def test_pack_tables():
+    nat = BlockManager(16, 16, list(range(15, -1, -1)))
+    for s, n in ((0, 1), (1, 40), (2, 16)):
+        nat.add_seq(s)
+        nat.append_tokens(s, n)
+    tab, ctx = nat.pack([2, 0, 1], 4)
+    assert ctx.tolist() == [16, 1, 40]
+    assert tab.tolist() == [[11, -1, -1, -1], [15, -1, -1, -1], [14, 13, 12, -1]]
+    with pytest.raises(N.PaError):
+        nat.pack([1], 2)
+
+
+@pytest.mark.parametrize("cfg", CONFIG_IDS)
+def test_workload_traces_match(cfg):
+    wl = make_workload(cfg)
+    nat = BlockManager(wl.num_blocks, 16, wl.free_order)
+    ref = REF.RefBlockManager(wl.num_blocks, 16, wl.free_order)
+    for op in wl.setup:
+        if op[0] == "add":
+            nat.add_seq(op[1])
+            ref.add_seq(op[1])
+        elif op[0] == "fork":
+            nat.fork(op[1], op[2])
+            ref.fork(op[1], op[2])
+        else:
+            s_nat, c_nat = nat.append_tokens(op[1], op[4])
+            s_ref, c_ref = ref.append_tokens(op[1], op[4])
+            assert np.array_equal(s_nat, np.asarray(s_ref, dtype=np.int64))
+            assert [tuple(p) for p in c_nat.tolist()] == c_ref
+    sids = [op[1] for op in wl.step]
+    s_nat, c_nat = nat.append_batch(sids)
+    s_ref, c_ref = ref.append_batch(sids)
+    assert s_nat.tolist() == s_ref and [tuple(p) for p in c_nat.tolist()] == c_ref
+    mb = -(-int(wl.ctx_lens.max()) // 16)
+    tab, ctx = nat.pack(sids, mb)
+    assert ctx.tolist() == wl.ctx_lens.tolist()
+    for i, s in enumerate(sids):
+        t = ref.block_table(s)
+        assert tab[i, :len(t)].tolist() == t and (tab[i, len(t):] == -1).all()
+    _same_state(nat, ref, sids)
