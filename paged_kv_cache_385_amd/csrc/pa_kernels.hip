@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -43,11 +44,11 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = PA_BLOCK_SIZE;                       // tokens per block
-constexpr int kPartTokens = PA_PARTITION_TOKENS;            // tokens per workgroup
-constexpr int kPartBlocks = kPartTokens / kBlock;           // 32
+constexpr int kPartTokens = PA_PARTITION_TOKENS;            // shortest partition (512)
+constexpr int kLongPartTokens = 2 * PA_PARTITION_TOKENS;    // partition of large launches
 constexpr int kWaves = 4;                                   // waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxParts = 1024;                             // merge LDS bound
+constexpr int kMaxParts = 1024;                             // longest context / 512
 
 // ---- element traits --------------------------------------------------------------
 struct F16 {
@@ -157,21 +158,123 @@ struct DecodeArgs {
   float* ws_acc;     // [B][H][P][D] unnormalised output
   int32_t num_seqs, num_heads, num_kv_heads, group;
   int32_t max_blocks, max_ctx, num_blocks, max_parts;
-  float scale_log2;  // scale * log2(e)
+  int32_t part_blocks;  // blocks per partition (32 or 64)
+  float scale_log2;     // scale * log2(e)
 };
 
-// Workgroup id -> logical work index.  Consecutive workgroup ids go round-robin
-// to the 8 XCDs; this permutation gives each XCD eight consecutive logical
-// indices, i.e. eight consecutive sequences of one (KV head, partition), so
-// sequences that alias prefix blocks meet in one XCD's L2.
-__device__ __forceinline__ int32_t xcd_swizzle(int32_t wg, int32_t n) {
-  const int32_t full = n & ~63;
-  if (wg >= full) return wg;
-  return (wg & ~63) | ((wg & 7) << 3) | ((wg >> 3) & 7);
+__device__ __forceinline__ int32_t wave_sum_i(int32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int32_t wave_incl_scan_i(int32_t x, int32_t lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+// Lane holding the k-th (0-based) set bit of `mask`.
+__device__ __forceinline__ int32_t kth_set_lane(uint64_t mask, int32_t k, int32_t lane) {
+  const bool mine = ((mask >> lane) & 1) && __popcll(mask & ((1ull << lane) - 1)) == k;
+  return __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
 }
 
+// How a sequence splits into work items: `nfull` partitions of part_blocks blocks,
+// then at most one shorter partition whose size class (0..3, quarters of a
+// partition) is `cls`, or -1 when there is none.  A context length outside
+// [1, max_ctx] is one item of class 0 (its workgroup writes NaN).
+__device__ __forceinline__ void seq_items(int32_t ctx, int32_t max_ctx, int32_t pb, int32_t* nfull,
+                                          int32_t* cls) {
+  if (ctx < 1 || ctx > max_ctx) {
+    *nfull = 0;
+    *cls = 0;
+    return;
+  }
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  *nfull = nblk / pb;
+  const int32_t rem = nblk - *nfull * pb;
+  *cls = rem ? (4 * rem) / pb : -1;
+}
+
+// Work item of this workgroup.  Every partition of every sequence and KV head is
+// one item; the list holds the full partitions first, ordered (KV head, sequence,
+// partition), then the last, shorter partitions from the largest size class to
+// the smallest, ordered (KV head, sequence) within a class -- big items start
+// first so the short ones fill the tail.  Workgroup ids are mapped to list
+// positions so that each of the 8 XCDs (which take workgroup ids round-robin)
+// gets 8 consecutive positions out of every 64.  Returns false for a workgroup
+// beyond the list (the launch is sized for the longest possible list).  Every
+// lane of every wave computes the same answer from the context lengths.
+__device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_t* okvh,
+                          int32_t* op) {
+  const int32_t B = a.num_seqs, pb = a.part_blocks, hkv = a.num_kv_heads;
+  int32_t nfull_tot = 0;
+  int32_t cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
+  for (int32_t c = 0; c < B; c += 64) {
+    int32_t nf = 0, cl = -1;
+    if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
+    nfull_tot += wave_sum_i(nf);
+    cnt0 += __popcll(__ballot(cl == 0));
+    cnt1 += __popcll(__ballot(cl == 1));
+    cnt2 += __popcll(__ballot(cl == 2));
+    cnt3 += __popcll(__ballot(cl == 3));
+  }
+  const int32_t n_full = nfull_tot * hkv;
+  const int32_t n_items = n_full + (cnt0 + cnt1 + cnt2 + cnt3) * hkv;
+  int32_t i = blockIdx.x;
+  if (i >= n_items) return false;
+  if (i < (n_items & ~63)) i = (i & ~63) | ((i & 7) << 3) | ((i >> 3) & 7);
+
+  if (i < n_full) {
+    const int32_t kvh = i / nfull_tot;
+    const int32_t j = i - kvh * nfull_tot;          // j-th full partition in sequence order
+    int32_t base = 0;
+    for (int32_t c = 0; c < B; c += 64) {
+      int32_t nf = 0, cl;
+      if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
+      const int32_t incl = base + wave_incl_scan_i(nf, lane);
+      const uint64_t hit = __ballot(incl - nf <= j && j < incl);
+      if (hit) {
+        const int32_t l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        *ob = c + l;
+        *okvh = kvh;
+        *op = j - (__shfl(incl, l) - __shfl(nf, l));
+        return true;
+      }
+      base = __shfl(incl, 63);
+    }
+    return false;   // not reached
+  }
+  int32_t r = i - n_full;
+  int32_t cls = 3, cnt = cnt3;
+  if (r >= cnt3 * hkv) { r -= cnt3 * hkv; cls = 2; cnt = cnt2;
+    if (r >= cnt2 * hkv) { r -= cnt2 * hkv; cls = 1; cnt = cnt1;
+      if (r >= cnt1 * hkv) { r -= cnt1 * hkv; cls = 0; cnt = cnt0; } } }
+  const int32_t kvh = r / cnt;
+  int32_t k = r - kvh * cnt;                        // k-th sequence of the class
+  for (int32_t c = 0; c < B; c += 64) {
+    int32_t nf = 0, cl = -1;
+    if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
+    const uint64_t m = __ballot(cl == cls);
+    const int32_t pc = __popcll(m);
+    if (k < pc) {
+      const int32_t l = kth_set_lane(m, k, lane);
+      *ob = c + l;
+      *okvh = kvh;
+      *op = __shfl(nf, l);
+      return true;
+    }
+    k -= pc;
+  }
+  return false;     // not reached
+}
+
+// Three waves per SIMD: 136 registers, no spills, and 3 x 34 KB of LDS per CU.
 template <class E, int D>
-__global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_attn_kernel(DecodeArgs a) {
   constexpr int KK = D / 32;        // 16x16x32 steps for q.K^T; also 16-byte V loads per lane
   constexpr int MT = D / 16;        // output tiles of 16 dims
   constexpr int kLdsStride = D + 4; // floats per head row in LDS (staggers banks)
@@ -179,21 +282,22 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
   __shared__ float s_l[kWaves][16];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][16 * kLdsStride];
 
-  const int32_t lin = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int32_t b = lin % a.num_seqs;
-  const int32_t rest = lin / a.num_seqs;
-  const int32_t kvh = rest % a.num_kv_heads;
-  const int32_t p = rest / a.num_kv_heads;
-  const int32_t G = a.group;
-
-  const int32_t ctx = a.ctx_lens[b];
-  const bool bad_ctx = ctx < 1 || ctx > a.max_ctx;
-  const int32_t nparts = bad_ctx ? 1 : (ctx + kPartTokens - 1) / kPartTokens;
-  if (p >= nparts) return;
-
   const int32_t tid = threadIdx.x;
   const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t lane = tid & 63;
+  int32_t b, kvh, p;
+  if (!plan_item(a, lane, &b, &kvh, &p)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  p = __builtin_amdgcn_readfirstlane(p);
+  const int32_t G = a.group;
+  const int32_t PB = a.part_blocks;
+
+  if (b >= a.num_seqs || kvh >= a.num_kv_heads) return;   // cannot happen; keeps every read in bounds
+  const int32_t ctx = a.ctx_lens[b];
+  const bool bad_ctx = ctx < 1 || ctx > a.max_ctx;
+  const int32_t nparts = bad_ctx ? 1 : (ctx + PB * kBlock - 1) / (PB * kBlock);
+  if (p < 0 || p >= nparts) return;
   const int32_t n = lane & 15;       // query head within the group (MFMA column)
   const int32_t g4 = lane >> 4;      // token quad within a block (MFMA row group)
   const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G) * D;
@@ -211,30 +315,34 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
                      : u32x4{0, 0, 0, 0};
   }
 
+  // This wave's blocks are first, first + 4, ... below jend (at most PB / 4 of them).
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t j0 = p * kPartBlocks + w;
-  const int32_t jend = min(nblk, (p + 1) * kPartBlocks);
-  const int32_t nw = j0 < jend ? (jend - j0 + kWaves - 1) / kWaves : 0;
+  const int32_t jend = min(nblk, (p + 1) * PB);
+  const int32_t first = p * PB + w;
+  const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
 
+  // All of the wave's block ids in one load: lane i holds the id of its i-th block,
+  // so no table read sits between two tile loads.
+  int32_t ids = 0;
+  if (lane < nw) ids = bt[first + kWaves * lane];
+  const bool id_bad = lane < nw && (ids < 0 || ids >= a.num_blocks);
+  if (id_bad) ids = 0;
+  const bool bad_blk = __ballot(id_bad) != 0;
+
   float m_run = -INFINITY;
   float l_run = 0.f;
-  bool bad_blk = false;
   f32x4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 kb[2][KK], vb[2][KK];
 
-  auto load_block = [&](int buf, int32_t j) {
-    int32_t phys = bt[j];
-    if (phys < 0 || phys >= a.num_blocks) {
-      bad_blk = true;
-      phys = 0;
-    }
+  auto load_block = [&](int buf, int32_t i) {
+    const int32_t phys = __builtin_amdgcn_readlane(ids, i);
     const uint16_t* kt = a.k_cache + phys * blk_stride + head_off;
     const uint16_t* vt = a.v_cache + phys * blk_stride + head_off;
 #pragma unroll
@@ -243,11 +351,13 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
     for (int j2 = 0; j2 < KK; ++j2) vb[buf][j2] = load16(vt + ((g4 * D) + 32 * j2 + 2 * n) * 4);
   };
 
-  auto compute_block = [&](int buf, int32_t j) {
+  // Block i of the wave; i >= nw is a padding step whose positions are all masked,
+  // which leaves m_run, l_run and acc unchanged (m_run is finite by then).
+  auto compute_block = [&](int buf, int32_t i) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
-    const int32_t valid = ctx - j * kBlock;   // >= 1; tokens of this block inside the context
+    const int32_t valid = i < nw ? ctx - (first + kWaves * i) * kBlock : 0;   // tokens in context
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -291,15 +401,21 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecodeArgs a) {
     }
   };
 
+  // Two register buffers; every step issues the next block's loads before it
+  // computes the current one.  The loads are unconditional (the index is clamped
+  // to the last block, which then comes from L2) so the wait before each compute
+  // covers exactly the older buffer.
+  // The scheduling barriers keep the compiler from sinking a prefetch below the
+  // first wait of the compute that follows it.
   if (nw > 0) {
-    load_block(0, j0);
+    load_block(0, 0);
     for (int32_t i = 0; i < nw; i += 2) {
-      const int32_t ja = j0 + i * kWaves;
-      if (i + 1 < nw) load_block(1, ja + kWaves);
-      compute_block(0, ja);
-      if (i + 1 >= nw) break;
-      if (i + 2 < nw) load_block(0, ja + 2 * kWaves);
-      compute_block(1, ja + kWaves);
+      load_block(1, min(i + 1, nw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_block(0, i);
+      load_block(0, min(i + 2, nw - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_block(1, i + 1);
     }
   }
 
@@ -377,68 +493,80 @@ struct MergeArgs {
   uint16_t* out;
   const float2* ws_ml;
   const float* ws_acc;
-  int32_t num_seqs, num_heads, max_ctx, max_parts;
+  int32_t num_seqs, num_heads, max_ctx, max_parts, part_tokens;
 };
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per (sequence, query head): M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p acc_p / sum_p w_p l_p.  Lane l owns D/64 consecutive dims; the
+// partitions are visited in index order, so the result does not depend on timing.
 template <class E, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
-  constexpr int C4 = D / 4;              // float4 columns
-  constexpr int GROUPS = 256 / C4;       // partition groups
-  __shared__ float s_w[kMaxParts];
-  __shared__ float s_red[256];
-  __shared__ __attribute__((aligned(16))) f32x4 s_part[GROUPS][C4];
-
-  const int32_t b = blockIdx.x / a.num_heads;
-  const int32_t h = blockIdx.x - b * a.num_heads;
+  constexpr int V = D / 64;              // floats per lane
+  const int32_t row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.num_seqs * a.num_heads) return;
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t b = row / a.num_heads;
   const int32_t ctx = a.ctx_lens[b];
   if (ctx < 1 || ctx > a.max_ctx) return;                 // attention pass wrote NaN
-  const int32_t nparts = (ctx + kPartTokens - 1) / kPartTokens;
+  const int32_t nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;                                // attention pass wrote out
-  const int64_t st0 = (static_cast<int64_t>(b) * a.num_heads + h) * a.max_parts;
-  const int32_t tid = threadIdx.x;
+  const int64_t st0 = static_cast<int64_t>(row) * a.max_parts;
+  const float2* ml = a.ws_ml + st0;
 
   float mx = -INFINITY;
-  for (int32_t i = tid; i < nparts; i += 256) mx = fmaxf(mx, a.ws_ml[st0 + i].x);
-  s_red[tid] = mx;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) s_red[tid] = fmaxf(s_red[tid], s_red[tid + s]);
-    __syncthreads();
-  }
-  const float M = s_red[0];
-  __syncthreads();
+  for (int32_t i = lane; i < nparts; i += 64) mx = fmaxf(mx, ml[i].x);
+  const float M = wave_max(mx);
   float lsum = 0.f;
-  for (int32_t i = tid; i < nparts; i += 256) {
-    const float2 ml = a.ws_ml[st0 + i];
-    const float wgt = fast_exp2(ml.x - M);
-    s_w[i] = wgt;
-    lsum += wgt * ml.y;
+  for (int32_t i = lane; i < nparts; i += 64) {
+    const float2 v = ml[i];
+    lsum += fast_exp2(v.x - M) * v.y;
   }
-  s_red[tid] = lsum;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) s_red[tid] += s_red[tid + s];
-    __syncthreads();
-  }
-  const float L = s_red[0];
+  const float L = wave_sum(lsum);
 
-  const int32_t col = tid % C4;
-  const int32_t grp = tid / C4;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  const f32x4* acc4 = reinterpret_cast<const f32x4*>(a.ws_acc) + st0 * C4 + col;
-  for (int32_t i = grp; i < nparts; i += GROUPS) o += s_w[i] * acc4[static_cast<int64_t>(i) * C4];
-  s_part[grp][col] = o;
-  __syncthreads();
-  if (tid < C4) {
-    f32x4 t = s_part[0][tid];
+  float o[V];
 #pragma unroll
-    for (int g = 1; g < GROUPS; ++g) t += s_part[g][tid];
-    const float inv = 1.f / L;
-    u16x4 ov;
+  for (int e = 0; e < V; ++e) o[e] = 0.f;
+  const float* acc = a.ws_acc + st0 * D + lane * V;
+  for (int32_t c = 0; c < nparts; c += 64) {
+    const int32_t cnt = min(64, nparts - c);
+    const float wl = lane < cnt ? fast_exp2(ml[c + lane].x - M) : 0.f;
+    int32_t i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      float t[4][V];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ov[r] = E::from_float(t[r] * inv);
-    *reinterpret_cast<u16x4*>(a.out + (static_cast<int64_t>(b) * a.num_heads + h) * D + 4 * tid) = ov;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e) t[u][e] = acc[static_cast<int64_t>(c + i + u) * D + e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int32_t, wl), i + u));
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] += wgt * t[u][e];
+      }
+    }
+    for (; i < cnt; ++i) {
+      const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int32_t, wl), i));
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] += wgt * acc[static_cast<int64_t>(c + i) * D + e];
+    }
   }
+  const float inv = 1.f / L;
+  uint16_t* dst = a.out + static_cast<int64_t>(row) * D + lane * V;
+#pragma unroll
+  for (int e = 0; e < V; ++e) dst[e] = E::from_float(o[e] * inv);
 }
 
 // ---- host-side helpers -------------------------------------------------------------
@@ -466,7 +594,34 @@ pa_status launch_status(const char* fn) {
   return PA_OK;
 }
 
-int32_t parts_for(int32_t max_ctx) { return (max_ctx + kPartTokens - 1) / kPartTokens; }
+int32_t parts_for(int32_t max_ctx, int32_t part_tokens) {
+  return (max_ctx + part_tokens - 1) / part_tokens;
+}
+
+// Compute units of the current device (queried once per device).
+int32_t device_cus() {
+  static std::atomic<int32_t> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int32_t n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    n = v;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Partition length of one launch: 1024 tokens when even the longest possible
+// list of 1024-token items gives every compute unit at least 4 of them (fewer,
+// longer items cost less start-up and workspace traffic), else 512 tokens.
+int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                        parts_for(max_ctx, kLongPartTokens);
+  return items >= 4 * static_cast<int64_t>(device_cus()) ? kLongPartTokens : kPartTokens;
+}
 
 size_t ws_ml_bytes(int64_t rows) { return (static_cast<size_t>(rows) * sizeof(float2) + 255) & ~size_t(255); }
 
@@ -498,9 +653,12 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   }
   if (num_seqs > 0 && (!ctx_lens || !out || !aligned16(out)))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: context_lens / out NULL or out misaligned", fn);
-  const int32_t P = parts_for(max_ctx);
-  if (P > kMaxParts) return pa::fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d too long", fn, max_ctx);
-  const size_t need = pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx);
+  if (parts_for(max_ctx, kPartTokens) > kMaxParts)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d too long", fn, max_ctx);
+  const int32_t PT = part_tokens_for(num_seqs, cache->num_kv_heads, max_ctx);
+  const int32_t P = parts_for(max_ctx, PT);
+  // The workspace is sized for 512-token partitions; a launch with longer ones uses a prefix.
+  const size_t need = P > 1 ? pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return pa::fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
   const int64_t grid = static_cast<int64_t>(P) * cache->num_kv_heads * num_seqs;
@@ -523,6 +681,7 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.max_ctx = max_ctx;
   a.num_blocks = cache->num_blocks;
   a.max_parts = P;
+  a.part_blocks = PT / kBlock;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   su->grid = grid;
   return PA_OK;
@@ -612,7 +771,7 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, const int3
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_context_len) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= kPartTokens) return 0;
-  const int64_t P = parts_for(max_context_len);
+  const int64_t P = parts_for(max_context_len, kPartTokens);
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * P;
   return ws_ml_bytes(rows) + static_cast<size_t>(rows) * head_dim * sizeof(float);
 }
@@ -644,7 +803,7 @@ pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_h
   pa_status st = prepare_decode("pa_decode_merge", cache, nullptr, num_seqs, num_heads, nullptr, 0,
                                 context_lens, max_context_len, 1.f, out, workspace,
                                 workspace_bytes, false, &su);
-  if (st != PA_OK || num_seqs == 0 || parts_for(max_context_len) <= 1) return st;
+  if (st != PA_OK || num_seqs == 0 || su.args.max_parts <= 1) return st;
   MergeArgs m;
   m.ctx_lens = context_lens;
   m.out = static_cast<uint16_t*>(out);
@@ -654,8 +813,10 @@ pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_h
   m.num_heads = num_heads;
   m.max_ctx = max_context_len;
   m.max_parts = su.args.max_parts;
-  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads;
-  if (grid > INT32_MAX) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode_merge: grid too large");
+  m.part_tokens = su.args.part_blocks * kBlock;
+  const int64_t grid = (static_cast<int64_t>(num_seqs) * num_heads + 3) / 4;
+  if (static_cast<int64_t>(num_seqs) * num_heads > INT32_MAX)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode_merge: grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->dtype == PA_F16)
     launch_merge<F16>(m, grid, cache->head_dim, s);
