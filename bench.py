@@ -145,14 +145,17 @@ def main():
         batch.step(*steps_kv[i], q)
     torch.cuda.synchronize()
 
+    # timing events are created (first record) before the timed region
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [start, stop] + [x for pair in ev for x in pair]:
+        e.record(batch.stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
+    start.record(batch.stream)
     for j in range(K):
         batch.step(*steps_kv[W + j], q, attn_events=ev[j])
-    stop.record()
+    stop.record(batch.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     gpu_ms = start.elapsed_time(stop)

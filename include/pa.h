@@ -155,6 +155,26 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
                     const int32_t* context_lens, int32_t max_context_len, float scale,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pa_decode_fused -- the step's cache write and its decode in one attention pass.
+ * Same result as pa_cache_write(cache, k_new, v_new, slot_mapping, num_seqs)
+ * followed by pa_decode(...), when token i (k_new[i], v_new[i], [Hkv][D]) is
+ * the newest token of sequence i: its slot is the last context position,
+ *     slot_mapping[i] == block_tables[i][(n_i - 1) / 16] * 16 + (n_i - 1) % 16,
+ * which is what the block manager's append returns.  The workgroup that reads
+ * that position stores the token first, so no separate cache-write launch runs
+ * and the new token is read back from the cache it was written to.
+ *   slot_mapping[i] < 0    the token is not stored (the cache is read as is);
+ *   any other mismatch     the token is not stored and sequence i's output is NaN;
+ *   invalid context length sequence i's output is NaN and its token is not stored.
+ * Arguments otherwise as pa_cache_write and pa_decode.
+ * ------------------------------------------------------------------------- */
+pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* v_new,
+                          const int64_t* slot_mapping, const void* q, int32_t num_seqs,
+                          int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two stages of pa_decode, for callers that time or schedule them apart.
  * pa_decode_attention is the attention pass: one workgroup per (sequence, KV
  * head, 512-token partition) walks its blocks with an online softmax.  For a
@@ -240,6 +260,51 @@ pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* out);
 /* Free blocks, next-to-pop first, into out[0..cap); *n = how many are free. */
 pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
+/* One decode step's host work for n distinct sequences: pa_bm_append_batch, then
+ * pa_bm_pack into tables[n][max_blocks] and ctx_lens[n]; *max_ctx receives the
+ * longest context.  All or nothing: fails before any change when a table would
+ * outgrow max_blocks after its append. */
+pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slots,
+                     int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow, int32_t* tables,
+                     int32_t max_blocks, int32_t* ctx_lens, int32_t* max_ctx);
+
+/* ===========================================================================
+ * pa_decode_step -- one whole decode step of a batch, in one call.
+ * The order a decode step needs: the new token's K/V is stored before attention
+ * reads every cached token ("vLLM 核心概念", section "为什么需要 KV Cache？"),
+ * and a sequence about to write into a shared block first gets its own copy
+ * ("理解 vLLM PagedAttention", section 六).  The call
+ *   1. runs pa_bm_step for seq_ids on the host, writing slots, lengths, tables
+ *      and copy-on-write pairs into staging_host (pinned host memory) in the
+ *      layout below;
+ *   2. enqueues one copy of that region to staging_dev (device memory);
+ *   3. enqueues pa_copy_blocks (if any pair), pa_cache_write of k_new/v_new
+ *      ([num_seqs][num_kv_heads][head_dim], token i belongs to seq_ids[i]),
+ *      pa_decode_attention and pa_decode_merge, all on `stream`.
+ * Staging layout (each part 256-byte aligned, both buffers 256-byte aligned and
+ * at least pa_decode_step_staging_bytes() long): int64 slots[n] | int32 ctx[n] |
+ * int32 tables[n][max_blocks_per_seq] | int32 pairs[n][2].  staging_host must
+ * not be rewritten while an earlier copy from it may still be pending (the
+ * caller alternates two buffers or waits on an event).
+ * workspace: at least pa_decode_workspace_size(n, num_heads, head_dim,
+ * 16 * max_blocks_per_seq) bytes.  attn_begin / attn_end: optional hipEvent_t
+ * recorded around the attention pass (NULL to skip).  info (optional) receives
+ * the number of copy-on-write pairs and the longest context of the step.
+ * Every argument is checked before the block manager changes; after that only
+ * PA_ERR_HIP can occur.
+ * ========================================================================= */
+typedef struct pa_step_info {
+  int32_t num_cow;
+  int32_t max_context_len;
+} pa_step_info;
+
+size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);
+pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, const int64_t* seq_ids,
+                         const void* k_new, const void* v_new, const void* q, int32_t num_heads,
+                         float scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* staging_host, void* staging_dev, size_t staging_bytes,
+                         int32_t max_blocks_per_seq, void* attn_begin, void* attn_end,
+                         pa_step_info* info, void* stream);
 
 #ifdef __cplusplus
 }

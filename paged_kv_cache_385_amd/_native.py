@@ -36,6 +36,10 @@ class PaBmStats(C.Structure):
                 ("occupied_slots", C.c_int64), ("waste", C.c_double)]
 
 
+class PaStepInfo(C.Structure):
+    _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32)]
+
+
 class PaError(RuntimeError):
     def __init__(self, status: int, fn: str, detail: str):
         self.status = status
@@ -63,6 +67,8 @@ SIGNATURES = {
                                       C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_decode_merge": (C.c_int, [C.POINTER(PaCache), _I32, _I32, _P, _I32, _P, _P, C.c_size_t,
                                   _P]),
+    "pa_decode_fused": (C.c_int, [C.POINTER(PaCache), _P, _P, _P, _P, _I32, _I32, _P, _I32, _P,
+                                  _I32, C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_status_string": (C.c_char_p, [C.c_int]),
     "pa_last_error": (C.c_char_p, []),
     "pa_bm_create": (C.c_int, [_I32, _I32, _P, C.POINTER(C.c_void_p)]),
@@ -79,6 +85,11 @@ SIGNATURES = {
     "pa_bm_refcount": (C.c_int, [_P, _I32, _PI32]),
     "pa_bm_free_list": (C.c_int, [_P, _P, _I32, _PI32]),
     "pa_bm_stats_get": (C.c_int, [_P, C.POINTER(PaBmStats)]),
+    "pa_bm_step": (C.c_int, [_P, _I32, _P, _P, _P, _I32, _PI32, _P, _I32, _P, _PI32]),
+    "pa_decode_step_staging_bytes": (C.c_size_t, [_I32, _I32]),
+    "pa_decode_step": (C.c_int, [_P, C.POINTER(PaCache), _I32, _P, _P, _P, _P, _I32, C.c_float, _P,
+                                 _P, C.c_size_t, _P, _P, C.c_size_t, _I32, _P, _P,
+                                 C.POINTER(PaStepInfo), _P]),
 }
 
 _lib = None

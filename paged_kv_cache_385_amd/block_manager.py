@@ -100,6 +100,24 @@ class BlockManager:
                 "pa_bm_pack")
         return tables, ctx
 
+    def step(self, sids: Sequence[int], max_blocks: int):
+        """pa_bm_step: one token for each sequence, then pack.
+
+        Returns (slots int64[n], cow pairs int32[k, 2], tables int32[n, max_blocks],
+        context lengths int32[n], longest context).
+        """
+        ids = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
+        n = ids.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        cows = np.empty((max(n, 1), 2), dtype=np.int32)
+        tables = np.empty((max(n, 1), max_blocks), dtype=np.int32)
+        ctx = np.empty(max(n, 1), dtype=np.int32)
+        nc, mx = C.c_int32(), C.c_int32()
+        N.check(self._lib.pa_bm_step(self._h, n, _ptr(ids), _ptr(slots), _ptr(cows), max(n, 1),
+                                     C.byref(nc), _ptr(tables), max_blocks, _ptr(ctx), C.byref(mx)),
+                "pa_bm_step")
+        return slots[:n], cows[:nc.value], tables[:n], ctx[:n], mx.value
+
     def refcount(self, blk: int) -> int:
         r = C.c_int32()
         N.check(self._lib.pa_bm_refcount(self._h, blk, C.byref(r)), "pa_bm_refcount")

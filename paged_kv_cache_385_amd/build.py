@@ -53,11 +53,15 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     k_o = os.path.join(BUILD, "pa_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", *inc, "-c",
           os.path.join(CSRC, "block_manager.cpp"), "-o", bm_o], verbose)
+    step_o = os.path.join(BUILD, "decode_step.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", *inc,
+          "-I", "/opt/rocm/include", "-c", os.path.join(CSRC, "decode_step.cpp"), "-o", step_o],
+         verbose)
     extra = ["-save-temps=obj"] if save_temps else []
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "pa_kernels.hip"), "-o", k_o],
          verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, k_o, "-o", tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -317,6 +317,33 @@ pa_status pa_bm_pack(const pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t
   return PA_OK;
 }
 
+pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slots,
+                     int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow, int32_t* tables,
+                     int32_t max_blocks, int32_t* ctx_lens, int32_t* max_ctx) {
+  if (!bm || n < 0 || max_blocks <= 0 || !n_cow || !max_ctx ||
+      (n > 0 && (!seq_ids || !slots || !tables || !ctx_lens)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_step: bad arguments");
+  *n_cow = 0;
+  *max_ctx = 0;
+  // the packing must hold every table after its append, checked before anything changes
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = bm->find(seq_ids[i]);
+    if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_step: no sequence %lld", (long long)seq_ids[i]);
+    const int64_t blocks_after = (s->len + bm->block_size) / bm->block_size;
+    if (blocks_after > max_blocks || s->len + 1 > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_step: sequence %lld needs %lld blocks > %d",
+                      (long long)seq_ids[i], (long long)blocks_after, max_blocks);
+  }
+  pa_status st = pa_bm_append_batch(bm, n, seq_ids, slots, cow_pairs, cow_cap, n_cow);
+  if (st != PA_OK) return st;
+  st = pa_bm_pack(bm, n, seq_ids, tables, max_blocks, ctx_lens);
+  if (st != PA_OK) return st;   // not reached: checked above
+  int32_t m = 0;
+  for (int32_t i = 0; i < n; ++i) m = std::max(m, ctx_lens[i]);
+  *max_ctx = m;
+  return PA_OK;
+}
+
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* out) {
   if (!bm || !out || block < 0 || block >= bm->num_blocks)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: bad arguments");

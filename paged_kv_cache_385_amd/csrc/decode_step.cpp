@@ -1,0 +1,113 @@
+// One decode step of a batch of sequences, host work and device work in one call.
+//
+// The order is the one a decode step needs ("vLLM 核心概念", section "为什么需要
+// KV Cache？": the new token's K/V is cached, then attention reads all cached
+// tokens; "理解 vLLM PagedAttention", section 六: a sequence that diverges from a
+// shared block gets its private copy before it writes):
+//   1. host: the block manager reserves every sequence's next slot, reporting
+//      copy-on-write pairs, and packs tables and lengths into the staging buffer;
+//   2. one host-to-device copy of the staging buffer;
+//   3. pa_copy_blocks for the pairs, then pa_decode_fused (the new tokens'
+//      store and the decode in one attention pass, then the merge) -- all on
+//      the caller's stream.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct StagingLayout {
+  size_t slots, ctx, tables, pairs, total;
+};
+
+StagingLayout layout(int32_t n, int32_t max_blocks) {
+  StagingLayout l;
+  l.slots = 0;
+  l.ctx = l.slots + align_up(sizeof(int64_t) * static_cast<size_t>(n));
+  l.tables = l.ctx + align_up(sizeof(int32_t) * static_cast<size_t>(n));
+  l.pairs = l.tables + align_up(sizeof(int32_t) * static_cast<size_t>(n) * max_blocks);
+  l.total = l.pairs + align_up(sizeof(int32_t) * 2 * static_cast<size_t>(n));
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq) {
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
+  return layout(num_seqs, max_blocks_per_seq).total;
+}
+
+pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, const int64_t* seq_ids,
+                         const void* k_new, const void* v_new, const void* q, int32_t num_heads,
+                         float scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* staging_host, void* staging_dev, size_t staging_bytes,
+                         int32_t max_blocks_per_seq, void* attn_begin, void* attn_end,
+                         pa_step_info* info, void* stream) {
+  pa::clear_error();
+  if (!bm || !cache || num_seqs <= 0 || !seq_ids || !k_new || !v_new || !q || !out ||
+      !staging_host || !staging_dev || max_blocks_per_seq <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: bad arguments");
+  const StagingLayout l = layout(num_seqs, max_blocks_per_seq);
+  if (staging_bytes < l.total)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: staging %zu bytes, %zu needed",
+                    staging_bytes, l.total);
+  if (reinterpret_cast<uintptr_t>(staging_host) % kAlign || reinterpret_cast<uintptr_t>(staging_dev) % kAlign)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: staging buffers must be 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: k_new / v_new must be 16-byte aligned");
+  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * PA_BLOCK_SIZE;
+  if (max_tokens > INT32_MAX)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: max_blocks_per_seq %d too large", max_blocks_per_seq);
+  // Everything the device calls check, against the longest context the packing allows,
+  // before the block manager changes.
+  pa_status st = pa::decode_check(cache, q, num_seqs, num_heads, max_blocks_per_seq,
+                                  static_cast<int32_t>(max_tokens), scale, out, workspace,
+                                  workspace_bytes);
+  if (st != PA_OK) return st;
+
+  char* hb = static_cast<char*>(staging_host);
+  char* db = static_cast<char*>(staging_dev);
+  auto* slots_h = reinterpret_cast<int64_t*>(hb + l.slots);
+  auto* ctx_h = reinterpret_cast<int32_t*>(hb + l.ctx);
+  auto* tables_h = reinterpret_cast<int32_t*>(hb + l.tables);
+  auto* pairs_h = reinterpret_cast<int32_t*>(hb + l.pairs);
+  int32_t n_cow = 0, max_ctx = 0;
+  st = pa_bm_step(bm, num_seqs, seq_ids, slots_h, pairs_h, num_seqs, &n_cow, tables_h,
+                  max_blocks_per_seq, ctx_h, &max_ctx);
+  if (st != PA_OK) return st;
+  if (info) {
+    info->num_cow = n_cow;
+    info->max_context_len = max_ctx;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t upload = n_cow ? l.pairs + sizeof(int32_t) * 2 * n_cow : l.pairs;
+  if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, s) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
+  if (n_cow) {
+    st = pa_copy_blocks(cache, reinterpret_cast<const int32_t*>(db + l.pairs), pairs_h, n_cow, stream);
+    if (st != PA_OK) return st;
+  }
+  if (attn_begin && hipEventRecord(static_cast<hipEvent_t>(attn_begin), s) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipEventRecord failed");
+  st = pa::decode_fused_attention(cache, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots),
+                                  q, num_seqs, num_heads, reinterpret_cast<const int32_t*>(db + l.tables),
+                                  max_blocks_per_seq, reinterpret_cast<const int32_t*>(db + l.ctx),
+                                  max_ctx, scale, out, workspace, workspace_bytes, stream);
+  if (st != PA_OK) return st;
+  if (attn_end && hipEventRecord(static_cast<hipEvent_t>(attn_end), s) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipEventRecord failed");
+  return pa_decode_merge(cache, num_seqs, num_heads, reinterpret_cast<const int32_t*>(db + l.ctx),
+                         max_ctx, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

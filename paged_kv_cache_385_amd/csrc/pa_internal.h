@@ -12,4 +12,19 @@ namespace pa {
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
+// Argument checks of pa_decode for a call whose context lengths are at most
+// max_ctx, with a workspace of at least pa_decode_workspace_size(..., max_ctx)
+// bytes; enqueues nothing.
+pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_blocks_per_seq, int32_t max_ctx, float scale, void* out,
+                       void* workspace, size_t workspace_bytes);
+
+// The attention pass of pa_decode_fused (the new tokens' store included), without the merge.
+pa_status decode_fused_attention(const pa_cache* cache, const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, const void* q, int32_t num_seqs,
+                                 int32_t num_heads, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, float scale, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 }  // namespace pa

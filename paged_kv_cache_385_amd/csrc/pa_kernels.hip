@@ -154,6 +154,11 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* ctx_lens;
   uint16_t* out;
+  uint16_t* k_dst;             // the pools again, for the fused store of the new tokens
+  uint16_t* v_dst;
+  const uint16_t* k_new;       // [B][Hkv][D] new tokens, or NULL: no fused store
+  const uint16_t* v_new;
+  const int64_t* new_slots;    // [B]
   float2* ws_ml;     // [B][H][P] (max in log2 units, sum)
   float* ws_acc;     // [B][H][P][D] unnormalised output
   int32_t num_seqs, num_heads, num_kv_heads, group;
@@ -306,6 +311,41 @@ void decode_attn_kernel(DecodeArgs a) {
     for (int32_t i = tid; i < G * D; i += kThreads) a.out[q_row0 + i] = E::kNaN;
     return;
   }
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+
+  // Fused store of the step's new token (pa_decode_fused): the workgroup of the
+  // sequence's last partition writes the token's K and V for its KV head into
+  // the slot, then reads the cache as usual.  Only this workgroup reads that
+  // position, so a workgroup barrier orders the store before the reads.  A slot
+  // that is not the sequence's last position is not written, and the sequence's
+  // output becomes NaN.
+  bool slot_bad = false;
+  if (a.new_slots != nullptr && p == nparts - 1) {
+    const int64_t slot = a.new_slots[b];
+    if (slot >= 0) {
+      const int32_t last = ctx - 1;
+      const int32_t off = last % kBlock;
+      const int32_t phys = bt[last / kBlock];
+      if (phys >= 0 && phys < a.num_blocks && slot == static_cast<int64_t>(phys) * kBlock + off) {
+        if (w == 0 && lane < 2 * (D / 8)) {
+          const int32_t c = lane % (D / 8);
+          const int64_t src = (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * D + 8 * c;
+          const int64_t tile = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * (kBlock * D);
+          if (lane < D / 8) {
+            store16(a.k_dst + tile + (static_cast<int64_t>(c) * kBlock + off) * 8, load16(a.k_new + src));
+          } else {
+            const u16x8 vv = __builtin_bit_cast(u16x8, load16(a.v_new + src));
+            uint16_t* vdst = a.v_dst + tile + (static_cast<int64_t>(off >> 2) * D + 8 * c) * 4 + (off & 3);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vdst[4 * i] = vv[i];
+          }
+        }
+        __syncthreads();
+      } else {
+        slot_bad = true;
+      }
+    }
+  }
 
   // q fragments: B operand of q.K^T, dims 32kk + 8*g4 .. +7 of head n (zero for n >= G)
   u32x4 qf[KK];
@@ -320,7 +360,6 @@ void decode_attn_kernel(DecodeArgs a) {
   const int32_t jend = min(nblk, (p + 1) * PB);
   const int32_t first = p * PB + w;
   const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
@@ -331,7 +370,7 @@ void decode_attn_kernel(DecodeArgs a) {
   if (lane < nw) ids = bt[first + kWaves * lane];
   const bool id_bad = lane < nw && (ids < 0 || ids >= a.num_blocks);
   if (id_bad) ids = 0;
-  const bool bad_blk = __ballot(id_bad) != 0;
+  const bool bad_blk = __ballot(id_bad) != 0 || slot_bad;
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -671,6 +710,11 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.ctx_lens = ctx_lens;
   a.out = static_cast<uint16_t*>(out);
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * P;
+  a.k_dst = static_cast<uint16_t*>(cache->k_cache);
+  a.v_dst = static_cast<uint16_t*>(cache->v_cache);
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.new_slots = nullptr;
   a.ws_ml = need ? static_cast<float2*>(workspace) : nullptr;
   a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_ml_bytes(rows)) : nullptr;
   a.num_seqs = num_seqs;
@@ -704,6 +748,52 @@ void launch_merge(const MergeArgs& m, int64_t grid, int d, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace pa {
+
+pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_blocks_per_seq, int32_t max_ctx, float scale, void* out,
+                       void* workspace, size_t workspace_bytes) {
+  DecodeSetup su;
+  const int32_t dummy_table = 0, dummy_ctx = 0;
+  pa_status st = prepare_decode("pa_decode", cache, q, num_seqs, num_heads, &dummy_table,
+                                max_blocks_per_seq, &dummy_ctx, max_ctx, scale, out, workspace,
+                                workspace_bytes, true, &su);
+  if (st != PA_OK) return st;
+  const size_t need = pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return pa::fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes, %zu needed for contexts up to %d",
+                    workspace_bytes, need, max_ctx);
+  return PA_OK;
+}
+
+pa_status decode_fused_attention(const pa_cache* cache, const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, const void* q, int32_t num_seqs,
+                                 int32_t num_heads, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, float scale, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  DecodeSetup su;
+  pa_status st = prepare_decode("pa_decode_fused", cache, q, num_seqs, num_heads, block_tables,
+                                max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                                workspace, workspace_bytes, true, &su);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_fused: k_new / v_new / slot_mapping NULL or misaligned");
+  su.args.k_new = static_cast<const uint16_t*>(k_new);
+  su.args.v_new = static_cast<const uint16_t*>(v_new);
+  su.args.new_slots = slot_mapping;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == PA_F16)
+    launch_attn<F16>(su, cache->head_dim, s);
+  else
+    launch_attn<BF16>(su, cache->head_dim, s);
+  return launch_status("pa_decode_fused");
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -793,6 +883,20 @@ pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_
   else
     launch_attn<BF16>(su, cache->head_dim, s);
   return launch_status("pa_decode_attention");
+}
+
+pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* v_new,
+                          const int64_t* slot_mapping, const void* q, int32_t num_seqs,
+                          int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = pa::decode_fused_attention(cache, k_new, v_new, slot_mapping, q, num_seqs,
+                                            num_heads, block_tables, max_blocks_per_seq,
+                                            context_lens, max_context_len, scale, out, workspace,
+                                            workspace_bytes, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_merge(cache, num_seqs, num_heads, context_lens, max_context_len, out, workspace,
+                         workspace_bytes, stream);
 }
 
 pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_heads,

@@ -2,15 +2,17 @@
 
 ``PagedKVCache`` owns a K/V pool pair in the library layout and a native
 block manager.  ``DecodeBatch`` runs decode steps for a fixed set of
-sequences; one step is the whole hot path, in this order:
+sequences; one step is the whole hot path, done by one native call
+(``pa_decode_step``), in this order:
 
 1. host: the block manager reserves each sequence's next slot (and reports
-   copy-on-write pairs), then packs block tables and context lengths;
-2. one pinned host-to-device copy of slots, lengths, tables and pairs;
+   copy-on-write pairs), then packs block tables and context lengths into a
+   pinned staging buffer;
+2. one host-to-device copy of that buffer;
 3. ``pa_copy_blocks`` for the pairs (before any write can land in a block
    that is still shared);
 4. ``pa_cache_write`` of the new tokens' K and V;
-5. ``pa_decode_attention`` then ``pa_decode_merge``.
+5. the attention pass then the log-sum-exp merge.
 
 The copy-before-write order follows copy-on-write as "理解 vLLM PagedAttention"
 section 六 describes it: a diverging sequence must get its private copy of
@@ -19,6 +21,7 @@ the shared block before its new token is stored.
 
 from __future__ import annotations
 
+import ctypes as C
 from typing import Callable, Iterable, Optional, Sequence, Tuple
 
 import numpy as np
@@ -29,6 +32,10 @@ from . import ops
 from .block_manager import BlockManager
 
 _ALIGN = 256
+
+
+def _round(n: int) -> int:
+    return (n + _ALIGN - 1) // _ALIGN * _ALIGN
 
 
 class PagedKVCache:
@@ -94,7 +101,14 @@ class PagedKVCache:
 
 
 class DecodeBatch:
-    """Decode steps for a fixed list of sequences on one stream (see module docstring)."""
+    """Decode steps for a fixed list of sequences on one stream.
+
+    ``step`` is one ``pa_decode_step`` call: the native block manager reserves
+    the slots and packs the tables into a pinned staging buffer, which is copied
+    to the device, then the copy-on-write copy, the cache write and the decode
+    are enqueued.  Two pinned buffers alternate so the host can prepare step
+    i + 1 while the copy of step i may still be pending.
+    """
 
     def __init__(self, cache: PagedKVCache, sids: Sequence[int], num_heads: int, scale: float,
                  max_blocks_per_seq: int, stream: Optional[torch.cuda.Stream] = None):
@@ -106,68 +120,79 @@ class DecodeBatch:
         self.max_blocks = max_blocks_per_seq
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
         dev = cache.device
-        # one staging region: slots int64[B] | ctx int32[B] | tables int32[B*MB] | pairs int32[B*2]
-        self._off = []
-        off = 0
-        for nbytes in (8 * B, 4 * B, 4 * B * max_blocks_per_seq, 8 * B):
-            self._off.append(off)
-            off += (nbytes + _ALIGN - 1) // _ALIGN * _ALIGN
-        self._bytes = off
-        self._pinned = [torch.empty(off, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        lib = N.lib()
+        self._lib = lib
+        self._bytes = int(lib.pa_decode_step_staging_bytes(B, max_blocks_per_seq))
+        # 256-byte aligned regions carved from slightly larger allocations
+        self._pinned_raw = [torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, pin_memory=True)
+                            for _ in range(2)]
+        self._pinned = [self._aligned(t) for t in self._pinned_raw]
         self._staged = [torch.cuda.Event() for _ in range(2)]
-        self._dev = torch.empty(off, dtype=torch.uint8, device=dev)
-        self.slots_d = self._view(self._dev, 0, torch.int64, (B,))
-        self.ctx_d = self._view(self._dev, 1, torch.int32, (B,))
-        self.tables_d = self._view(self._dev, 2, torch.int32, (B, max_blocks_per_seq))
-        self.pairs_d = self._view(self._dev, 3, torch.int32, (B, 2))
+        self._dev_raw = torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, device=dev)
+        self._dev = self._aligned(self._dev_raw)
+        off_ctx = _round(8 * B)
+        off_tab = off_ctx + _round(4 * B)
+        off_pairs = off_tab + _round(4 * B * max_blocks_per_seq)
+        self._offs = (0, off_ctx, off_tab, off_pairs)
+        self.slots_d = self._dev[0:8 * B].view(torch.int64)
+        self.ctx_d = self._dev[off_ctx:off_ctx + 4 * B].view(torch.int32)
+        self.tables_d = self._dev[off_tab:off_tab + 4 * B * max_blocks_per_seq].view(
+            torch.int32).view(B, max_blocks_per_seq)
+        self.pairs_d = self._dev[off_pairs:off_pairs + 8 * B].view(torch.int32).view(B, 2)
         self.out = torch.empty((B, num_heads, cache.head_dim), dtype=cache.dtype, device=dev)
         self.workspace = ops.alloc_workspace(B, num_heads, cache.head_dim,
                                              max_blocks_per_seq * N.BLOCK_SIZE, dev)
+        self._desc = ops.cache_desc(cache.k_cache, cache.v_cache)
+        self._info = N.PaStepInfo()
+        self._sids_ptr = self.sids.ctypes.data
+        self._device = cache.k_cache.device
+        self._kv_shape = (B, cache.num_kv_heads, cache.head_dim)
+        self._q_shape = (B, num_heads, cache.head_dim)
         self._i = 0
         self.last_max_ctx = 0
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
 
-    def _view(self, buf: torch.Tensor, i: int, dtype, shape):
-        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
-        return buf[self._off[i]:self._off[i] + n].view(dtype).view(*shape)
+    @staticmethod
+    def _aligned(t: torch.Tensor) -> torch.Tensor:
+        pad = (-t.data_ptr()) % _ALIGN
+        return t[pad:]
 
-    def reserve(self) -> int:
-        """Host part of a step: reserve slots, pack tables, stage and upload.  Returns max context."""
+    def step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+             attn_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> torch.Tensor:
+        """One decode step (host reservation included).  Returns the output tensor (reused).
+
+        k_new, v_new: [B, Hkv, D] of the step's new tokens; q: [B, H, D]; all
+        contiguous device tensors of the cache dtype.  ``attn_events``, if given,
+        are recorded around the attention pass.
+        """
+        for t, shape in ((k_new, self._kv_shape), (v_new, self._kv_shape), (q, self._q_shape)):
+            if (t.dtype != self.cache.dtype or t.device != self._device
+                    or tuple(t.shape) != shape or not t.is_contiguous()):
+                raise ValueError(f"step inputs: need contiguous {self.cache.dtype} tensors of shape "
+                                 f"{shape} on {self._device}")
+        if attn_events is not None:
+            for e in attn_events:
+                if not e.cuda_event:
+                    e.record(self.stream)        # creates the handle
         buf = self._i & 1
         self._i += 1
         self._staged[buf].synchronize()          # the copy that last read this buffer is done
         pin = self._pinned[buf]
-        slots = self._view(pin, 0, torch.int64, (self.B,)).numpy()
-        ctx = self._view(pin, 1, torch.int32, (self.B,)).numpy()
-        tabs = self._view(pin, 2, torch.int32, (self.B, self.max_blocks)).numpy()
-        pairs = self._view(pin, 3, torch.int32, (self.B, 2)).numpy()
-        _, cows = self.cache.bm.append_batch(self.sids, slots_out=slots)
-        pairs[:len(cows)] = cows
-        self.cache.bm.pack(self.sids, self.max_blocks, tables_out=tabs, ctx_out=ctx)
-        with torch.cuda.stream(self.stream):
-            self._dev.copy_(pin, non_blocking=True)
-            self._staged[buf].record(self.stream)
-        self.last_pairs = cows.copy()
-        self.last_max_ctx = int(ctx.max())
-        return self.last_max_ctx
-
-    def step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
-             attn_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> torch.Tensor:
-        """One decode step (host reservation included).  Returns the output tensor (reused)."""
-        max_ctx = self.reserve()
-        c = self.cache
-        n_cow = len(self.last_pairs)
-        s = self.stream
+        ev = (None, None) if attn_events is None else (attn_events[0].cuda_event,
+                                                       attn_events[1].cuda_event)
+        ws = self.workspace
+        N.check(self._lib.pa_decode_step(
+            self.cache.bm._h, C.byref(self._desc), self.B, self._sids_ptr, k_new.data_ptr(),
+            v_new.data_ptr(), q.data_ptr(), self.H, self.scale, self.out.data_ptr(),
+            ws.data_ptr(), ws.numel(), pin.data_ptr(), self._dev.data_ptr(), self._bytes,
+            self.max_blocks, ev[0], ev[1], C.byref(self._info), self.stream.cuda_stream),
+            "pa_decode_step")
+        self._staged[buf].record(self.stream)
+        n_cow = self._info.num_cow
         if n_cow:
-            ops.copy_blocks(c.k_cache, c.v_cache, self.pairs_d[:n_cow], pairs_host=self.last_pairs,
-                            stream=s)
-        ops.cache_write(c.k_cache, c.v_cache, k_new, v_new, self.slots_d, stream=s)
-        if attn_events is not None:
-            attn_events[0].record(s)
-        ops.decode_attention(c.k_cache, c.v_cache, q, self.tables_d, self.ctx_d, max_ctx, self.scale,
-                             out=self.out, workspace=self.workspace, stream=s)
-        if attn_events is not None:
-            attn_events[1].record(s)
-        ops.decode_merge(c.k_cache, c.v_cache, self.ctx_d, max_ctx, self.out,
-                         workspace=self.workspace, stream=s)
+            o = self._offs[3]
+            self.last_pairs = pin[o:o + 8 * n_cow].view(torch.int32).view(n_cow, 2).numpy().copy()
+        else:
+            self.last_pairs = np.zeros((0, 2), dtype=np.int32)
+        self.last_max_ctx = self._info.max_context_len
         return self.out

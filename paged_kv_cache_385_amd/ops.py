@@ -125,6 +125,24 @@ def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int
     return out
 
 
+def decode_fused(k_cache, v_cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
+                 max_context_len: int, scale: float, out=None, workspace=None,
+                 stream=None) -> torch.Tensor:
+    """pa_decode_fused: store each sequence's newest token, then decode; returns out [B, H, D]."""
+    desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
+                                            workspace)
+    shp = (B, desc.num_kv_heads, desc.head_dim)
+    _need(k_new, k_cache.dtype, k_cache.device, "k_new", shp)
+    _need(v_new, k_cache.dtype, k_cache.device, "v_new", shp)
+    _need(slot_mapping, torch.int64, k_cache.device, "slot_mapping", (B,))
+    N.check(N.lib().pa_decode_fused(C.byref(desc), k_new.data_ptr(), v_new.data_ptr(),
+                                    slot_mapping.data_ptr(), q.data_ptr(), B, H,
+                                    block_tables.data_ptr(), block_tables.shape[1],
+                                    context_lens.data_ptr(), max_context_len, scale, out.data_ptr(),
+                                    ws, wsb, _stream_ptr(stream, q.device)), "pa_decode_fused")
+    return out
+
+
 def decode_attention(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
                      scale: float, out=None, workspace=None, stream=None) -> torch.Tensor:
     desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,

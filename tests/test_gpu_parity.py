@@ -162,3 +162,69 @@ def test_single_token_context_is_exact():
         _, v = wl.seq_kv(b, segs)
         for h in range(8):
             assert torch.equal(out[b, h].cpu(), v[0, h // 4])
+
+
+def _step_inputs(wl, segs, dev="cuda"):
+    """The step's tables, lengths, slots and new tokens from the oracle's block manager."""
+    bm, slots, cows = oracle_step_tables(wl)
+    assert not cows
+    sids = [op[1] for op in wl.step]
+    mb = -(-int(wl.ctx_lens.max()) // 16)
+    tab = np.full((len(sids), mb), -1, dtype=np.int32)
+    for i, s in enumerate(sids):
+        t = bm.block_table(s)
+        tab[i, :len(t)] = t
+    ks, vs = zip(*(segs.tokens(op[2], op[3], 1) for op in wl.step))
+    return (torch.from_numpy(tab).to(dev), torch.from_numpy(wl.ctx_lens.astype(np.int32)).to(dev),
+            torch.tensor(slots, dtype=torch.int64, device=dev), torch.cat(ks).to(dev),
+            torch.cat(vs).to(dev))
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_fused_write_decode_equals_write_then_decode(cfg):
+    from paged_kv_cache_385_amd import alloc_workspace, cache_write, decode, decode_fused
+    wl = make_workload(cfg)
+    say(f"fused store + decode vs separate, workload {cfg}")
+    cache, segs = build_device(wl)
+    tab, ctx, slots, k_new, v_new = _step_inputs(wl, segs)
+    q = wl.q().cuda()
+    mx = int(wl.ctx_lens.max())
+    ws = alloc_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, mx)
+    k2, v2 = cache.k_cache.clone(), cache.v_cache.clone()
+    cache_write(cache.k_cache, cache.v_cache, k_new, v_new, slots)
+    ref = decode(cache.k_cache, cache.v_cache, q, tab, ctx, mx, wl.scale, workspace=ws).clone()
+    out = decode_fused(k2, v2, k_new, v_new, slots, q, tab, ctx, mx, wl.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(k2.view(torch.int16), cache.k_cache.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), cache.v_cache.view(torch.int16))
+    check_close(out, oracle_out(wl, segs), wl.dtype, label=f"fused workload {cfg}")
+
+
+def test_fused_rejects_a_slot_that_is_not_the_last_position():
+    from paged_kv_cache_385_amd import alloc_workspace, decode_fused
+    wl = custom_workload([20, 37, 600, 9], 8, 2, 128, dtype="f16", seed=11)
+    say("fused store: mismatched and negative slots")
+    cache, segs = build_device(wl)
+    tab, ctx, slots, k_new, v_new = _step_inputs(wl, segs)
+    q = wl.q().cuda()
+    mx = int(wl.ctx_lens.max())
+    ws = alloc_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, mx)
+    before_k = cache.k_cache.clone()
+    bad = slots.clone()
+    bad[1] = slots[1] - 1          # an earlier position of sequence 1: rejected, not stored
+    bad[3] = -1                    # not stored; sequence 3 reads the cache as is
+    out = decode_fused(cache.k_cache, cache.v_cache, k_new, v_new, bad, q, tab, ctx, mx, wl.scale,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    assert not torch.isnan(out[[0, 2]].float()).any()
+    ref = oracle_out(wl, segs, seqs=[0, 2])
+    check_close(out, ref, wl.dtype, rows=[0, 2], label="fused, valid rows")
+    # only sequences 0 and 2 stored their token
+    from oracle import layout as OL
+    kd = OL.k_to_logical(cache.k_cache.view(torch.int16).cpu().numpy().view(np.uint16))
+    kb = OL.k_to_logical(before_k.view(torch.int16).cpu().numpy().view(np.uint16))
+    changed = {int(s) for s in np.argwhere((kd != kb).any(axis=(1, 3)))[:, 0] * 16 +
+               np.argwhere((kd != kb).any(axis=(1, 3)))[:, 1]}
+    assert changed == {int(slots[0]), int(slots[2])}

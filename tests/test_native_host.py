@@ -241,3 +241,78 @@ def test_workload_traces_match(cfg):
         t = ref.block_table(s)
         assert tab[i, :len(t)].tolist() == t and (tab[i, len(t):] == -1).all()
     _same_state(nat, ref, sids)
+
+
+# ---- the step entry points ---------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_bm_step_matches_reference(seed):
+    """pa_bm_step = append one token to each sequence, then pack, against the oracle's manager."""
+    rng = np.random.default_rng(50 + seed)
+    nb = 300
+    order = rng.permutation(nb)
+    nat, ref = BlockManager(nb, 16, order), REF.RefBlockManager(nb, 16, order)
+    for s in range(6):
+        nat.add_seq(s)
+        ref.add_seq(s)
+        n = int(rng.integers(0, 60))
+        nat.append_tokens(s, n)
+        ref.append_tokens(s, n)
+    for s in range(6, 9):                       # forks share a partly filled block
+        nat.fork(s - 6, s)
+        ref.fork(s - 6, s)
+    sids = rng.permutation(9).tolist()
+    mb = 8
+    for _ in range(40):
+        slots, cows, tabs, ctx, mx = nat.step(sids, mb)
+        s_ref, c_ref = ref.append_batch(sids)
+        assert slots.tolist() == s_ref and [tuple(p) for p in cows.tolist()] == c_ref
+        assert ctx.tolist() == [ref.seq_len(s) for s in sids] and mx == max(ctx.tolist())
+        for i, s in enumerate(sids):
+            t = ref.block_table(s)
+            assert tabs[i, :len(t)].tolist() == t and (tabs[i, len(t):] == -1).all()
+        _same_state(nat, ref, sids)
+
+
+def test_bm_step_is_all_or_nothing():
+    nat = BlockManager(8, 16)
+    nat.add_seq(0)
+    nat.add_seq(1)
+    nat.append_tokens(0, 32)                     # two full blocks: the next token needs a third
+    nat.append_tokens(1, 5)
+    before = (nat.free_list(), nat.block_table(0), nat.block_table(1), nat.seq_len(0))
+    with pytest.raises(N.PaError):
+        nat.step([1, 0], 2)                      # sequence 0 would need 3 table entries
+    with pytest.raises(N.PaError):
+        nat.step([1, 1], 4)                      # a sequence twice
+    assert (nat.free_list(), nat.block_table(0), nat.block_table(1), nat.seq_len(0)) == before
+    slots, cows, tabs, ctx, mx = nat.step([1, 0], 3)
+    assert ctx.tolist() == [6, 33] and mx == 33 and len(cows) == 0
+
+
+@no_device
+def test_decode_step_rejects_before_the_block_manager_changes():
+    lib = N.lib()
+    c = _cache()
+    bm = BlockManager(8, 16)
+    bm.add_seq(0)
+    bm.append_tokens(0, 3)
+    ids = np.array([0], dtype=np.int64)
+    staging = int(lib.pa_decode_step_staging_bytes(1, 4))
+    assert staging >= 8 + 4 + 16 + 8 and staging % 256 == 0
+    info = N.PaStepInfo()
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, q=FAKE, H=2, out=FAKE, ws=None, wsb=0, sh=FAKE, sd=FAKE,
+                 sb=staging, mb=4)
+        a.update(kw)
+        return lib.pa_decode_step(bm._h, C.byref(c), 1, ids.ctypes.data, a["k"], a["v"], a["q"],
+                                  a["H"], 0.1, a["out"], a["ws"], a["wsb"], a["sh"], a["sd"],
+                                  a["sb"], a["mb"], None, None, C.byref(info), None)
+
+    assert call(sb=staging - 1) == N.PA_ERR_INVALID_ARG             # staging too small
+    assert call(sh=FAKE + 16) == N.PA_ERR_INVALID_ARG                # staging misaligned
+    assert call(k=FAKE + 2) == N.PA_ERR_INVALID_ARG                  # k_new misaligned
+    assert call(H=3) == N.PA_ERR_INVALID_ARG                         # heads not a multiple of Hkv
+    assert call(mb=64) == N.PA_ERR_WORKSPACE                         # 1024 tokens need a workspace
+    assert call(q=None) == N.PA_ERR_INVALID_ARG
+    assert bm.seq_len(0) == 3 and bm.block_table(0) == [0]
