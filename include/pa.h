@@ -117,10 +117,17 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs,
 
 /* ---------------------------------------------------------------------------
  * pa_decode_workspace_size -- bytes of workspace pa_decode needs.
- * Sequences longer than PA_PARTITION_TOKENS are split into partitions whose
+ * Long contexts are split into partitions, each covered by one workgroup, whose
  * partial softmax states (max, sum, unnormalised output; float32) are kept in
- * the workspace and merged by log-sum-exp.  Returns 0 when max_context_len <=
- * PA_PARTITION_TOKENS (no merge) and for invalid arguments.
+ * the workspace and merged by log-sum-exp ("PagedAttention 实战", section
+ * "2026 年的新变化": sequence split).  A launch uses partitions of
+ * PA_PARTITION_TOKENS (512) tokens, or of 1024 tokens when even the longest
+ * possible list of 1024-token items gives every compute unit at least four;
+ * the size returned covers either choice.  Layout: int32 counters[num_seqs *
+ * num_heads] (padded to 256 bytes), then the states.
+ * The counters must be zero before a workspace's first use (allocate it
+ * zero-filled); every completed call leaves them zero.  Returns 0 when
+ * max_context_len <= PA_PARTITION_TOKENS (no merge) and for invalid arguments.
  * ------------------------------------------------------------------------- */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_context_len);
@@ -144,8 +151,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *   context_lens        device, int32[num_seqs], each in [1, max_context_len].
  *   max_context_len     host bound on every context length, <= 16*max_blocks_per_seq.
  *   num_heads           a multiple of num_kv_heads, at most 16 per KV head.
- *   workspace           device, >= pa_decode_workspace_size(...) bytes (may be
- *                       NULL when that size is 0).
+ *   workspace           device, >= pa_decode_workspace_size(...) bytes, 16-byte
+ *                       aligned, counters zero (may be NULL when that size is 0).
+ * When every sequence has at most 8 partitions the merge runs inside the
+ * attention pass: the last workgroup of a (sequence, KV head) to finish, found
+ * with the workspace counter, combines the partitions (one launch); otherwise
+ * a second launch merges.  Calls that share a workspace must not overlap.
  * A sequence with context length outside [1, max_context_len] or a block id
  * outside [0, num_blocks) gets NaN in its output rows.
  * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
@@ -175,16 +186,17 @@ pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* 
                           const int32_t* context_lens, int32_t max_context_len, float scale,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two stages of pa_decode, for callers that time or schedule them apart.
- * pa_decode_attention is the attention pass: one workgroup per (sequence, KV
- * head, 512-token partition) walks its blocks with an online softmax.  For a
- * sequence with one partition it writes out[] itself; otherwise it writes the
- * partition's float32 state (max in log2 units of the scaled score, sum,
- * unnormalised output) to the workspace.  pa_decode_merge combines those states
- * by log-sum-exp ("PagedAttention 实战", section "2026 年的新变化": sequence split)
- * and writes out[] for every sequence with more than one partition.  Same
- * arguments and errors as pa_decode; pa_decode_merge is a no-op when
- * max_context_len <= PA_PARTITION_TOKENS. */
+/* The two stages of pa_decode as separate launches, for callers that time or
+ * schedule them apart.  pa_decode_attention is the attention pass: one
+ * workgroup per (sequence, KV head, partition) walks its blocks with an online
+ * softmax.  For a sequence with one partition it writes out[] itself;
+ * otherwise it writes the partition's float32 state (max in log2 units of the
+ * scaled score, sum, unnormalised output) to the workspace and never merges.
+ * pa_decode_merge combines those states by log-sum-exp and writes out[] for
+ * every sequence with more than one partition; it must be given the same
+ * num_seqs, num_heads and max_context_len (hence the same partition length).
+ * Same arguments and errors as pa_decode; pa_decode_merge is a no-op when
+ * there is a single partition. */
 pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_seqs,
                               int32_t num_heads, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -97,17 +97,11 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
     st = pa_copy_blocks(cache, reinterpret_cast<const int32_t*>(db + l.pairs), pairs_h, n_cow, stream);
     if (st != PA_OK) return st;
   }
-  if (attn_begin && hipEventRecord(static_cast<hipEvent_t>(attn_begin), s) != hipSuccess)
-    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipEventRecord failed");
-  st = pa::decode_fused_attention(cache, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots),
-                                  q, num_seqs, num_heads, reinterpret_cast<const int32_t*>(db + l.tables),
-                                  max_blocks_per_seq, reinterpret_cast<const int32_t*>(db + l.ctx),
-                                  max_ctx, scale, out, workspace, workspace_bytes, stream);
-  if (st != PA_OK) return st;
-  if (attn_end && hipEventRecord(static_cast<hipEvent_t>(attn_end), s) != hipSuccess)
-    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipEventRecord failed");
-  return pa_decode_merge(cache, num_seqs, num_heads, reinterpret_cast<const int32_t*>(db + l.ctx),
-                         max_ctx, out, workspace, workspace_bytes, stream);
+  return pa::decode_run("pa_decode_step", cache, q, num_seqs, num_heads,
+                        reinterpret_cast<const int32_t*>(db + l.tables), max_blocks_per_seq,
+                        reinterpret_cast<const int32_t*>(db + l.ctx), max_ctx, scale, out, workspace,
+                        workspace_bytes, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots),
+                        true, true, attn_begin, attn_end, stream);
 }
 
 }  // extern "C"

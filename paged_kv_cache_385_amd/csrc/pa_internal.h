@@ -19,12 +19,15 @@ pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, i
                        int32_t max_blocks_per_seq, int32_t max_ctx, float scale, void* out,
                        void* workspace, size_t workspace_bytes);
 
-// The attention pass of pa_decode_fused (the new tokens' store included), without the merge.
-pa_status decode_fused_attention(const pa_cache* cache, const void* k_new, const void* v_new,
-                                 const int64_t* slot_mapping, const void* q, int32_t num_seqs,
-                                 int32_t num_heads, const int32_t* block_tables,
-                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                 int32_t max_context_len, float scale, void* out, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+// Every decode entry point: the optional fused store of new tokens (k_new != NULL),
+// the attention pass between the optional events ev_begin / ev_end (hipEvent_t),
+// then, if merge, the log-sum-exp merge (inside the attention pass when
+// fuse_merge allows and the partitions are few, else a second launch).
+pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                     int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, bool merge, bool fuse_merge, void* ev_begin,
+                     void* ev_end, void* stream);
 
 }  // namespace pa

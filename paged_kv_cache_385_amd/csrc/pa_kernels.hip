@@ -27,6 +27,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <vector>
 
@@ -159,6 +160,7 @@ struct DecodeArgs {
   const uint16_t* k_new;       // [B][Hkv][D] new tokens, or NULL: no fused store
   const uint16_t* v_new;
   const int64_t* new_slots;    // [B]
+  int32_t* counters; // [B][Hkv] partitions finished, or NULL: the merge is a separate launch
   float2* ws_ml;     // [B][H][P] (max in log2 units, sum)
   float* ws_acc;     // [B][H][P][D] unnormalised output
   int32_t num_seqs, num_heads, num_kv_heads, group;
@@ -166,6 +168,19 @@ struct DecodeArgs {
   int32_t part_blocks;  // blocks per partition (32 or 64)
   float scale_log2;     // scale * log2(e)
 };
+
+// Stores and loads of partition states that another workgroup of the same launch
+// reads: agent-scope relaxed atomics, which stay coherent across the XCDs' L2
+// caches without any cache-wide write-back or invalidation (agent-scope fences
+// do both and made the pass several times slower).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's stores are performed (vmcnt counts stores on gfx9).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ int32_t wave_sum_i(int32_t x) {
 #pragma unroll
@@ -520,10 +535,56 @@ void decode_attn_kernel(DecodeArgs a) {
     } else {
       const int64_t st = (static_cast<int64_t>(b) * a.num_heads + kvh * G + hh) * a.max_parts + p;
       if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
-      *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
-      if (d == 0) a.ws_ml[st] = poisoned ? float2{0.f, NAN} : float2{Mh, L};
+      const float2 ml = poisoned ? float2{0.f, NAN} : float2{Mh, L};
+      if (a.counters) {
+        // read by another workgroup of this launch: device-coherent stores
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store_coherent(a.ws_acc + st * D + d + r, o[r]);
+        if (d == 0) {
+          store_coherent(&a.ws_ml[st].x, ml.x);
+          store_coherent(&a.ws_ml[st].y, ml.y);
+        }
+      } else {
+        *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
+        if (d == 0) a.ws_ml[st] = ml;
+      }
     }
   }
+  if (nparts == 1 || a.counters == nullptr) return;
+
+  // Fused merge: the last of the sequence's partitions (for this KV head) to
+  // finish combines all of them.  Its partial stores are complete (waited for)
+  // before the count is raised, and the merging workgroup reads the states with
+  // device-coherent loads after it has seen the count reach nparts - 1.
+  __shared__ int32_t s_ticket;
+  wait_stores();
+  __syncthreads();
+  int32_t* counter = a.counters + static_cast<int64_t>(b) * a.num_kv_heads + kvh;
+  if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != nparts - 1) return;
+  for (int32_t i4 = tid; i4 < G * (D / 4); i4 += kThreads) {
+    const int32_t hh = i4 / (D / 4);
+    const int32_t d = (i4 - hh * (D / 4)) * 4;
+    const int64_t st0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G + hh) * a.max_parts;
+    float M = -INFINITY;
+    for (int32_t u = 0; u < nparts; ++u) M = fmaxf(M, load_coherent(&a.ws_ml[st0 + u].x));
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t u = 0; u < nparts; ++u) {
+      const float wgt = fast_exp2(load_coherent(&a.ws_ml[st0 + u].x) - M);
+      L += wgt * load_coherent(&a.ws_ml[st0 + u].y);
+      const float* src = a.ws_acc + (st0 + u) * D + d;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] += wgt * load_coherent(src + r);
+    }
+    const float inv = 1.f / L;
+    u16x4 ov;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+    *reinterpret_cast<u16x4*>(a.out + q_row0 + static_cast<int64_t>(hh) * D + d) = ov;
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- decode: log-sum-exp merge -----------------------------------------------------
@@ -534,17 +595,6 @@ struct MergeArgs {
   const float* ws_acc;
   int32_t num_seqs, num_heads, max_ctx, max_parts, part_tokens;
 };
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 
 // One wave per (sequence, query head): M = max_p m_p, w_p = 2^(m_p - M),
 // out = sum_p w_p acc_p / sum_p w_p l_p.  Lane l owns D/64 consecutive dims; the
@@ -563,15 +613,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
   const int64_t st0 = static_cast<int64_t>(row) * a.max_parts;
   const float2* ml = a.ws_ml + st0;
 
-  float mx = -INFINITY;
-  for (int32_t i = lane; i < nparts; i += 64) mx = fmaxf(mx, ml[i].x);
-  const float M = wave_max(mx);
-  float lsum = 0.f;
-  for (int32_t i = lane; i < nparts; i += 64) {
+  // Every lane forms M and L itself, in partition order: the same arithmetic, in
+  // the same order, as the merge inside the attention pass, so both give the
+  // same bits.
+  float M = -INFINITY;
+  for (int32_t i = 0; i < nparts; ++i) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  for (int32_t i = 0; i < nparts; ++i) {
     const float2 v = ml[i];
-    lsum += fast_exp2(v.x - M) * v.y;
+    L += fast_exp2(v.x - M) * v.y;
   }
-  const float L = wave_sum(lsum);
 
   float o[V];
 #pragma unroll
@@ -662,7 +713,23 @@ int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx)
   return items >= 4 * static_cast<int64_t>(device_cus()) ? kLongPartTokens : kPartTokens;
 }
 
-size_t ws_ml_bytes(int64_t rows) { return (static_cast<size_t>(rows) * sizeof(float2) + 255) & ~size_t(255); }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t ws_ml_bytes(int64_t rows) { return round256(static_cast<size_t>(rows) * sizeof(float2)); }
+// Workspace: counters int32[B][H] (zero between calls) | (max, sum) float2[rows] | acc float[rows][D]
+size_t ws_counter_bytes(int64_t num_seqs, int64_t num_heads) {
+  return round256(static_cast<size_t>(num_seqs) * num_heads * sizeof(int32_t));
+}
+// The merge runs inside the attention pass when a sequence has at most this many partitions.
+constexpr int32_t kMaxFusedParts = 8;
+
+// PA_FUSED_MERGE=0 in the environment keeps the merge a separate launch (read once).
+bool fused_merge_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_FUSED_MERGE");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
 
 struct DecodeSetup {
   DecodeArgs args;
@@ -715,8 +782,10 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.new_slots = nullptr;
-  a.ws_ml = need ? static_cast<float2*>(workspace) : nullptr;
-  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_ml_bytes(rows)) : nullptr;
+  a.counters = nullptr;
+  char* wsb = static_cast<char*>(workspace) + ws_counter_bytes(num_seqs, num_heads);
+  a.ws_ml = need ? reinterpret_cast<float2*>(wsb) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(wsb + ws_ml_bytes(rows)) : nullptr;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = cache->num_kv_heads;
@@ -767,30 +836,62 @@ pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, i
   return PA_OK;
 }
 
-pa_status decode_fused_attention(const pa_cache* cache, const void* k_new, const void* v_new,
-                                 const int64_t* slot_mapping, const void* q, int32_t num_seqs,
-                                 int32_t num_heads, const int32_t* block_tables,
-                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                 int32_t max_context_len, float scale, void* out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+// Every decode entry point: optional fused store of the new tokens (k_new != NULL),
+// the attention pass (between the optional events), and the merge -- inside the
+// attention pass when fuse_merge and every sequence has at most kMaxFusedParts
+// partitions, else as a second launch.  merge == false stops after the attention
+// pass (the partition states stay in the workspace).
+pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                     int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, bool merge, bool fuse_merge, void* ev_begin,
+                     void* ev_end, void* stream) {
   pa::clear_error();
   DecodeSetup su;
-  pa_status st = prepare_decode("pa_decode_fused", cache, q, num_seqs, num_heads, block_tables,
-                                max_blocks_per_seq, context_lens, max_context_len, scale, out,
-                                workspace, workspace_bytes, true, &su);
+  pa_status st = prepare_decode(fn, cache, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
+                                context_lens, max_context_len, scale, out, workspace,
+                                workspace_bytes, true, &su);
   if (st != PA_OK || num_seqs == 0) return st;
-  if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
-      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_fused: k_new / v_new / slot_mapping NULL or misaligned");
-  su.args.k_new = static_cast<const uint16_t*>(k_new);
-  su.args.v_new = static_cast<const uint16_t*>(v_new);
-  su.args.new_slots = slot_mapping;
+  if (k_new) {
+    if (!v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+      return pa::fail(PA_ERR_INVALID_ARG, "%s: k_new / v_new / slot_mapping NULL or misaligned", fn);
+    su.args.k_new = static_cast<const uint16_t*>(k_new);
+    su.args.v_new = static_cast<const uint16_t*>(v_new);
+    su.args.new_slots = slot_mapping;
+  }
+  const int32_t P = su.args.max_parts;
+  if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())
+    su.args.counters = static_cast<int32_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
   if (cache->dtype == PA_F16)
     launch_attn<F16>(su, cache->head_dim, s);
   else
     launch_attn<BF16>(su, cache->head_dim, s);
-  return launch_status("pa_decode_fused");
+  st = launch_status(fn);
+  if (st != PA_OK) return st;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
+  if (!merge || P <= 1 || su.args.counters) return PA_OK;
+  MergeArgs m;
+  m.ctx_lens = context_lens;
+  m.out = static_cast<uint16_t*>(out);
+  m.ws_ml = su.args.ws_ml;
+  m.ws_acc = su.args.ws_acc;
+  m.num_seqs = num_seqs;
+  m.num_heads = num_heads;
+  m.max_ctx = max_context_len;
+  m.max_parts = P;
+  m.part_tokens = su.args.part_blocks * kBlock;
+  const int64_t grid = (static_cast<int64_t>(num_seqs) * num_heads + 3) / 4;
+  if (cache->dtype == PA_F16)
+    launch_merge<F16>(m, grid, cache->head_dim, s);
+  else
+    launch_merge<BF16>(m, grid, cache->head_dim, s);
+  return launch_status(fn);
 }
 
 }  // namespace pa
@@ -863,7 +964,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= kPartTokens) return 0;
   const int64_t P = parts_for(max_context_len, kPartTokens);
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * P;
-  return ws_ml_bytes(rows) + static_cast<size_t>(rows) * head_dim * sizeof(float);
+  return ws_counter_bytes(num_seqs, num_heads) + ws_ml_bytes(rows) +
+         static_cast<size_t>(rows) * head_dim * sizeof(float);
 }
 
 pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_seqs,
@@ -871,32 +973,10 @@ pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t max_context_len, float scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  pa::clear_error();
-  DecodeSetup su;
-  pa_status st = prepare_decode("pa_decode_attention", cache, q, num_seqs, num_heads, block_tables,
-                                max_blocks_per_seq, context_lens, max_context_len, scale, out,
-                                workspace, workspace_bytes, true, &su);
-  if (st != PA_OK || num_seqs == 0) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache->dtype == PA_F16)
-    launch_attn<F16>(su, cache->head_dim, s);
-  else
-    launch_attn<BF16>(su, cache->head_dim, s);
-  return launch_status("pa_decode_attention");
-}
-
-pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* v_new,
-                          const int64_t* slot_mapping, const void* q, int32_t num_seqs,
-                          int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t max_context_len, float scale,
-                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  pa_status st = pa::decode_fused_attention(cache, k_new, v_new, slot_mapping, q, num_seqs,
-                                            num_heads, block_tables, max_blocks_per_seq,
-                                            context_lens, max_context_len, scale, out, workspace,
-                                            workspace_bytes, stream);
-  if (st != PA_OK) return st;
-  return pa_decode_merge(cache, num_seqs, num_heads, context_lens, max_context_len, out, workspace,
-                         workspace_bytes, stream);
+  return pa::decode_run("pa_decode_attention", cache, q, num_seqs, num_heads, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                        workspace_bytes, nullptr, nullptr, nullptr, false, false, nullptr, nullptr,
+                        stream);
 }
 
 pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_heads,
@@ -919,8 +999,6 @@ pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_h
   m.max_parts = su.args.max_parts;
   m.part_tokens = su.args.part_blocks * kBlock;
   const int64_t grid = (static_cast<int64_t>(num_seqs) * num_heads + 3) / 4;
-  if (static_cast<int64_t>(num_seqs) * num_heads > INT32_MAX)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode_merge: grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->dtype == PA_F16)
     launch_merge<F16>(m, grid, cache->head_dim, s);
@@ -933,12 +1011,22 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  pa_status st = pa_decode_attention(cache, q, num_seqs, num_heads, block_tables,
-                                     max_blocks_per_seq, context_lens, max_context_len, scale, out,
-                                     workspace, workspace_bytes, stream);
-  if (st != PA_OK) return st;
-  return pa_decode_merge(cache, num_seqs, num_heads, context_lens, max_context_len, out, workspace,
-                         workspace_bytes, stream);
+  return pa::decode_run("pa_decode", cache, q, num_seqs, num_heads, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                        workspace_bytes, nullptr, nullptr, nullptr, true, true, nullptr, nullptr,
+                        stream);
+}
+
+pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* v_new,
+                          const int64_t* slot_mapping, const void* q, int32_t num_seqs,
+                          int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new) return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_fused: k_new is NULL");
+  return pa::decode_run("pa_decode_fused", cache, q, num_seqs, num_heads, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                        workspace_bytes, k_new, v_new, slot_mapping, true, true, nullptr, nullptr,
+                        stream);
 }
 
 }  // extern "C"

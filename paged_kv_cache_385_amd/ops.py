@@ -91,8 +91,14 @@ def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len
 
 
 def alloc_workspace(num_seqs, num_heads, head_dim, max_context_len, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace: its leading counters must be zero before the first call."""
     n = workspace_size(num_seqs, num_heads, head_dim, max_context_len)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def workspace_counter_bytes(num_seqs: int, num_heads: int) -> int:
+    """Bytes of the workspace's leading counter region (kept zero between calls)."""
+    return (4 * num_seqs * num_heads + 255) // 256 * 256
 
 
 def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace):

@@ -57,7 +57,10 @@ def run_step(wl, cache, segs, max_blocks=None):
     batch = DecodeBatch(cache, sids, wl.num_heads, wl.scale, max_blocks)
     # NaN in the output and the partition workspace: a work item the kernels skip shows up
     batch.out.fill_(float("nan"))
-    batch.workspace.view(torch.float32)[: batch.workspace.numel() // 4].fill_(float("nan"))
+    from paged_kv_cache_385_amd.ops import workspace_counter_bytes
+    c = workspace_counter_bytes(batch.B, batch.H)
+    if batch.workspace.numel() > c:
+        batch.workspace[c:].view(torch.float32).fill_(float("nan"))
     ks, vs = zip(*(segs.tokens(op[2], op[3], 1) for op in wl.step))
     k_new = torch.cat(ks).to(cache.device)
     v_new = torch.cat(vs).to(cache.device)

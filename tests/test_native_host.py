@@ -108,8 +108,9 @@ def test_workspace_size():
     for B, H, D, mc in ((8, 32, 128, 131072), (128, 64, 128, 4096), (3, 5, 64, 513)):
         P = -(-mc // 512)
         n = lib.pa_decode_workspace_size(B, H, D, mc)
-        assert n >= B * H * P * (D + 2) * 4                          # states fit
-        assert n < B * H * P * (D + 2) * 4 + 512
+        counters = -(-4 * B * H // 256) * 256                        # zeroed counter region
+        assert n >= counters + B * H * P * (D + 2) * 4               # counters and states fit
+        assert n < counters + B * H * P * (D + 2) * 4 + 512
 
 
 # ---- native block manager vs the oracle's -------------------------------------------------
