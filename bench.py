@@ -33,6 +33,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 METRIC = "paged-attn decode KV GB/s read (% of HBM peak); sequence-steps/s"
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc", "pa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_traffic.json")
+CONTEXT_TEXT = {
+    1: "17, 33, 64, 100 tokens",
+    2: "uniform in [128, 2048]",
+    3: "lognormal median 1024, sigma 1, clipped to [16, 4096]",
+    4: "16 prompts x 8 samples: 1024 + U{1..15} shared prefix tokens, U{0..512} private",
+    5: "uniform in [32768, 131072]",
+}
 
 
 def parse():
@@ -45,7 +54,64 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --copy-calibration MIB' into the per-launch traffic file")
     return ap.parse_args()
+
+
+def source_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def summarize_counters(args):
+    """Per-launch HBM traffic of the attention kernel from two counter runs.
+
+    Each counter is scaled by what it reads for the calibration copy (a plain
+    device copy of known size run by the same command): bytes moved / counter.
+    The timed launches are the last ``--steps`` attention dispatches.
+    """
+    import csv
+    out = {"kernel": None, "workload": args.workload, "steps": args.steps, "warmup": args.warmup,
+           "copy_bytes": args.copy_calibration << 20}
+    for name, path in (("fetch", args.summarize_counters[0]), ("write", args.summarize_counters[1])):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        attn = [r for r in rows if "decode_attn_kernel" in r["Kernel_Name"]]
+        first = int(attn[0]["Dispatch_Id"])
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first]
+        calib = copies[-3:]                       # the three calibration copies come last
+        kib = float(np.mean([float(r["Counter_Value"]) for r in calib]))
+        scale = out["copy_bytes"] / (kib * 1024.0)
+        timed = attn[-args.steps:]
+        mean_kib = float(np.mean([float(r["Counter_Value"]) for r in timed]))
+        out[f"{name}_counter"] = timed[0]["Counter_Name"]
+        out[f"{name}_copy_kib"] = kib
+        out[f"{name}_scale"] = round(scale, 4)
+        out[f"{name}_kib_per_launch"] = round(mean_kib, 1)
+        out[f"{name}_bytes_per_launch"] = int(mean_kib * 1024.0 * scale)
+        out["kernel"] = timed[0]["Kernel_Name"]
+        out["launches"] = len(timed)
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    out["source_sha256"] = source_sha256()
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def recorded_traffic(workload: int, steps: int, warmup: int):
+    """Traffic per launch from the counter file, if it was taken on this kernel source and run."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("source_sha256") != source_sha256() or t.get("workload") != workload
+            or t.get("steps") != steps or t.get("warmup") != warmup):
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def log(msg):
@@ -81,6 +147,9 @@ def cpu_baseline(wl, budget_s: float):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -184,14 +253,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": 16, "kv_dtype": wl.dtype_name,
-                   "context": "lognormal median 1024, sigma 1, clipped to [16, 4096]",
+                   "context": CONTEXT_TEXT[wl.cfg_id],
                    "mean_context": round(float(base_ctx.mean() + W + (K - 1) / 2), 1),
                    "num_blocks": wl.num_blocks},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(B * K / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_attn_kernel<BF16,128>",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload, K, W),
+                     "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}>",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "bytes_per_launch": int(attn_bytes)},
     }
