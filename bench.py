@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3 = 70B-shaped GQA-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--upload", action="store_true",
+                    help="copy the staged tables to the device each step instead of reading them in place")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
@@ -183,7 +185,7 @@ def main():
     segs.clear()
     sids = [op[1] for op in wl.step]
     max_blocks = -(-(int(wl.ctx_lens.max()) + K + W) // 16)
-    batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks)
+    batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, zero_copy=not args.upload)
     q = wl.q().to(dev)
     steps_kv = []
     for i in range(K + W):

@@ -289,7 +289,10 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
  *   1. runs pa_bm_step for seq_ids on the host, writing slots, lengths, tables
  *      and copy-on-write pairs into staging_host (pinned host memory) in the
  *      layout below;
- *   2. enqueues one copy of that region to staging_dev (device memory);
+ *   2. enqueues one copy of that region to staging_dev (device memory) -- or,
+ *      when staging_dev is NULL, nothing: the kernels read staging_host in
+ *      place (it must then be pinned host memory mapped for the device, as
+ *      hipHostMalloc returns);
  *   3. enqueues pa_copy_blocks (if any pair), pa_cache_write of k_new/v_new
  *      ([num_seqs][num_kv_heads][head_dim], token i belongs to seq_ids[i]),
  *      pa_decode_attention and pa_decode_merge, all on `stream`.

@@ -6,7 +6,8 @@
 // shared block gets its private copy before it writes):
 //   1. host: the block manager reserves every sequence's next slot, reporting
 //      copy-on-write pairs, and packs tables and lengths into the staging buffer;
-//   2. one host-to-device copy of the staging buffer;
+//   2. one host-to-device copy of the staging buffer -- or none: with no device
+//      staging buffer the kernels read the pinned one in place;
 //   3. pa_copy_blocks for the pairs, then pa_decode_fused (the new tokens'
 //      store and the decode in one attention pass, then the merge) -- all on
 //      the caller's stream.
@@ -54,8 +55,9 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
                          pa_step_info* info, void* stream) {
   pa::clear_error();
   if (!bm || !cache || num_seqs <= 0 || !seq_ids || !k_new || !v_new || !q || !out ||
-      !staging_host || !staging_dev || max_blocks_per_seq <= 0)
+      !staging_host || max_blocks_per_seq <= 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: bad arguments");
+  const bool zero_copy = staging_dev == nullptr;
   const StagingLayout l = layout(num_seqs, max_blocks_per_seq);
   if (staging_bytes < l.total)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: staging %zu bytes, %zu needed",
@@ -90,9 +92,17 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t upload = n_cow ? l.pairs + sizeof(int32_t) * 2 * n_cow : l.pairs;
-  if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, s) != hipSuccess)
-    return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
+  if (zero_copy) {
+    // the kernels read the pinned staging buffer in place, over the host link
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, staging_host, 0) != hipSuccess || !dp)
+      return pa::fail(PA_ERR_HIP, "pa_decode_step: staging_host is not pinned, mapped host memory");
+    db = static_cast<char*>(dp);
+  } else {
+    const size_t upload = n_cow ? l.pairs + sizeof(int32_t) * 2 * n_cow : l.pairs;
+    if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, s) != hipSuccess)
+      return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
+  }
   if (n_cow) {
     st = pa_copy_blocks(cache, reinterpret_cast<const int32_t*>(db + l.pairs), pairs_h, n_cow, stream);
     if (st != PA_OK) return st;

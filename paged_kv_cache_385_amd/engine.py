@@ -104,14 +104,17 @@ class DecodeBatch:
     """Decode steps for a fixed list of sequences on one stream.
 
     ``step`` is one ``pa_decode_step`` call: the native block manager reserves
-    the slots and packs the tables into a pinned staging buffer, which is copied
-    to the device, then the copy-on-write copy, the cache write and the decode
-    are enqueued.  Two pinned buffers alternate so the host can prepare step
-    i + 1 while the copy of step i may still be pending.
+    the slots and packs the tables into a pinned staging buffer, which the
+    kernels read in place (``zero_copy``) or which is first copied to the
+    device, then the copy-on-write copy, the cache write and the decode are
+    enqueued.  Two pinned buffers alternate so the host can prepare step i + 1
+    while step i may still read its buffer.  ``slots_d``, ``ctx_d``,
+    ``tables_d`` and ``pairs_d`` view the last step's staged values.
     """
 
     def __init__(self, cache: PagedKVCache, sids: Sequence[int], num_heads: int, scale: float,
-                 max_blocks_per_seq: int, stream: Optional[torch.cuda.Stream] = None):
+                 max_blocks_per_seq: int, stream: Optional[torch.cuda.Stream] = None,
+                 zero_copy: bool = True):
         self.cache = cache
         self.sids = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
         self.B = B = len(self.sids)
@@ -119,6 +122,8 @@ class DecodeBatch:
         self.scale = float(scale)
         self.max_blocks = max_blocks_per_seq
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
+        # zero_copy: the kernels read the pinned staging buffer in place (no upload)
+        self.zero_copy = zero_copy
         dev = cache.device
         lib = N.lib()
         self._lib = lib
@@ -134,11 +139,13 @@ class DecodeBatch:
         off_tab = off_ctx + _round(4 * B)
         off_pairs = off_tab + _round(4 * B * max_blocks_per_seq)
         self._offs = (0, off_ctx, off_tab, off_pairs)
-        self.slots_d = self._dev[0:8 * B].view(torch.int64)
-        self.ctx_d = self._dev[off_ctx:off_ctx + 4 * B].view(torch.int32)
-        self.tables_d = self._dev[off_tab:off_tab + 4 * B * max_blocks_per_seq].view(
+        self._slots_d = self._dev[0:8 * B].view(torch.int64)
+        self._ctx_d = self._dev[off_ctx:off_ctx + 4 * B].view(torch.int32)
+        self._tables_d = self._dev[off_tab:off_tab + 4 * B * max_blocks_per_seq].view(
             torch.int32).view(B, max_blocks_per_seq)
-        self.pairs_d = self._dev[off_pairs:off_pairs + 8 * B].view(torch.int32).view(B, 2)
+        self._pairs_d = self._dev[off_pairs:off_pairs + 8 * B].view(torch.int32).view(B, 2)
+        self._last_buf = None
+        self._dev_current = True
         self.out = torch.empty((B, num_heads, cache.head_dim), dtype=cache.dtype, device=dev)
         self.workspace = ops.alloc_workspace(B, num_heads, cache.head_dim,
                                              max_blocks_per_seq * N.BLOCK_SIZE, dev)
@@ -151,6 +158,32 @@ class DecodeBatch:
         self._i = 0
         self.last_max_ctx = 0
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
+
+    def _staged_dev(self) -> None:
+        """With zero_copy, bring the last step's staged values to the device buffer."""
+        if not self._dev_current and self._last_buf is not None:
+            self._dev.copy_(self._pinned[self._last_buf], non_blocking=False)
+            self._dev_current = True
+
+    @property
+    def slots_d(self) -> torch.Tensor:
+        self._staged_dev()
+        return self._slots_d
+
+    @property
+    def ctx_d(self) -> torch.Tensor:
+        self._staged_dev()
+        return self._ctx_d
+
+    @property
+    def tables_d(self) -> torch.Tensor:
+        self._staged_dev()
+        return self._tables_d
+
+    @property
+    def pairs_d(self) -> torch.Tensor:
+        self._staged_dev()
+        return self._pairs_d
 
     @staticmethod
     def _aligned(t: torch.Tensor) -> torch.Tensor:
@@ -184,10 +217,13 @@ class DecodeBatch:
         N.check(self._lib.pa_decode_step(
             self.cache.bm._h, C.byref(self._desc), self.B, self._sids_ptr, k_new.data_ptr(),
             v_new.data_ptr(), q.data_ptr(), self.H, self.scale, self.out.data_ptr(),
-            ws.data_ptr(), ws.numel(), pin.data_ptr(), self._dev.data_ptr(), self._bytes,
+            ws.data_ptr(), ws.numel(), pin.data_ptr(),
+            None if self.zero_copy else self._dev.data_ptr(), self._bytes,
             self.max_blocks, ev[0], ev[1], C.byref(self._info), self.stream.cuda_stream),
             "pa_decode_step")
         self._staged[buf].record(self.stream)
+        self._last_buf = buf
+        self._dev_current = not self.zero_copy
         n_cow = self._info.num_cow
         if n_cow:
             o = self._offs[3]
