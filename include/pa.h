@@ -64,9 +64,17 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
 /* Tokens of context one decode workgroup covers before partitions are merged. */
 #define PA_PARTITION_TOKENS 512
 
+/* Hint for pa_cache.flags: blocks may be referenced by several sequences of one
+ * call (shared prefixes).  The decode then reads K/V through the caches so that
+ * sequences sharing a block can hit on it; without the hint it streams K/V with
+ * non-temporal loads, which read HBM faster when every block is read once.
+ * Results are the same bits either way. */
+#define PA_CACHE_SHARED_BLOCKS 1
+
 /* A KV pool pair.  k_cache and v_cache are device pointers in the layout above,
  * 16-byte aligned, each num_blocks*num_kv_heads*16*head_dim elements of dtype.
- * block_size must be 16; head_dim must be 64 or 128. */
+ * block_size must be 16; head_dim must be 64 or 128; flags is 0 or
+ * PA_CACHE_SHARED_BLOCKS. */
 typedef struct pa_cache {
   void* k_cache;
   void* v_cache;
@@ -75,6 +83,7 @@ typedef struct pa_cache {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;            /* pa_dtype */
+  int32_t flags;            /* PA_CACHE_* hints */
 } pa_cache;
 
 /* ---------------------------------------------------------------------------
@@ -305,6 +314,8 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
  * 16 * max_blocks_per_seq) bytes.  attn_begin / attn_end: optional hipEvent_t
  * recorded around the attention pass (NULL to skip).  info (optional) receives
  * the number of copy-on-write pairs and the longest context of the step.
+ * The decode reads through the caches (PA_CACHE_SHARED_BLOCKS) whenever the
+ * block manager holds a block with more than one reference.
  * Every argument is checked before the block manager changes; after that only
  * PA_ERR_HIP can occur.
  * ========================================================================= */

@@ -35,6 +35,16 @@ struct pa_bm {
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
   std::unordered_map<int32_t, int32_t> scratch_drop;  // reused by batch planning
+  int64_t n_shared = 0;             // blocks with refcount > 1
+
+  void ref_inc(int32_t b) {
+    if (++ref[b] == 2) ++n_shared;
+  }
+  // returns the new count
+  int32_t ref_dec(int32_t b) {
+    if (ref[b]-- == 2) --n_shared;
+    return ref[b];
+  }
 
   Seq* find(int64_t id) {
     auto it = seqs.find(id);
@@ -63,7 +73,7 @@ struct pa_bm {
       const int32_t last = s.table.back();
       if (ref[last] > 1) {
         blk = pop_free();
-        ref[last] -= 1;
+        ref_dec(last);
         s.table.back() = blk;
         *cow_src = last;
         *cow_dst = blk;
@@ -257,7 +267,7 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!p) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_fork: no sequence %lld", (long long)parent);
   if (bm->find(child)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: sequence %lld exists", (long long)child);
   Seq c = *p;
-  for (int32_t b : c.table) bm->ref[b] += 1;
+  for (int32_t b : c.table) bm->ref_inc(b);
   bm->seqs.emplace(child, std::move(c));
   return PA_OK;
 }
@@ -268,7 +278,7 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (it == bm->seqs.end()) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_free_seq: no sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& t = it->second.table;
   for (auto r = t.rbegin(); r != t.rend(); ++r) {
-    if (--bm->ref[*r] == 0) bm->free_stack.push_back(*r);
+    if (bm->ref_dec(*r) == 0) bm->free_stack.push_back(*r);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -344,6 +354,14 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
   return PA_OK;
 }
 
+}  // extern "C"
+
+namespace pa {
+int64_t bm_shared_blocks(const pa_bm* bm) { return bm->n_shared; }
+}  // namespace pa
+
+extern "C" {
+
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* out) {
   if (!bm || !out || block < 0 || block >= bm->num_blocks)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: bad arguments");
@@ -373,12 +391,12 @@ pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
       o = std::max<int32_t>(o, static_cast<int32_t>(fill));
     }
   }
-  int64_t used = 0, shared = 0, occ = 0;
+  int64_t used = 0, occ = 0;
   for (int32_t b = 0; b < bm->num_blocks; ++b) {
     used += bm->ref[b] > 0;
-    shared += bm->ref[b] > 1;
     occ += occupied[b];
   }
+  const int64_t shared = bm->n_shared;   // kept up to date by every reference change
   out->num_blocks = bm->num_blocks;
   out->free_blocks = static_cast<int64_t>(bm->free_stack.size());
   out->used_blocks = used;

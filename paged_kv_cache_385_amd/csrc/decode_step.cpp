@@ -107,7 +107,10 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
     st = pa_copy_blocks(cache, reinterpret_cast<const int32_t*>(db + l.pairs), pairs_h, n_cow, stream);
     if (st != PA_OK) return st;
   }
-  return pa::decode_run("pa_decode_step", cache, q, num_seqs, num_heads,
+  // blocks shared by several sequences are read through the caches
+  pa_cache c = *cache;
+  if (pa::bm_shared_blocks(bm) > 0) c.flags |= PA_CACHE_SHARED_BLOCKS;
+  return pa::decode_run("pa_decode_step", &c, q, num_seqs, num_heads,
                         reinterpret_cast<const int32_t*>(db + l.tables), max_blocks_per_seq,
                         reinterpret_cast<const int32_t*>(db + l.ctx), max_ctx, scale, out, workspace,
                         workspace_bytes, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots),

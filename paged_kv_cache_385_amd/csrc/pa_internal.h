@@ -12,6 +12,9 @@ namespace pa {
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
+// Blocks of the manager whose reference count is above one (kept up to date).
+int64_t bm_shared_blocks(const pa_bm* bm);
+
 // Argument checks of pa_decode for a call whose context lengths are at most
 // max_ctx, with a workspace of at least pa_decode_workspace_size(..., max_ctx)
 // bytes; enqueues nothing.

@@ -43,7 +43,8 @@ def _stream_ptr(stream, device) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
-def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> N.PaCache:
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, shared_blocks: bool = False) -> N.PaCache:
+    """Descriptor of a pool pair; ``shared_blocks``: blocks may be shared within one call."""
     if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DT:
         raise TypeError("pools must both be float16 or both bfloat16")
     if not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
@@ -51,7 +52,8 @@ def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> N.PaCache:
     nb, hkv, dc, bs, eight = k_cache.shape
     if eight != 8 or bs != N.BLOCK_SIZE or tuple(v_cache.shape) != v_pool_shape(nb, hkv, dc * 8):
         raise ValueError(f"pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} do not match the layout")
-    return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, dc * 8, _DT[k_cache.dtype])
+    return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, dc * 8, _DT[k_cache.dtype],
+                     N.PA_CACHE_SHARED_BLOCKS if shared_blocks else 0)
 
 
 def _need(t: torch.Tensor, dtype, device, name, shape=None):
@@ -101,8 +103,9 @@ def workspace_counter_bytes(num_seqs: int, num_heads: int) -> int:
     return (4 * num_seqs * num_heads + 255) // 256 * 256
 
 
-def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace):
-    desc = cache_desc(k_cache, v_cache)
+def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace,
+                 shared_blocks=False):
+    desc = cache_desc(k_cache, v_cache, shared_blocks)
     B, H, D = q.shape
     _need(q, k_cache.dtype, k_cache.device, "q")
     if D != desc.head_dim:
@@ -120,10 +123,10 @@ def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace
 
 
 def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int, scale: float,
-           out=None, workspace=None, stream=None) -> torch.Tensor:
+           out=None, workspace=None, stream=None, shared_blocks: bool = False) -> torch.Tensor:
     """pa_decode: attention pass then log-sum-exp merge; returns out [B, H, D]."""
     desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
-                                            workspace)
+                                            workspace, shared_blocks)
     N.check(N.lib().pa_decode(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
                               block_tables.shape[1], context_lens.data_ptr(), max_context_len,
                               scale, out.data_ptr(), ws, wsb, _stream_ptr(stream, q.device)),

@@ -255,3 +255,21 @@ def test_merge_in_attention_pass_equals_separate_merge(cfg):
     from paged_kv_cache_385_amd.ops import workspace_counter_bytes
     c = workspace_counter_bytes(wl.num_seqs, wl.num_heads)
     assert int(ws[:c].count_nonzero()) == 0
+
+
+def test_shared_block_hint_gives_the_same_bits():
+    """Cached (shared-prefix hint) and streaming K/V loads compute the same result."""
+    from paged_kv_cache_385_amd import alloc_workspace, decode
+    wl = make_workload(4)
+    say("cached vs streaming loads, workload 4")
+    cache, segs = build_device(wl)
+    out_step, batch = run_step(wl, cache, segs)
+    mx = int(wl.ctx_lens.max())
+    q = wl.q().cuda()
+    ws = alloc_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, mx)
+    a = decode(cache.k_cache, cache.v_cache, q, batch.tables_d, batch.ctx_d, mx, wl.scale,
+               workspace=ws, shared_blocks=True).clone()
+    b = decode(cache.k_cache, cache.v_cache, q, batch.tables_d, batch.ctx_d, mx, wl.scale,
+               workspace=ws, shared_blocks=False).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, out_step)

@@ -72,6 +72,15 @@ def test_cache_descriptor_validation(kw, status):
 
 
 @no_device
+def test_cache_flags_validation():
+    lib = N.lib()
+    c = _cache(flags=4)
+    assert lib.pa_decode(C.byref(c), FAKE, 1, 2, FAKE, 1, FAKE, 16, 0.1, FAKE, FAKE, 4096, None) \
+        == N.PA_ERR_INVALID_ARG
+    assert b"flags" in lib.pa_last_error()
+
+
+@no_device
 def test_call_validation():
     lib = N.lib()
     c = _cache()
