@@ -181,9 +181,10 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
  * followed by pa_decode(...), when token i (k_new[i], v_new[i], [Hkv][D]) is
  * the newest token of sequence i: its slot is the last context position,
  *     slot_mapping[i] == block_tables[i][(n_i - 1) / 16] * 16 + (n_i - 1) % 16,
- * which is what the block manager's append returns.  The workgroup that reads
- * that position stores the token first, so no separate cache-write launch runs
- * and the new token is read back from the cache it was written to.
+ * which is what the block manager's append returns.  The wave that reads that
+ * position puts the token into the tile it loaded and stores it to the cache
+ * from there, so no separate cache-write launch runs and nothing waits for the
+ * store.
  *   slot_mapping[i] < 0    the token is not stored (the cache is read as is);
  *   any other mismatch     the token is not stored and sequence i's output is NaN;
  *   invalid context length sequence i's output is NaN and its token is not stored.

@@ -333,40 +333,6 @@ void decode_attn_kernel(DecodeArgs a) {
   }
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
 
-  // Fused store of the step's new token (pa_decode_fused): the workgroup of the
-  // sequence's last partition writes the token's K and V for its KV head into
-  // the slot, then reads the cache as usual.  Only this workgroup reads that
-  // position, so a workgroup barrier orders the store before the reads.  A slot
-  // that is not the sequence's last position is not written, and the sequence's
-  // output becomes NaN.
-  bool slot_bad = false;
-  if (a.new_slots != nullptr && p == nparts - 1) {
-    const int64_t slot = a.new_slots[b];
-    if (slot >= 0) {
-      const int32_t last = ctx - 1;
-      const int32_t off = last % kBlock;
-      const int32_t phys = bt[last / kBlock];
-      if (phys >= 0 && phys < a.num_blocks && slot == static_cast<int64_t>(phys) * kBlock + off) {
-        if (w == 0 && lane < 2 * (D / 8)) {
-          const int32_t c = lane % (D / 8);
-          const int64_t src = (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * D + 8 * c;
-          const int64_t tile = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * (kBlock * D);
-          if (lane < D / 8) {
-            store16(a.k_dst + tile + (static_cast<int64_t>(c) * kBlock + off) * 8, load16(a.k_new + src));
-          } else {
-            const u16x8 vv = __builtin_bit_cast(u16x8, load16(a.v_new + src));
-            uint16_t* vdst = a.v_dst + tile + (static_cast<int64_t>(off >> 2) * D + 8 * c) * 4 + (off & 3);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vdst[4 * i] = vv[i];
-          }
-        }
-        __syncthreads();
-      } else {
-        slot_bad = true;
-      }
-    }
-  }
-
   // q fragments: B operand of q.K^T, dims 32kk + 8*g4 .. +7 of head n (zero for n >= G)
   u32x4 qf[KK];
 #pragma unroll
@@ -390,7 +356,55 @@ void decode_attn_kernel(DecodeArgs a) {
   if (lane < nw) ids = bt[first + kWaves * lane];
   const bool id_bad = lane < nw && (ids < 0 || ids >= a.num_blocks);
   if (id_bad) ids = 0;
+
+  // Fused store of the step's new token (pa_decode_fused).  The sequence's last
+  // position sits in its last block, the st_i-th block of one wave of the last
+  // partition's workgroup.  That wave loads the token's K and V
+  // fragments alongside q, puts them into the loaded tile in registers (the
+  // cache still holds the old bytes there when the tile is read) and stores them
+  // into the cache from the same registers and addresses.  No other workgroup
+  // reads that position.  A slot that is not the sequence's last position is not
+  // written and poisons the sequence's output; a negative slot stores nothing.
+  // The fragments wait in the wave's (not yet used) LDS combine area.
+  bool st_on = false, slot_bad = false;
+  int32_t st_i = -1, st_off = 0;
+  u32x4* st_k = reinterpret_cast<u32x4*>(&s_acc[w][0]) + lane * KK;          // [64][KK]
+  uint32_t* st_v = reinterpret_cast<uint32_t*>(&s_acc[w][0]) + 64 * 4 * KK + lane * KK;
+  u32x4 kpatch[KK];
+  uint32_t vpatch[KK];
+  if (a.new_slots != nullptr && p == nparts - 1) {
+    const int64_t slot = a.new_slots[b];
+    const int32_t jl = nblk - 1 - p * PB;       // last block, within the partition
+    if (slot >= 0 && (jl & (kWaves - 1)) == w) {
+      st_i = jl / kWaves;
+      st_off = (ctx - 1) % kBlock;
+      const int32_t phys = __builtin_amdgcn_readlane(ids, st_i);
+      const bool phys_bad = __builtin_amdgcn_readlane(id_bad ? 1 : 0, st_i) != 0;
+      st_on = !phys_bad && slot == static_cast<int64_t>(phys) * kBlock + st_off;
+      slot_bad = !st_on;
+      const int64_t src = (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * D;
+      if (st_on && n == st_off) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kpatch[kk] = load16(a.k_new + src + 32 * kk + 8 * g4);
+      }
+      if (st_on && g4 == (st_off >> 2)) {
+#pragma unroll
+        for (int j2 = 0; j2 < KK; ++j2)
+          vpatch[j2] = *reinterpret_cast<const uint32_t*>(a.v_new + src + 32 * j2 + 2 * n);
+      }
+    }
+  }
   const bool bad_blk = __ballot(id_bad) != 0 || slot_bad;
+  auto stash_patch = [&]() {   // after the first tile loads are issued
+    if (st_on && n == st_off) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) st_k[kk] = kpatch[kk];
+    }
+    if (st_on && g4 == (st_off >> 2)) {
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2) st_v[j2] = vpatch[j2];
+    }
+  };
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -417,6 +431,32 @@ void decode_attn_kernel(DecodeArgs a) {
   // Block i of the wave; i >= nw is a padding step whose positions are all masked,
   // which leaves m_run, l_run and acc unchanged (m_run is finite by then).
   auto compute_block = [&](int buf, int32_t i) {
+    if (st_on && i == st_i) {
+      const int32_t phys = __builtin_amdgcn_readlane(ids, i);
+      uint16_t* kt = a.k_dst + phys * blk_stride + head_off;
+      uint16_t* vt = a.v_dst + phys * blk_stride + head_off;
+      if (n == st_off) {          // K row st_off: 8 dims per lane per step
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          kb[buf][kk] = st_k[kk];
+          store16(kt + (kk * 64 + lane) * 8, kb[buf][kk]);
+        }
+      }
+      if (g4 == (st_off >> 2)) {  // V column st_off: dims 2n, 2n + 1 per lane per step
+        const int32_t e = st_off & 3;
+#pragma unroll
+        for (int j2 = 0; j2 < KK; ++j2) {
+          u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+          const uint32_t pv = st_v[j2];
+          vv[e] = static_cast<uint16_t>(pv & 0xffff);
+          vv[e + 4] = static_cast<uint16_t>(pv >> 16);
+          vb[buf][j2] = __builtin_bit_cast(u32x4, vv);
+          uint16_t* vd = vt + ((g4 * D) + 32 * j2 + 2 * n) * 4 + e;
+          vd[0] = vv[e];
+          vd[4] = vv[e + 4];
+        }
+      }
+    }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
@@ -472,6 +512,7 @@ void decode_attn_kernel(DecodeArgs a) {
   // first wait of the compute that follows it.
   if (nw > 0) {
     load_block(0, 0);
+    stash_patch();
     for (int32_t i = 0; i < nw; i += 2) {
       load_block(1, min(i + 1, nw - 1));
       __builtin_amdgcn_sched_barrier(0);
