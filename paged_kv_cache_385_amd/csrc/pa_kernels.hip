@@ -93,10 +93,17 @@ struct BF16 {
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-// K/V tiles are read once per launch: a streaming (non-temporal) load keeps them
-// from displacing reusable lines and reads HBM markedly faster on gfx950.
-__device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// A buffer resource for `bytes` bytes at p (raw buffer, no swizzle; word 3 is
+// the gfx9 default format).  Loads past `bytes` return zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, bytes, 0x00020000);
+}
+// 16 bytes of a K/V tile.  Tiles are read once per launch unless blocks are
+// shared: the streaming form sets the non-temporal bit, which keeps them from
+// displacing reusable lines and reads HBM markedly faster on gfx950.
+template <bool kStream>
+__device__ __forceinline__ u32x4 load_tile(__amdgpu_buffer_rsrc_t r, int32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kStream ? 2 : 0));
 }
 __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
@@ -414,18 +421,19 @@ void decode_attn_kernel(DecodeArgs a) {
 
   u32x4 kb[2][KK], vb[2][KK];
 
+  // Tiles are read with buffer loads whose resource covers exactly the tile; a
+  // step past the wave's last block (i >= nw) gets an empty range, so its loads
+  // return zeros without touching memory and the loop needs no branch.
   auto load_block = [&](int buf, int32_t i) {
-    const int32_t phys = __builtin_amdgcn_readlane(ids, i);
-    const uint16_t* kt = a.k_cache + phys * blk_stride + head_off;
-    const uint16_t* vt = a.v_cache + phys * blk_stride + head_off;
+    const int32_t phys = __builtin_amdgcn_readlane(ids, min(i, nw - 1));
+    const int32_t bytes = i < nw ? static_cast<int32_t>(tile_elems * sizeof(uint16_t)) : 0;
+    const auto kr = tile_rsrc(a.k_cache + phys * blk_stride + head_off, bytes);
+    const auto vr = tile_rsrc(a.v_cache + phys * blk_stride + head_off, bytes);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      kb[buf][kk] = kStream ? load16_stream(kt + (kk * 64 + lane) * 8) : load16(kt + (kk * 64 + lane) * 8);
+    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
 #pragma unroll
-    for (int j2 = 0; j2 < KK; ++j2) {
-      const uint16_t* pv = vt + ((g4 * D) + 32 * j2 + 2 * n) * 4;
-      vb[buf][j2] = kStream ? load16_stream(pv) : load16(pv);
-    }
+    for (int j2 = 0; j2 < KK; ++j2)
+      vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
   };
 
   // Block i of the wave; i >= nw is a padding step whose positions are all masked,
@@ -514,10 +522,10 @@ void decode_attn_kernel(DecodeArgs a) {
     load_block(0, 0);
     stash_patch();
     for (int32_t i = 0; i < nw; i += 2) {
-      load_block(1, min(i + 1, nw - 1));
+      load_block(1, i + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute_block(0, i);
-      load_block(0, min(i + 2, nw - 1));
+      load_block(0, i + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute_block(1, i + 1);
     }
