@@ -129,10 +129,11 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs,
  * Long contexts are split into partitions, each covered by one workgroup, whose
  * partial softmax states (max, sum, unnormalised output; float32) are kept in
  * the workspace and merged by log-sum-exp ("PagedAttention 实战", section
- * "2026 年的新变化": sequence split).  A launch uses partitions of
- * PA_PARTITION_TOKENS (512) tokens, or of 1024 tokens when even the longest
- * possible list of 1024-token items gives every compute unit at least four;
- * the size returned covers either choice.  Layout: int32 counters[num_seqs *
+ * "2026 年的新变化": sequence split).  A launch uses partitions of 4096, 2048
+ * or 1024 tokens -- the longest for which even the longest possible list of
+ * items gives every workgroup slot of the device (three per compute unit) two
+ * of them -- else of PA_PARTITION_TOKENS (512) tokens; the size returned
+ * covers every choice.  Layout: int32 counters[num_seqs *
  * num_heads] (padded to 256 bytes), then the states.
  * The counters must be zero before a workspace's first use (allocate it
  * zero-filled); every completed call leaves them zero.  Returns 0 when
@@ -299,18 +300,23 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
  *   1. runs pa_bm_step for seq_ids on the host, writing slots, lengths, tables
  *      and copy-on-write pairs into staging_host (pinned host memory) in the
  *      layout below;
- *   2. enqueues one copy of that region to staging_dev (device memory) -- or,
- *      when staging_dev is NULL, nothing: the kernels read staging_host in
- *      place (it must then be pinned host memory mapped for the device, as
- *      hipHostMalloc returns);
- *   3. enqueues pa_copy_blocks (if any pair), pa_cache_write of k_new/v_new
- *      ([num_seqs][num_kv_heads][head_dim], token i belongs to seq_ids[i]),
- *      pa_decode_attention and pa_decode_merge, all on `stream`.
+ *   2. enqueues one copy of that region to staging_dev (device memory) -- on
+ *      `stream`, or, when copy_stream is given, on copy_stream, records
+ *      copy_event (a hipEvent_t) there and makes `stream` wait for it, so the
+ *      copy can run while earlier work of `stream` still runs -- or, when
+ *      staging_dev is NULL, nothing: the kernels read staging_host in place (it
+ *      must then be pinned host memory mapped for the device, as hipHostMalloc
+ *      returns);
+ *   3. enqueues pa_copy_blocks (if any pair), then pa_decode_fused: the store
+ *      of k_new/v_new ([num_seqs][num_kv_heads][head_dim], token i belongs to
+ *      seq_ids[i]) and the decode, all on `stream`.
  * Staging layout (each part 256-byte aligned, both buffers 256-byte aligned and
  * at least pa_decode_step_staging_bytes() long): int64 slots[n] | int32 ctx[n] |
  * int32 tables[n][max_blocks_per_seq] | int32 pairs[n][2].  staging_host must
- * not be rewritten while an earlier copy from it may still be pending (the
- * caller alternates two buffers or waits on an event).
+ * not be rewritten while an earlier copy from it may still be pending, nor
+ * staging_dev while kernels of an earlier step may still read it (the caller
+ * alternates two buffers of each and waits on events; with copy_stream, it
+ * makes copy_stream wait for the end of the step that last read staging_dev).
  * workspace: at least pa_decode_workspace_size(n, num_heads, head_dim,
  * 16 * max_blocks_per_seq) bytes.  attn_begin / attn_end: optional hipEvent_t
  * recorded around the attention pass (NULL to skip).  info (optional) receives
@@ -331,7 +337,7 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
                          float scale, void* out, void* workspace, size_t workspace_bytes,
                          void* staging_host, void* staging_dev, size_t staging_bytes,
                          int32_t max_blocks_per_seq, void* attn_begin, void* attn_end,
-                         pa_step_info* info, void* stream);
+                         pa_step_info* info, void* copy_stream, void* copy_event, void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,10 +46,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = PA_BLOCK_SIZE;                       // tokens per block
 constexpr int kPartTokens = PA_PARTITION_TOKENS;            // shortest partition (512)
-constexpr int kLongPartTokens = 2 * PA_PARTITION_TOKENS;    // partition of large launches
+constexpr int kMaxPartTokens = 8 * PA_PARTITION_TOKENS;     // longest partition (4096)
 constexpr int kWaves = 4;                                   // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxParts = 1024;                             // longest context / 512
+#ifndef PA_SIZE_CLASSES
+#define PA_SIZE_CLASSES 4
+#endif
+constexpr int kClasses = PA_SIZE_CLASSES;                   // size classes of last partitions
+static_assert(kClasses >= 1 && kClasses <= 64, "one lane per size class");
 
 // ---- element traits --------------------------------------------------------------
 struct F16 {
@@ -177,7 +182,8 @@ struct DecodeArgs {
   float* ws_acc;     // [B][H][P][D] unnormalised output
   int32_t num_seqs, num_heads, num_kv_heads, group;
   int32_t max_blocks, max_ctx, num_blocks, max_parts;
-  int32_t part_blocks;  // blocks per partition (32 or 64)
+  int32_t part_blocks;  // blocks per partition (32 .. 256)
+  int32_t part_shift;   // log2(part_blocks)
   float scale_log2;     // scale * log2(e)
 };
 
@@ -213,21 +219,39 @@ __device__ __forceinline__ int32_t kth_set_lane(uint64_t mask, int32_t k, int32_
   return __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
 }
 
-// How a sequence splits into work items: `nfull` partitions of part_blocks blocks,
-// then at most one shorter partition whose size class (0..3, quarters of a
-// partition) is `cls`, or -1 when there is none.  A context length outside
-// [1, max_ctx] is one item of class 0 (its workgroup writes NaN).
-__device__ __forceinline__ void seq_items(int32_t ctx, int32_t max_ctx, int32_t pb, int32_t* nfull,
-                                          int32_t* cls) {
+// How a sequence splits into work items: `nfull` partitions of 2^pbs blocks,
+// then at most one shorter partition whose size class (0 .. kClasses - 1, in
+// steps of 1/kClasses of a partition) is `cls`, or -1 when there is none.  A context length outside
+// [1, max_ctx] is one item of class 0 (its workgroup writes NaN); a lane past
+// the last sequence (live == false) has no items.
+__device__ __forceinline__ void seq_items(int32_t ctx, bool live, int32_t max_ctx, int32_t pbs,
+                                          int32_t* nfull, int32_t* cls) {
+  if (!live) {
+    *nfull = 0;
+    *cls = -1;
+    return;
+  }
   if (ctx < 1 || ctx > max_ctx) {
     *nfull = 0;
     *cls = 0;
     return;
   }
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  *nfull = nblk / pb;
-  const int32_t rem = nblk - *nfull * pb;
-  *cls = rem ? (4 * rem) / pb : -1;
+  *nfull = nblk >> pbs;
+  const int32_t rem = nblk & ((1 << pbs) - 1);
+  *cls = rem ? (kClasses * rem) >> pbs : -1;
+}
+
+// Context lengths are read kPlanChunks x 64 at a time: all loads of a group are
+// in flight together, and for up to 256 sequences the second pass reuses them.
+constexpr int kPlanChunks = 4;
+__device__ __forceinline__ void load_ctx_group(const DecodeArgs& a, int32_t c0, int32_t lane,
+                                               int32_t cv[kPlanChunks]) {
+#pragma unroll
+  for (int k = 0; k < kPlanChunks; ++k) {
+    const int32_t i = c0 + 64 * k + lane;
+    cv[k] = i < a.num_seqs ? a.ctx_lens[i] : 0;
+  }
 }
 
 // Work item of this workgroup.  Every partition of every sequence and KV head is
@@ -238,67 +262,109 @@ __device__ __forceinline__ void seq_items(int32_t ctx, int32_t max_ctx, int32_t 
 // positions so that each of the 8 XCDs (which take workgroup ids round-robin)
 // gets 8 consecutive positions out of every 64.  Returns false for a workgroup
 // beyond the list (the launch is sized for the longest possible list).  Every
-// lane of every wave computes the same answer from the context lengths.
+// lane of every wave computes the same answer from the context lengths; the
+// item's context length comes back in *octx.
 __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_t* okvh,
-                          int32_t* op) {
-  const int32_t B = a.num_seqs, pb = a.part_blocks, hkv = a.num_kv_heads;
-  int32_t nfull_tot = 0;
-  int32_t cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
-  for (int32_t c = 0; c < B; c += 64) {
-    int32_t nf = 0, cl = -1;
-    if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
-    nfull_tot += wave_sum_i(nf);
-    cnt0 += __popcll(__ballot(cl == 0));
-    cnt1 += __popcll(__ballot(cl == 1));
-    cnt2 += __popcll(__ballot(cl == 2));
-    cnt3 += __popcll(__ballot(cl == 3));
+                          int32_t* op, int32_t* octx) {
+  const int32_t B = a.num_seqs, pbs = a.part_shift, hkv = a.num_kv_heads;
+  constexpr int32_t kGroup = 64 * kPlanChunks;
+  int32_t cv0[kPlanChunks];            // the first group, kept for the second pass
+  load_ctx_group(a, 0, lane, cv0);
+  int32_t nfull_tot = 0, n_part = 0;
+  int32_t cnt = 0;                     // lane c: sequences whose last partition has class c
+  for (int32_t c0 = 0; c0 < B; c0 += kGroup) {
+    int32_t cv[kPlanChunks];
+    if (c0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kPlanChunks; ++k) cv[k] = cv0[k];
+    } else {
+      load_ctx_group(a, c0, lane, cv);
+    }
+#pragma unroll
+    for (int k = 0; k < kPlanChunks; ++k) {
+      int32_t nf, cl;
+      seq_items(cv[k], c0 + 64 * k + lane < B, a.max_ctx, pbs, &nf, &cl);
+      nfull_tot += wave_sum_i(nf);
+      n_part += __popcll(__ballot(cl >= 0));
+#pragma unroll 1
+      for (int32_t c = 0; c < kClasses; ++c) {
+        const int32_t nc = __popcll(__ballot(cl == c));
+        cnt += lane == c ? nc : 0;
+      }
+    }
   }
   const int32_t n_full = nfull_tot * hkv;
-  const int32_t n_items = n_full + (cnt0 + cnt1 + cnt2 + cnt3) * hkv;
+  const int32_t n_items = n_full + n_part * hkv;
   int32_t i = blockIdx.x;
   if (i >= n_items) return false;
   if (i < (n_items & ~63)) i = (i & ~63) | ((i & 7) << 3) | ((i >> 3) & 7);
 
-  if (i < n_full) {
-    const int32_t kvh = i / nfull_tot;
-    const int32_t j = i - kvh * nfull_tot;          // j-th full partition in sequence order
-    int32_t base = 0;
-    for (int32_t c = 0; c < B; c += 64) {
-      int32_t nf = 0, cl;
-      if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
-      const int32_t incl = base + wave_incl_scan_i(nf, lane);
-      const uint64_t hit = __ballot(incl - nf <= j && j < incl);
+  // Second pass: find the item's sequence.  In the full-partition part the
+  // target is the j-th full partition in sequence order; in the class part, the
+  // k-th sequence of class cls.
+  const bool full = i < n_full;
+  int32_t kvh, j = 0, cls = -1, k = 0;
+  if (full) {
+    kvh = i / nfull_tot;
+    j = i - kvh * nfull_tot;
+  } else {
+    // classes from the largest down; r indexes into class cls
+    int32_t r = i - n_full;
+    int32_t ccount = 0;
+    for (int32_t c = kClasses - 1; c >= 0; --c) {
+      const int32_t cc = __builtin_amdgcn_readlane(cnt, c);
+      if (r < cc * hkv) {
+        cls = c;
+        ccount = cc;
+        break;
+      }
+      r -= cc * hkv;
+    }
+    kvh = r / ccount;
+    k = r - kvh * ccount;
+  }
+  int32_t base = 0;
+  for (int32_t c0 = 0; c0 < B; c0 += kGroup) {
+    int32_t cv[kPlanChunks];
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kPlanChunks; ++u) cv[u] = cv0[u];
+    } else {
+      load_ctx_group(a, c0, lane, cv);
+    }
+#pragma unroll
+    for (int u = 0; u < kPlanChunks; ++u) {
+      int32_t nf, cl;
+      seq_items(cv[u], c0 + 64 * u + lane < B, a.max_ctx, pbs, &nf, &cl);
+      uint64_t hit;
+      int32_t part = 0;
+      if (full) {
+        const int32_t incl = base + wave_incl_scan_i(nf, lane);
+        hit = __ballot(incl - nf <= j && j < incl);
+        if (hit) {
+          const int32_t l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+          part = j - (__shfl(incl, l) - __shfl(nf, l));
+        }
+        base = __shfl(incl, 63);
+      } else {
+        const uint64_t m = __ballot(cl == cls);
+        const int32_t pc = __popcll(m);
+        hit = 0;
+        if (k < pc) {
+          hit = 1ull << kth_set_lane(m, k, lane);
+          part = __shfl(nf, __ffsll(static_cast<unsigned long long>(hit)) - 1);
+        }
+        k -= pc;
+      }
       if (hit) {
         const int32_t l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        *ob = c + l;
+        *ob = c0 + 64 * u + l;
         *okvh = kvh;
-        *op = j - (__shfl(incl, l) - __shfl(nf, l));
+        *op = part;
+        *octx = __shfl(cv[u], l);
         return true;
       }
-      base = __shfl(incl, 63);
     }
-    return false;   // not reached
-  }
-  int32_t r = i - n_full;
-  int32_t cls = 3, cnt = cnt3;
-  if (r >= cnt3 * hkv) { r -= cnt3 * hkv; cls = 2; cnt = cnt2;
-    if (r >= cnt2 * hkv) { r -= cnt2 * hkv; cls = 1; cnt = cnt1;
-      if (r >= cnt1 * hkv) { r -= cnt1 * hkv; cls = 0; cnt = cnt0; } } }
-  const int32_t kvh = r / cnt;
-  int32_t k = r - kvh * cnt;                        // k-th sequence of the class
-  for (int32_t c = 0; c < B; c += 64) {
-    int32_t nf = 0, cl = -1;
-    if (c + lane < B) seq_items(a.ctx_lens[c + lane], a.max_ctx, pb, &nf, &cl);
-    const uint64_t m = __ballot(cl == cls);
-    const int32_t pc = __popcll(m);
-    if (k < pc) {
-      const int32_t l = kth_set_lane(m, k, lane);
-      *ob = c + l;
-      *okvh = kvh;
-      *op = __shfl(nf, l);
-      return true;
-    }
-    k -= pc;
   }
   return false;     // not reached
 }
@@ -317,16 +383,16 @@ void decode_attn_kernel(DecodeArgs a) {
   const int32_t tid = threadIdx.x;
   const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t lane = tid & 63;
-  int32_t b, kvh, p;
-  if (!plan_item(a, lane, &b, &kvh, &p)) return;
+  int32_t b, kvh, p, ctx;
+  if (!plan_item(a, lane, &b, &kvh, &p, &ctx)) return;
   b = __builtin_amdgcn_readfirstlane(b);
   kvh = __builtin_amdgcn_readfirstlane(kvh);
   p = __builtin_amdgcn_readfirstlane(p);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int32_t G = a.group;
   const int32_t PB = a.part_blocks;
 
   if (b >= a.num_seqs || kvh >= a.num_kv_heads) return;   // cannot happen; keeps every read in bounds
-  const int32_t ctx = a.ctx_lens[b];
   const bool bad_ctx = ctx < 1 || ctx > a.max_ctx;
   const int32_t nparts = bad_ctx ? 1 : (ctx + PB * kBlock - 1) / (PB * kBlock);
   if (p < 0 || p >= nparts) return;
@@ -764,13 +830,18 @@ int32_t device_cus() {
   return n;
 }
 
-// Partition length of one launch: 1024 tokens when even the longest possible
-// list of 1024-token items gives every compute unit at least 4 of them (fewer,
-// longer items cost less start-up and workspace traffic), else 512 tokens.
+// Partition length of one launch: the longest of 4096, 2048 and 1024 tokens for
+// which even the longest possible item list gives every workgroup slot of the
+// device (three per compute unit) two items, else 512 tokens.  A longer item
+// spends less of its time on start-up and combine per byte it reads; two items
+// per slot keep enough of them for the largest-first order to balance the slots.
 int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
-  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads *
-                        parts_for(max_ctx, kLongPartTokens);
-  return items >= 4 * static_cast<int64_t>(device_cus()) ? kLongPartTokens : kPartTokens;
+  const int64_t slots = 3 * static_cast<int64_t>(device_cus());
+  for (int32_t pt = kMaxPartTokens; pt > kPartTokens; pt /= 2) {
+    const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * parts_for(max_ctx, pt);
+    if (items >= 2 * slots) return pt;
+  }
+  return kPartTokens;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -856,6 +927,7 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.num_blocks = cache->num_blocks;
   a.max_parts = P;
   a.part_blocks = PT / kBlock;
+  a.part_shift = __builtin_ctz(static_cast<unsigned>(PT / kBlock));
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   su->grid = grid;
   su->shared_blocks = (cache->flags & PA_CACHE_SHARED_BLOCKS) != 0;
