@@ -5,7 +5,8 @@ Workload: the 70B-shaped GQA-8 decode layer (128 sequences, 64 query heads,
 8 KV heads, head_dim 128, bf16 cache, context lengths lognormal with median
 1024 clipped to [16, 4096], blocks of 16 tokens placed at random).  One step
 is the whole hot path for the batch: the host block manager reserves the next
-slot of every sequence and packs the tables, one pinned upload, the
+slot of every sequence and packs the tables into pinned memory, one upload of
+them (on a side stream, overlapping the previous step's kernels), the
 copy-on-write copy (none arise here), the slot-mapped cache write of the 128
 new tokens, the attention pass and the log-sum-exp merge.  Contexts grow by
 one token per step, as in real decoding.
@@ -51,8 +52,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3 = 70B-shaped GQA-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--upload", action="store_true",
-                    help="copy the staged tables to the device each step instead of reading them in place")
+    ap.add_argument("--staging", choices=("mapped", "upload", "side"), default="side",
+                    help="how the step's staged tables reach the kernels: read in place from pinned "
+                         "host memory, copied on the step's stream, or copied on a side stream "
+                         "(overlapping the previous step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
@@ -185,7 +188,7 @@ def main():
     segs.clear()
     sids = [op[1] for op in wl.step]
     max_blocks = -(-(int(wl.ctx_lens.max()) + K + W) // 16)
-    batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, zero_copy=not args.upload)
+    batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, staging=args.staging)
     q = wl.q().to(dev)
     steps_kv = []
     for i in range(K + W):

@@ -90,7 +90,7 @@ SIGNATURES = {
     "pa_decode_step_staging_bytes": (C.c_size_t, [_I32, _I32]),
     "pa_decode_step": (C.c_int, [_P, C.POINTER(PaCache), _I32, _P, _P, _P, _P, _I32, C.c_float, _P,
                                  _P, C.c_size_t, _P, _P, C.c_size_t, _I32, _P, _P,
-                                 C.POINTER(PaStepInfo), _P]),
+                                 C.POINTER(PaStepInfo), _P, _P, _P]),
 }
 
 _lib = None

@@ -6,8 +6,10 @@
 // shared block gets its private copy before it writes):
 //   1. host: the block manager reserves every sequence's next slot, reporting
 //      copy-on-write pairs, and packs tables and lengths into the staging buffer;
-//   2. one host-to-device copy of the staging buffer -- or none: with no device
-//      staging buffer the kernels read the pinned one in place;
+//   2. one host-to-device copy of the staging buffer -- on the caller's stream,
+//      or on a copy stream that the caller's stream then waits for (the copy
+//      of step i + 1 can run while step i's kernels still run) -- or none: with
+//      no device staging buffer the kernels read the pinned one in place;
 //   3. pa_copy_blocks for the pairs, then pa_decode_fused (the new tokens'
 //      store and the decode in one attention pass, then the merge) -- all on
 //      the caller's stream.
@@ -52,12 +54,14 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
                          float scale, void* out, void* workspace, size_t workspace_bytes,
                          void* staging_host, void* staging_dev, size_t staging_bytes,
                          int32_t max_blocks_per_seq, void* attn_begin, void* attn_end,
-                         pa_step_info* info, void* stream) {
+                         pa_step_info* info, void* copy_stream, void* copy_event, void* stream) {
   pa::clear_error();
   if (!bm || !cache || num_seqs <= 0 || !seq_ids || !k_new || !v_new || !q || !out ||
       !staging_host || max_blocks_per_seq <= 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: bad arguments");
   const bool zero_copy = staging_dev == nullptr;
+  if (copy_stream && (zero_copy || !copy_event))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: a copy stream needs staging_dev and copy_event");
   const StagingLayout l = layout(num_seqs, max_blocks_per_seq);
   if (staging_bytes < l.total)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_step: staging %zu bytes, %zu needed",
@@ -100,8 +104,14 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
     db = static_cast<char*>(dp);
   } else {
     const size_t upload = n_cow ? l.pairs + sizeof(int32_t) * 2 * n_cow : l.pairs;
-    if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, s) != hipSuccess)
+    hipStream_t cs = copy_stream ? static_cast<hipStream_t>(copy_stream) : s;
+    if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, cs) != hipSuccess)
       return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
+    if (copy_stream) {
+      hipEvent_t ev = static_cast<hipEvent_t>(copy_event);
+      if (hipEventRecord(ev, cs) != hipSuccess || hipStreamWaitEvent(s, ev, 0) != hipSuccess)
+        return pa::fail(PA_ERR_HIP, "pa_decode_step: copy-stream event failed");
+    }
   }
   if (n_cow) {
     st = pa_copy_blocks(cache, reinterpret_cast<const int32_t*>(db + l.pairs), pairs_h, n_cow, stream);

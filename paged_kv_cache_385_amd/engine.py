@@ -104,17 +104,25 @@ class DecodeBatch:
     """Decode steps for a fixed list of sequences on one stream.
 
     ``step`` is one ``pa_decode_step`` call: the native block manager reserves
-    the slots and packs the tables into a pinned staging buffer, which the
-    kernels read in place (``zero_copy``) or which is first copied to the
-    device, then the copy-on-write copy, the cache write and the decode are
-    enqueued.  Two pinned buffers alternate so the host can prepare step i + 1
-    while step i may still read its buffer.  ``slots_d``, ``ctx_d``,
-    ``tables_d`` and ``pairs_d`` view the last step's staged values.
+    the slots and packs the tables into a pinned staging buffer, then the
+    copy-on-write copy and the fused store + decode are enqueued.  ``staging``
+    says how the kernels get the staged values:
+
+    * ``"mapped"``: they read the pinned buffer in place (no copy);
+    * ``"upload"``: one copy to a device buffer on the step's stream;
+    * ``"side"``: the copy runs on a side stream and the step's stream waits
+      for it, so the copy of step i + 1 overlaps the kernels of step i.
+
+    The default is "side"; ``zero_copy`` is the older switch (True: "mapped",
+    False: "upload"), and an explicit ``staging`` wins over it.  Two pinned buffers (and, for "side", two device
+    buffers) alternate so the host can prepare step i + 1 while step i may
+    still read its buffer.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d``
+    view the last step's staged values.
     """
 
     def __init__(self, cache: PagedKVCache, sids: Sequence[int], num_heads: int, scale: float,
                  max_blocks_per_seq: int, stream: Optional[torch.cuda.Stream] = None,
-                 zero_copy: bool = True):
+                 zero_copy: Optional[bool] = None, staging: Optional[str] = None):
         self.cache = cache
         self.sids = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
         self.B = B = len(self.sids)
@@ -122,8 +130,16 @@ class DecodeBatch:
         self.scale = float(scale)
         self.max_blocks = max_blocks_per_seq
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
-        # zero_copy: the kernels read the pinned staging buffer in place (no upload)
-        self.zero_copy = zero_copy
+        if staging is not None:
+            mode = staging
+        elif zero_copy is None:
+            mode = "side"
+        else:
+            mode = "mapped" if zero_copy else "upload"
+        if mode not in ("mapped", "upload", "side"):
+            raise ValueError(f"staging must be 'mapped', 'upload' or 'side', not {mode!r}")
+        self.staging = mode
+        self.zero_copy = mode == "mapped"
         dev = cache.device
         lib = N.lib()
         self._lib = lib
@@ -133,18 +149,23 @@ class DecodeBatch:
                             for _ in range(2)]
         self._pinned = [self._aligned(t) for t in self._pinned_raw]
         self._staged = [torch.cuda.Event() for _ in range(2)]
-        self._dev_raw = torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, device=dev)
-        self._dev = self._aligned(self._dev_raw)
+        n_dev = 2 if mode == "side" else 1
+        self._dev_raw = [torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, device=dev)
+                         for _ in range(n_dev)]
+        self._dev = [self._aligned(t) for t in self._dev_raw]
+        self._copy_stream = None
+        self._copied = []
+        if mode == "side":
+            self._copy_stream = torch.cuda.Stream(dev)       # default priority
+            self._copied = [torch.cuda.Event() for _ in range(2)]
+            for e in self._copied:
+                e.record(self._copy_stream)                  # creates the handles
         off_ctx = _round(8 * B)
         off_tab = off_ctx + _round(4 * B)
         off_pairs = off_tab + _round(4 * B * max_blocks_per_seq)
         self._offs = (0, off_ctx, off_tab, off_pairs)
-        self._slots_d = self._dev[0:8 * B].view(torch.int64)
-        self._ctx_d = self._dev[off_ctx:off_ctx + 4 * B].view(torch.int32)
-        self._tables_d = self._dev[off_tab:off_tab + 4 * B * max_blocks_per_seq].view(
-            torch.int32).view(B, max_blocks_per_seq)
-        self._pairs_d = self._dev[off_pairs:off_pairs + 8 * B].view(torch.int32).view(B, 2)
         self._last_buf = None
+        self._last_dev = 0
         self._dev_current = True
         self.out = torch.empty((B, num_heads, cache.head_dim), dtype=cache.dtype, device=dev)
         self.workspace = ops.alloc_workspace(B, num_heads, cache.head_dim,
@@ -159,31 +180,34 @@ class DecodeBatch:
         self.last_max_ctx = 0
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
 
-    def _staged_dev(self) -> None:
-        """With zero_copy, bring the last step's staged values to the device buffer."""
+    def _staged_dev(self) -> torch.Tensor:
+        """The device buffer holding the last step's staged values (copied there on
+        demand in "mapped" mode)."""
+        d = self._dev[self._last_dev]
         if not self._dev_current and self._last_buf is not None:
-            self._dev.copy_(self._pinned[self._last_buf], non_blocking=False)
+            d.copy_(self._pinned[self._last_buf], non_blocking=False)
             self._dev_current = True
+        return d
 
     @property
     def slots_d(self) -> torch.Tensor:
-        self._staged_dev()
-        return self._slots_d
+        return self._staged_dev()[0:8 * self.B].view(torch.int64)
 
     @property
     def ctx_d(self) -> torch.Tensor:
-        self._staged_dev()
-        return self._ctx_d
+        o = self._offs[1]
+        return self._staged_dev()[o:o + 4 * self.B].view(torch.int32)
 
     @property
     def tables_d(self) -> torch.Tensor:
-        self._staged_dev()
-        return self._tables_d
+        o = self._offs[2]
+        n = 4 * self.B * self.max_blocks
+        return self._staged_dev()[o:o + n].view(torch.int32).view(self.B, self.max_blocks)
 
     @property
     def pairs_d(self) -> torch.Tensor:
-        self._staged_dev()
-        return self._pairs_d
+        o = self._offs[3]
+        return self._staged_dev()[o:o + 8 * self.B].view(torch.int32).view(self.B, 2)
 
     @staticmethod
     def _aligned(t: torch.Tensor) -> torch.Tensor:
@@ -209,20 +233,28 @@ class DecodeBatch:
                     e.record(self.stream)        # creates the handle
         buf = self._i & 1
         self._i += 1
-        self._staged[buf].synchronize()          # the copy that last read this buffer is done
+        self._staged[buf].synchronize()          # the step that last used this buffer is done
         pin = self._pinned[buf]
         ev = (None, None) if attn_events is None else (attn_events[0].cuda_event,
                                                        attn_events[1].cuda_event)
         ws = self.workspace
+        side = self._copy_stream is not None
+        di = buf if side else 0
+        if side:
+            # the device buffer's last reader (two steps back) has finished
+            self._copy_stream.wait_event(self._staged[buf])
         N.check(self._lib.pa_decode_step(
             self.cache.bm._h, C.byref(self._desc), self.B, self._sids_ptr, k_new.data_ptr(),
             v_new.data_ptr(), q.data_ptr(), self.H, self.scale, self.out.data_ptr(),
             ws.data_ptr(), ws.numel(), pin.data_ptr(),
-            None if self.zero_copy else self._dev.data_ptr(), self._bytes,
-            self.max_blocks, ev[0], ev[1], C.byref(self._info), self.stream.cuda_stream),
+            None if self.zero_copy else self._dev[di].data_ptr(), self._bytes,
+            self.max_blocks, ev[0], ev[1], C.byref(self._info),
+            self._copy_stream.cuda_stream if side else None,
+            self._copied[buf].cuda_event if side else None, self.stream.cuda_stream),
             "pa_decode_step")
         self._staged[buf].record(self.stream)
         self._last_buf = buf
+        self._last_dev = di
         self._dev_current = not self.zero_copy
         n_cow = self._info.num_cow
         if n_cow:

@@ -273,3 +273,36 @@ def test_shared_block_hint_gives_the_same_bits():
                workspace=ws, shared_blocks=False).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, out_step)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_staging_modes_give_the_same_bits(cfg):
+    """Tables read in place, uploaded on the step's stream, or uploaded on a side
+    stream: the same outputs, pools and staged tables over several steps (the
+    side mode alternates two device buffers)."""
+    from paged_kv_cache_385_amd import DecodeBatch
+    from workloads import new_token_kv
+    steps = 4
+    wl = make_workload(cfg, grow=steps)
+    sids = [op[1] for op in wl.step]
+    mb = -(-(int(wl.ctx_lens.max()) + steps) // 16)
+    got = {}
+    for mode in ("mapped", "upload", "side"):
+        say(f"workload {cfg}, staging {mode}, {steps} steps")
+        cache, _ = build_device(wl)
+        batch = DecodeBatch(cache, sids, wl.num_heads, wl.scale, mb, staging=mode)
+        q = wl.q().to(cache.device)
+        outs = []
+        for i in range(steps):
+            k, v = new_token_kv(wl.seed, i, wl.num_seqs, wl.num_kv_heads, wl.head_dim, wl.dtype)
+            outs.append(batch.step(k.to(cache.device), v.to(cache.device), q).clone())
+        torch.cuda.synchronize()
+        got[mode] = (torch.stack(outs), cache.k_cache.clone(), cache.v_cache.clone(),
+                     batch.tables_d.clone(), batch.ctx_d.clone())
+        del cache, batch
+    ref = got["mapped"]
+    assert not torch.isnan(ref[0]).any()
+    for mode in ("upload", "side"):
+        for a, b in zip(ref, got[mode]):
+            assert torch.equal(a.view(torch.int16) if a.is_floating_point() else a,
+                               b.view(torch.int16) if b.is_floating_point() else b), mode

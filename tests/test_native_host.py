@@ -317,7 +317,8 @@ def test_decode_step_rejects_before_the_block_manager_changes():
         a.update(kw)
         return lib.pa_decode_step(bm._h, C.byref(c), 1, ids.ctypes.data, a["k"], a["v"], a["q"],
                                   a["H"], 0.1, a["out"], a["ws"], a["wsb"], a["sh"], a["sd"],
-                                  a["sb"], a["mb"], None, None, C.byref(info), None)
+                                  a["sb"], a["mb"], None, None, C.byref(info), a.get("cs"),
+                                  a.get("ce"), None)
 
     assert call(sb=staging - 1) == N.PA_ERR_INVALID_ARG             # staging too small
     assert call(sh=FAKE + 16) == N.PA_ERR_INVALID_ARG                # staging misaligned
@@ -325,4 +326,6 @@ def test_decode_step_rejects_before_the_block_manager_changes():
     assert call(H=3) == N.PA_ERR_INVALID_ARG                         # heads not a multiple of Hkv
     assert call(mb=64) == N.PA_ERR_WORKSPACE                         # 1024 tokens need a workspace
     assert call(q=None) == N.PA_ERR_INVALID_ARG
+    assert call(cs=FAKE) == N.PA_ERR_INVALID_ARG                     # copy stream without event
+    assert call(cs=FAKE, ce=FAKE, sd=None) == N.PA_ERR_INVALID_ARG   # copy stream, no device staging
     assert bm.seq_len(0) == 3 and bm.block_table(0) == [0]

@@ -119,8 +119,8 @@ class Workload:
 
 
 def new_token_kv(seed: int, step: int, num_seqs: int, num_kv_heads: int, head_dim: int,
-                 dtype: torch.dtype) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """k, v [B, Hkv, D] and q-like noise for an extra decode step ``step`` (bench growth)."""
+                 dtype: torch.dtype) -> Tuple[torch.Tensor, torch.Tensor]:
+    """k, v [B, Hkv, D] of the new tokens of an extra decode step ``step`` (bench growth)."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, _KIND_STEP_TOKEN, step]))
     k = rng.standard_normal((num_seqs, num_kv_heads, head_dim), dtype=np.float32)
     v = rng.standard_normal((num_seqs, num_kv_heads, head_dim), dtype=np.float32)
