@@ -18,6 +18,8 @@ What is computed, and where the pages fix it:
 * Long contexts split into partitions whose partial softmax states are merged
   by log-sum-exp (the "sequence split" of the same section): ``partial_state``
   and ``lse_merge`` below state that merge in its textbook form.
+* Several new tokens per sequence (a prefill chunk, a speculative verify):
+  ``chunk_attention`` / ``chunk_batch``, the causal reading stated with them.
 
 Everything is upcast exactly to float64 before any arithmetic.
 """
@@ -103,3 +105,59 @@ def lse_merge(ms, ls, accs, base: float = np.e) -> np.ndarray:
     M = ms.max()
     w = np.power(base, ms - M)
     return (w @ accs) / (w @ ls)
+
+
+# ---- several new tokens per sequence: a prefill chunk, or a speculative verify ----------
+#
+# A long prompt is prefilled in chunks: each chunk's tokens get their keys and
+# values cached and attend to everything before them, so later chunks build on
+# the cache the earlier ones left ("vLLM 核心概念", section "Chunked Prefill";
+# "PagedAttention 实战", section "Chunked Prefill：长 prompt 不要一次吃完全部预算").
+# Verifying the draft tokens of speculative decoding runs the main model over
+# several new tokens at once ("vLLM 核心概念", section "推测解码（Speculative
+# Decoding）").  Both are the same computation: the last
+# n of a sequence's ctx cached tokens are queries, and query i (position
+# ctx - n + i) attends over positions 0 .. ctx - n + i -- the causal reading
+# that the prompt's tokens see only what precedes them (and themselves).
+# With n = 1 it is exactly ``decode_attention``.
+
+
+def chunk_attention(q, k, v, scale: float) -> np.ndarray:
+    """One sequence: q [n, H, D] (its last n tokens), k and v [ctx, Hkv, D], n <= ctx
+    ->  out [n, H, D] (float64); query i attends over k[: ctx - n + i + 1]."""
+    qd = _f64(q)
+    n, H, D = qd.shape
+    ctx, Hkv = k.shape[0], k.shape[1]
+    if n > ctx:
+        raise ValueError(f"{n} new tokens but only {ctx} cached")
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = H // Hkv
+    out = np.empty((n, H, D), dtype=np.float64)
+    for g in range(Hkv):
+        kg = _f64(k[:, g, :])
+        vg = _f64(v[:, g, :])
+        for i in range(n):
+            visible = ctx - n + i + 1
+            for h in range(g * G, (g + 1) * G):
+                out[i, h] = attention_weights(qd[i, h], kg[:visible], scale) @ vg[:visible]
+    return out
+
+
+def chunk_batch(q, q_starts, seq_kv, ctx_lens, scale: float, seqs=None) -> np.ndarray:
+    """Packed queries q [total, H, D]; sequence b owns rows q_starts[b] .. q_starts[b+1]
+    and ``seq_kv(b)`` -> (k, v) of its ctx_lens[b] cached tokens.  Returns out
+    [total, H, D] (NaN in the rows of sequences not in ``seqs``)."""
+    qd = _f64(q)
+    out = np.full(qd.shape, np.nan)
+    B = len(ctx_lens)
+    seqs = range(B) if seqs is None else seqs
+    for b in seqs:
+        lo, hi = int(q_starts[b]), int(q_starts[b + 1])
+        if hi == lo:
+            continue
+        k, v = seq_kv(b)
+        if k.shape[0] != int(ctx_lens[b]):
+            raise ValueError(f"sequence {b}: {k.shape[0]} cached tokens, context {ctx_lens[b]}")
+        out[lo:hi] = chunk_attention(qd[lo:hi], k, v, scale)
+    return out

@@ -207,3 +207,150 @@ def test_pins_catch_planted_mistakes(monkeypatch, name):
     elif name == "kv_swapped":
         monkeypatch.setattr(A, "decode_attention", _mutant_kv_swapped)
     assert not _pins_pass()
+
+
+# -- several new tokens per sequence (prefill chunk / speculative verify) --------------
+def brute_force_chunk(q, k, v, scale):
+    """Independent loops: the last n of ctx tokens query, token i sees positions <= ctx-n+i."""
+    n, H, D = len(q), len(q[0]), len(q[0][0])
+    ctx, Hkv = len(k), len(k[0])
+    per_kv = H // Hkv
+    out = []
+    for i in range(n):
+        pos = ctx - n + i
+        rows = []
+        for h in range(H):
+            g = h // per_kv
+            w = []
+            for t in range(pos + 1):
+                dot = 0.0
+                for d in range(D):
+                    dot += q[i][h][d] * k[t][g][d]
+                w.append(math.exp(scale * dot))
+            z = sum(w)
+            rows.append([sum(w[t] * v[t][g][d] for t in range(pos + 1)) / z for d in range(D)])
+        out.append(rows)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n,ctx,H,Hkv,D", [(1, 1, 2, 2, 4), (3, 3, 2, 1, 8), (4, 9, 4, 2, 8),
+                                           (6, 20, 8, 2, 4), (5, 17, 2, 2, 16)])
+def test_chunk_brute_force(n, ctx, H, Hkv, D):
+    rng = np.random.default_rng(4000 + 31 * n + ctx)
+    q = rng.standard_normal((n, H, D))
+    k = rng.standard_normal((ctx, Hkv, D))
+    v = rng.standard_normal((ctx, Hkv, D))
+    scale = 1.0 / math.sqrt(D)
+    ref = brute_force_chunk(q.tolist(), k.tolist(), v.tolist(), scale)
+    np.testing.assert_allclose(A.chunk_attention(q, k, v, scale), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_chunk_of_one_token_is_decode():
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 23, 8, 2, 16)
+    np.testing.assert_array_equal(A.chunk_attention(q[None], k, v, 0.2)[0],
+                                  A.decode_attention(q, k, v, 0.2))
+
+
+def test_whole_prompt_equals_torch_causal_attention():
+    """n = ctx: the chunk is the whole prompt, i.e. plain causal self-attention
+    (torch's scaled_dot_product_attention, float64, is_causal)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    ctx, H, Hkv, D = 37, 8, 2, 16
+    q = rng.standard_normal((ctx, H, D))
+    k = rng.standard_normal((ctx, Hkv, D))
+    v = rng.standard_normal((ctx, Hkv, D))
+    scale = 0.125
+    tq = torch.from_numpy(q).permute(1, 0, 2)                       # [H, ctx, D]
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(H // Hkv, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(H // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                           scale=scale)
+    np.testing.assert_allclose(A.chunk_attention(q, k, v, scale), ref.permute(1, 0, 2).numpy(),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_chunking_a_prompt_does_not_change_its_outputs():
+    rng = np.random.default_rng(13)
+    ctx, H, Hkv, D = 41, 4, 2, 8
+    q = rng.standard_normal((ctx, H, D))
+    k = rng.standard_normal((ctx, Hkv, D))
+    v = rng.standard_normal((ctx, Hkv, D))
+    whole = A.chunk_attention(q, k, v, 0.3)
+    parts, start = [], 0
+    for size in (16, 1, 9, 15):
+        end = start + size
+        parts.append(A.chunk_attention(q[start:end], k[:end], v[:end], 0.3))
+        start = end
+    np.testing.assert_allclose(np.concatenate(parts), whole, rtol=1e-13, atol=1e-14)
+
+
+def test_chunk_queries_see_nothing_after_their_position():
+    rng = np.random.default_rng(14)
+    n, ctx, H, Hkv, D = 5, 12, 4, 2, 8
+    q = rng.standard_normal((n, H, D))
+    k = rng.standard_normal((ctx, Hkv, D))
+    v = rng.standard_normal((ctx, Hkv, D))
+    base = A.chunk_attention(q, k, v, 0.4)
+    for i in range(n):
+        pos = ctx - n + i
+        k2, v2 = k.copy(), v.copy()
+        k2[pos + 1:] += 3.0
+        v2[pos + 1:] -= 5.0
+        assert np.array_equal(A.chunk_attention(q, k2, v2, 0.4)[i], base[i])
+        k3 = k.copy()
+        k3[pos] += 3.0
+        assert not np.allclose(A.chunk_attention(q, k3, v, 0.4)[i], base[i])
+
+
+def test_chunk_batch_rows_follow_q_starts():
+    rng = np.random.default_rng(15)
+    H, Hkv, D = 4, 2, 8
+    ctx = [9, 3, 20]
+    n = [2, 0, 5]
+    starts = np.concatenate([[0], np.cumsum(n)])
+    kv = [(rng.standard_normal((c, Hkv, D)), rng.standard_normal((c, Hkv, D))) for c in ctx]
+    q = rng.standard_normal((int(starts[-1]), H, D))
+    out = A.chunk_batch(q, starts, lambda b: kv[b], ctx, 0.3)
+    for b in range(3):
+        lo, hi = starts[b], starts[b + 1]
+        if hi > lo:
+            np.testing.assert_array_equal(out[lo:hi], A.chunk_attention(q[lo:hi], *kv[b], 0.3))
+
+
+def _chunk_pins_pass():
+    try:
+        test_chunk_brute_force(4, 9, 4, 2, 8)
+        test_chunk_brute_force(6, 20, 8, 2, 4)
+        test_chunk_queries_see_nothing_after_their_position()
+        return True
+    except AssertionError:
+        return False
+
+
+def _make_chunk_mutant(shift=0, causal=True):
+    def mutant(q, k, v, scale):
+        qd = A._f64(q)
+        n, H, D = qd.shape
+        ctx, Hkv = k.shape[0], k.shape[1]
+        G = H // Hkv
+        out = np.empty((n, H, D))
+        for i in range(n):
+            visible = min(ctx, max(1, ctx - n + i + 1 + shift)) if causal else ctx
+            for h in range(H):
+                g = h // G
+                kg, vg = A._f64(k[:visible, g, :]), A._f64(v[:visible, g, :])
+                out[i, h] = A.attention_weights(qd[i, h], kg, scale) @ vg
+        return out
+    return mutant
+
+
+@pytest.mark.parametrize("name", ["excludes_self", "sees_next", "not_causal"])
+def test_chunk_pins_catch_planted_mistakes(monkeypatch, name):
+    assert _chunk_pins_pass()
+    mutant = {"excludes_self": _make_chunk_mutant(shift=-1),
+              "sees_next": _make_chunk_mutant(shift=1),
+              "not_causal": _make_chunk_mutant(causal=False)}[name]
+    monkeypatch.setattr(A, "chunk_attention", mutant)
+    assert not _chunk_pins_pass()
