@@ -291,6 +291,43 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
                      int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow, int32_t* tables,
                      int32_t max_blocks, int32_t* ctx_lens, int32_t* max_ctx);
 
+/* ---------------------------------------------------------------------------
+ * pa_chunk_attention -- several new tokens per sequence: the last q_len_b of
+ * sequence b's context_lens[b] cached tokens are queries, and query i (position
+ * context_lens[b] - q_len_b + i) attends over cached positions 0 .. its own.
+ * That is a prefill chunk ("vLLM 核心概念", section "Chunked Prefill";
+ * "PagedAttention 实战", section "Chunked Prefill：长 prompt 不要一次吃完全部预算")
+ * or the tokens of a speculative verify ("vLLM 核心概念", section "推测解码
+ * （Speculative Decoding）"); with q_len 1 it is the decode of pa_decode.  The new
+ * tokens' K/V must be in the cache already (pa_cache_write).
+ *   q, out           device, [total_q][num_heads][head_dim], cache dtype, 16-byte
+ *                    aligned; sequence b owns rows q_starts[b] .. q_starts[b+1].
+ *   q_starts         device, int32[num_seqs + 1], non-decreasing, q_starts[0] >= 0,
+ *                    q_starts[num_seqs] <= total_q; every q_len at most max_q_len
+ *                    (rows past max_q_len of a longer one are not written).
+ *   block_tables, context_lens, max_context_len, max_blocks_per_seq: as pa_decode.
+ *   workspace        device, >= pa_chunk_workspace_size(...) bytes, 16-byte aligned
+ *                    (NULL when that size is 0).
+ * One workgroup per (sequence, KV head, 16 (token, head) columns, key partition);
+ * when the column tiles alone do not fill the device, keys are split into
+ * partitions of 1024 tokens whose states are merged by log-sum-exp in a second
+ * launch ("PagedAttention 实战", section "2026 年的新变化").  A sequence whose rows
+ * fall outside [0, total_q] is skipped (nothing written); one with a context
+ * length outside [1, max_context_len] or more new tokens than cached ones gets
+ * NaN rows; a block id outside [0, num_blocks) poisons (NaN) the rows of every
+ * 16-column tile that reads it.
+ * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t total_q, int32_t max_q_len,
+                               int32_t max_context_len);
+pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t* q_starts,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ===========================================================================
  * pa_decode_step -- one whole decode step of a batch, in one call.
  * The order a decode step needs: the new token's K/V is stored before attention

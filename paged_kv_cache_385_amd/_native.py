@@ -87,6 +87,9 @@ SIGNATURES = {
     "pa_bm_free_list": (C.c_int, [_P, _P, _I32, _PI32]),
     "pa_bm_stats_get": (C.c_int, [_P, C.POINTER(PaBmStats)]),
     "pa_bm_step": (C.c_int, [_P, _I32, _P, _P, _P, _I32, _PI32, _P, _I32, _P, _PI32]),
+    "pa_chunk_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_chunk_attention": (C.c_int, [C.POINTER(PaCache), _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
+                                     _P, _I32, C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_decode_step_staging_bytes": (C.c_size_t, [_I32, _I32]),
     "pa_decode_step": (C.c_int, [_P, C.POINTER(PaCache), _I32, _P, _P, _P, _P, _I32, C.c_float, _P,
                                  _P, C.c_size_t, _P, _P, C.c_size_t, _I32, _P, _P,

@@ -60,8 +60,12 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     extra = ["-save-temps=obj"] if save_temps else []
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "pa_kernels.hip"), "-o", k_o],
          verbose)
+    c_o = os.path.join(BUILD, "chunk_attention.o")
+    _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "chunk_attention.hip"), "-o",
+          c_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, "-o", tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

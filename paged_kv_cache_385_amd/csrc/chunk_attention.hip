@@ -1,0 +1,489 @@
+// Paged attention for several new tokens per sequence, for gfx950 (CDNA4).
+//
+// The last n_b tokens of sequence b -- a prefill chunk ("vLLM 核心概念", section
+// "Chunked Prefill"; "PagedAttention 实战", section "Chunked Prefill：长 prompt 不要一次吃
+// 完全部预算") or the draft tokens of a speculative verify ("vLLM 核心概念", section
+// "推测解码（Speculative Decoding）") -- have their K/V in the cache already and are
+// the queries; query i, at position ctx_b - n_b + i, attends over cached positions
+// 0 .. ctx_b - n_b + i.
+//
+//   chunk_attn_kernel   one workgroup per (sequence, KV head, tile of 16 query
+//                       columns, key partition); a column is one (new token, query
+//                       head of the KV head's group) pair, so a tile holds 16 / G
+//                       tokens of G heads
+//   chunk_merge_kernel  log-sum-exp merge of the key partitions ("PagedAttention
+//                       实战", section "2026 年的新变化": sequence split)
+//
+// The matrix-core mapping is the decode kernel's with the 16 query heads of a KV
+// head replaced by 16 columns: S^T = K.Q^T (16 tokens x 16 columns) with
+// v_mfma_f32_16x16x32, then out^T += V^T.P^T with v_mfma_f32_16x16x16, whose B
+// operand is the S^T register layout.  Lane l owns column l % 16, so the causal
+// mask, the online softmax and the rescale are lane-local.  The 4 waves split a
+// partition's blocks (every 4th) and combine in LDS.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace {
+
+using namespace pa_dev;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kCols = 16;                       // query columns per workgroup
+constexpr int kPartBlocks = 64;                 // blocks per key partition (1024 tokens)
+constexpr int kPartTokens = kPartBlocks * kBlock;
+
+struct ChunkArgs {
+  const uint16_t* q;            // [total][H][D]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* q_starts;      // [B + 1]
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* ctx_lens;      // [B]
+  uint16_t* out;                // [total][H][D]
+  float2* ws_ml;                // [total][H][P] (max in log2 units, sum), when P > 1
+  float* ws_acc;                // [total][H][P][D] unnormalised output
+  int32_t num_seqs, total, num_heads, num_kv_heads, group;
+  int32_t max_blocks, max_ctx, num_blocks;
+  int32_t col_tiles;            // column tiles per (sequence, KV head) in the grid
+  int32_t parts;                // key partitions per column tile in the grid (P)
+  float scale_log2;             // scale * log2(e)
+};
+
+// Position of the work: every (sequence, KV head) group goes to XCD group % 8 (the
+// XCDs take workgroup ids round-robin) and its items -- partition-major, then
+// column tile -- run back to back there, so the tiles reading one partition's
+// blocks share that XCD's L2.
+struct ChunkItem {
+  int32_t b, kvh, tile, part;
+};
+__device__ __forceinline__ bool chunk_item(const ChunkArgs& a, int32_t parts, ChunkItem* it) {
+  const int32_t per_group = a.col_tiles * parts;
+  const int32_t x = blockIdx.x & 7;
+  const int32_t k = blockIdx.x >> 3;
+  const int32_t gi = x + 8 * (k / per_group);
+  if (gi >= a.num_seqs * a.num_kv_heads) return false;
+  const int32_t r = k - (k / per_group) * per_group;
+  it->part = r / a.col_tiles;
+  it->tile = r - it->part * a.col_tiles;
+  it->b = gi / a.num_kv_heads;
+  it->kvh = gi - it->b * a.num_kv_heads;
+  return true;
+}
+
+// The sequence's rows and the tile's columns.  Returns false when nothing may be
+// written (rows outside [0, total]) or the tile holds no column.
+struct ChunkSeq {
+  int32_t qs, n, ctx, cols, pmax;
+  bool bad;   // context length outside [1, max_ctx], or more new tokens than cached ones
+};
+__device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& it, ChunkSeq* s) {
+  const int32_t qs = a.q_starts[it.b], qe = a.q_starts[it.b + 1];
+  if (qs < 0 || qe < qs || qe > a.total) return false;
+  s->qs = qs;
+  s->n = qe - qs;
+  s->ctx = a.ctx_lens[it.b];
+  s->cols = s->n * a.group;
+  if (it.tile * kCols >= s->cols) return false;
+  s->bad = s->ctx < 1 || s->ctx > a.max_ctx || s->n > s->ctx;
+  const int32_t last_col = min(it.tile * kCols + kCols - 1, s->cols - 1);
+  s->pmax = s->ctx - s->n + last_col / a.group;   // furthest position a tile column sees
+  return true;
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void chunk_attn_kernel(ChunkArgs a) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int kLdsStride = D + 4;
+  __shared__ float s_m[kWaves][kCols];
+  __shared__ float s_l[kWaves][kCols];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kCols * kLdsStride];
+  __shared__ int s_bad;
+
+  ChunkItem it;
+  if (!chunk_item(a, a.parts, &it)) return;
+  ChunkSeq sq;
+  if (!chunk_seq(a, it, &sq)) return;
+  const int32_t b = __builtin_amdgcn_readfirstlane(it.b);
+  const int32_t kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  const int32_t part = __builtin_amdgcn_readfirstlane(it.part);
+  const int32_t tile = __builtin_amdgcn_readfirstlane(it.tile);
+  const int32_t ctx = __builtin_amdgcn_readfirstlane(sq.ctx);
+  const int32_t pmax = __builtin_amdgcn_readfirstlane(sq.pmax);
+  const int32_t G = a.group;
+  const int32_t H = a.num_heads;
+
+  const int32_t tid = threadIdx.x;
+  const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t lane = tid & 63;
+  const int32_t n = lane & 15;       // column of this lane
+  const int32_t g4 = lane >> 4;      // token quad within a block
+
+  // Blocks the tile reads: 0 .. pmax / 16, in partitions of kPartBlocks -- or all
+  // in one when the launch has a single partition (outputs written directly).
+  const bool direct = a.parts == 1;
+  const int32_t nblk_t = sq.bad ? 1 : pmax / kBlock + 1;
+  const int32_t pblocks = direct ? nblk_t : kPartBlocks;
+  if (part * pblocks >= nblk_t) return;
+
+  if (sq.bad) {
+    // NaN in every row of the tile (once: partition 0 writes it, the merge keeps it)
+    for (int32_t i = tid; i < kCols * D; i += kThreads) {
+      const int32_t c = tile * kCols + i / D;
+      if (c < sq.cols) {
+        const int64_t row = static_cast<int64_t>(sq.qs + c / G) * H + kvh * G + c % G;
+        a.out[row * D + i % D] = E::kNaN;
+      }
+    }
+    return;
+  }
+
+  // This lane's column: token ti of the chunk, head gh of the group, position pos.
+  const int32_t col = tile * kCols + n;
+  const bool col_ok = col < sq.cols;
+  const int32_t ti = col_ok ? col / G : 0;
+  const int32_t gh = col_ok ? col - ti * G : 0;
+  const int32_t pos = col_ok ? ctx - sq.n + ti : pmax;   // padding columns: zero q, no mask
+  const int64_t q_row = (static_cast<int64_t>(sq.qs + ti) * H + kvh * G + gh) * D;
+  u32x4 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t jbeg = part * pblocks;
+  const int32_t jend = min(nblk_t, jbeg + pblocks);
+  const int32_t first = jbeg + w;
+  const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+
+  bool bad_blk = false;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 kb[2][KK], vb[2][KK];
+  // The wave's blocks go in runs of up to 64: lane i holds the id of the run's i-th.
+  int32_t ids = 0, i0 = 0, cnt = 0;
+
+  // Bounded buffer loads as in the decode pass; a step past the run's last block
+  // has an empty range and reads nothing.  The tiles of one partition are read by
+  // every column tile of the group, so they go through the caches.
+  auto load_block = [&](int buf, int32_t i) {
+    const int32_t phys = __builtin_amdgcn_readlane(ids, min(i, cnt - 1));
+    const int32_t bytes = i < cnt ? static_cast<int32_t>(tile_elems * sizeof(uint16_t)) : 0;
+    const auto kr = tile_rsrc(a.k_cache + phys * blk_stride + head_off, bytes);
+    const auto vr = tile_rsrc(a.v_cache + phys * blk_stride + head_off, bytes);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<false>(kr, (kk * 64 + lane) * 16);
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2)
+      vb[buf][j2] = load_tile<false>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+  };
+
+  auto compute_block = [&](int buf, int32_t i) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
+    const int32_t t0 = (first + kWaves * (i0 + i)) * kBlock; // position of the block's token 0
+    const int32_t seen = i < cnt ? pos - t0 : -1;           // this column sees tokens 0 .. seen
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = s[r] * a.scale_log2;
+      if (4 * g4 + r > seen) sv[r] = -INFINITY;
+    }
+    float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(m_run, bmax);
+    // a column may have seen nothing yet: exponentiate against a finite stand-in
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    u16x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = E::from_float(fast_exp2(sv[r] - m_use));
+      psum += E::to_float(pb[r]);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] *= alpha;
+    const int32_t valid = i < cnt ? ctx - t0 : 0;            // tokens of the block in context
+    if (valid < kBlock) {
+      // positions past the context may hold anything (NaN included): zero their V
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2) {
+        u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (4 * g4 + (e & 3) >= valid) vv[e] = 0;
+        vb[buf][j2] = __builtin_bit_cast(u32x4, vv);
+      }
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2) {
+      const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+      const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
+      const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
+      acc[2 * j2] = E::mfma_pv(lo, pb, acc[2 * j2]);
+      acc[2 * j2 + 1] = E::mfma_pv(hi, pb, acc[2 * j2 + 1]);
+    }
+  };
+
+  for (i0 = 0; i0 < nw; i0 += 64) {
+    cnt = min(64, nw - i0);
+    ids = 0;
+    if (lane < cnt) ids = bt[first + kWaves * (i0 + lane)];
+    const bool id_bad = lane < cnt && (ids < 0 || ids >= a.num_blocks);
+    if (id_bad) ids = 0;
+    bad_blk = bad_blk || __ballot(id_bad) != 0;
+    load_block(0, 0);
+    for (int32_t i = 0; i < cnt; i += 2) {
+      load_block(1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_block(0, i);
+      load_block(0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_block(1, i + 1);
+    }
+  }
+
+  // ---- combine the four waves in LDS ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (g4 == 0) {
+    s_m[w][n] = m_run;
+    s_l[w][n] = l_run;
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (bad_blk) s_bad = 1;
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][n]);
+  const float wscale = fast_exp2(m_run - (M == -INFINITY ? 0.f : M));
+  {
+    float* row = &s_acc[w][n * kLdsStride];
+#pragma unroll
+    for (int j2 = 0; j2 < KK; ++j2) {
+      const f32x4 e = acc[2 * j2] * wscale;
+      const f32x4 o = acc[2 * j2 + 1] * wscale;
+      float* dst = row + 32 * j2 + 8 * g4;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], o[0], e[1], o[1]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[2], o[2], e[3], o[3]};
+    }
+  }
+  __syncthreads();
+  const bool poisoned = s_bad != 0;
+
+  // each thread finishes 4 consecutive dims of one column
+  for (int32_t i4 = tid; i4 < kCols * (D / 4); i4 += kThreads) {
+    const int32_t c = i4 / (D / 4);
+    const int32_t d = (i4 - c * (D / 4)) * 4;
+    const int32_t gc = tile * kCols + c;
+    if (gc >= sq.cols) continue;
+    float Mc = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) Mc = fmaxf(Mc, s_m[v][c]);
+    const float Mu = Mc == -INFINITY ? 0.f : Mc;
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      L += s_l[v][c] * fast_exp2(s_m[v][c] - Mu);
+      o += *reinterpret_cast<const f32x4*>(&s_acc[v][c * kLdsStride + d]);
+    }
+    const int64_t hrow = static_cast<int64_t>(sq.qs + gc / G) * H + kvh * G + gc % G;
+    if (direct) {
+      u16x4 ov;
+      if (poisoned) {
+        ov = u16x4{E::kNaN, E::kNaN, E::kNaN, E::kNaN};
+      } else {
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+      }
+      *reinterpret_cast<u16x4*>(a.out + hrow * D + d) = ov;
+    } else {
+      const int64_t st = hrow * a.parts + part;
+      if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
+      *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
+      if (d == 0) a.ws_ml[st] = poisoned ? float2{0.f, NAN} : float2{Mc, L};
+    }
+  }
+}
+
+// One workgroup per (sequence, KV head, column tile), 4 dims of one column per
+// thread: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
+// the partitions a column's own position reaches (later ones hold nothing for it),
+// in partition order.
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) void chunk_merge_kernel(ChunkArgs a) {
+  ChunkItem it;
+  if (!chunk_item(a, 1, &it)) return;
+  ChunkSeq sq;
+  if (!chunk_seq(a, it, &sq)) return;
+  if (sq.bad) return;                       // the attention pass wrote NaN
+  const int32_t G = a.group;
+  const int32_t H = a.num_heads;
+  for (int32_t i4 = threadIdx.x; i4 < kCols * (D / 4); i4 += kThreads) {
+    const int32_t c = i4 / (D / 4);
+    const int32_t d = (i4 - c * (D / 4)) * 4;
+    const int32_t gc = it.tile * kCols + c;
+    if (gc >= sq.cols) continue;
+    const int32_t pos = sq.ctx - sq.n + gc / G;
+    const int32_t np = pos / kPartTokens + 1;
+    const int64_t hrow = static_cast<int64_t>(sq.qs + gc / G) * H + it.kvh * G + gc % G;
+    const int64_t st0 = hrow * a.parts;
+    float M = -INFINITY;
+    for (int32_t p = 0; p < np; ++p) M = fmaxf(M, a.ws_ml[st0 + p].x);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t p = 0; p < np; ++p) {
+      const float2 ml = a.ws_ml[st0 + p];
+      const float wgt = fast_exp2(ml.x - M);
+      L += wgt * ml.y;
+      o += wgt * *reinterpret_cast<const f32x4*>(a.ws_acc + (st0 + p) * D + d);
+    }
+    const float inv = 1.f / L;
+    u16x4 ov;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+    *reinterpret_cast<u16x4*>(a.out + hrow * D + d) = ov;
+  }
+}
+
+// Key partitions of a launch: one when the column tiles alone give every
+// workgroup slot (three per compute unit) eight items, else partitions of 1024
+// tokens, so long contexts with few new tokens still spread over the device and
+// no single workgroup walks a whole long context.
+int32_t chunk_parts(int32_t num_seqs, int32_t num_kv_heads, int32_t col_tiles, int32_t max_ctx) {
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * col_tiles;
+  if (items >= 8 * 3 * static_cast<int64_t>(pa::device_cus())) return 1;
+  return (max_ctx + kPartTokens - 1) / kPartTokens;
+}
+
+int32_t chunk_col_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len) {
+  const int64_t cols = static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads);
+  return static_cast<int32_t>((cols + kCols - 1) / kCols);
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <class E>
+void launch_chunk(const ChunkArgs& a, int64_t grid, int64_t merge_grid, int d, hipStream_t s) {
+  if (d == 64) {
+    chunk_attn_kernel<E, 64><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+    if (a.parts > 1) chunk_merge_kernel<E, 64><<<dim3(merge_grid), dim3(kThreads), 0, s>>>(a);
+  } else {
+    chunk_attn_kernel<E, 128><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+    if (a.parts > 1) chunk_merge_kernel<E, 128><<<dim3(merge_grid), dim3(kThreads), 0, s>>>(a);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t total_q, int32_t max_q_len,
+                               int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      head_dim <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len <= 0)
+    return 0;
+  const int32_t tiles = chunk_col_tiles(num_heads, num_kv_heads, max_q_len);
+  const int32_t P = chunk_parts(num_seqs, num_kv_heads, tiles, max_context_len);
+  if (P <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
+  return round256(static_cast<size_t>(rows) * sizeof(float2)) +
+         static_cast<size_t>(rows) * head_dim * sizeof(float);
+}
+
+pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t* q_starts,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "pa_chunk_attention";
+  pa::clear_error();
+  pa_status st = pa::check_cache(cache, fn);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || total_q < 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d, total_q %d", fn, num_seqs, total_q);
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (num_heads <= 0 || num_heads % cache->num_kv_heads)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: num_heads %d not a multiple of num_kv_heads %d", fn,
+                    num_heads, cache->num_kv_heads);
+  if (max_q_len < 1 || max_context_len < 1)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: max_q_len %d, max_context_len %d", fn, max_q_len,
+                    max_context_len);
+  if (max_blocks_per_seq < 1 || static_cast<int64_t>(max_blocks_per_seq) * kBlock < max_context_len)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq %d cannot hold %d tokens", fn,
+                    max_blocks_per_seq, max_context_len);
+  if (!q || !q_starts || !block_tables || !context_lens || !out || !pa::aligned16(q) ||
+      !pa::aligned16(out))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer or q / out not 16-byte aligned", fn);
+  if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  const int32_t G = num_heads / cache->num_kv_heads;
+  const int32_t tiles = chunk_col_tiles(num_heads, cache->num_kv_heads, max_q_len);
+  const int32_t P = chunk_parts(num_seqs, cache->num_kv_heads, tiles, max_context_len);
+  const int64_t groups = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
+  const int64_t per_xcd = (groups + 7) / 8;
+  const int64_t grid = 8 * per_xcd * tiles * P;
+  const int64_t merge_grid = 8 * per_xcd * tiles;
+  if (grid > INT32_MAX || static_cast<int64_t>(total_q) * num_heads * P > INT32_MAX)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: launch too large", fn);
+  const size_t need = pa_chunk_workspace_size(num_seqs, num_heads, cache->num_kv_heads,
+                                              cache->head_dim, total_q, max_q_len, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need || !pa::aligned16(workspace)))
+    return pa::fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes,
+                    need);
+  ChunkArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t*>(cache->v_cache);
+  a.q_starts = q_starts;
+  a.block_tables = block_tables;
+  a.ctx_lens = context_lens;
+  a.out = static_cast<uint16_t*>(out);
+  const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
+  a.ws_ml = P > 1 ? static_cast<float2*>(workspace) : nullptr;
+  a.ws_acc = P > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              round256(static_cast<size_t>(rows) * sizeof(float2)))
+                   : nullptr;
+  a.num_seqs = num_seqs;
+  a.total = total_q;
+  a.num_heads = num_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = G;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.num_blocks = cache->num_blocks;
+  a.col_tiles = tiles;
+  a.parts = P;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == PA_F16)
+    launch_chunk<F16>(a, grid, merge_grid, cache->head_dim, s);
+  else
+    launch_chunk<BF16>(a, grid, merge_grid, cache->head_dim, s);
+  return pa::launch_status(fn);
+}
+
+}  // extern "C"

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "../../include/pa.h"
@@ -11,6 +12,14 @@ namespace pa {
 // Records a formatted detail for pa_last_error() and returns `st`.
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
+
+// Checks of a cache descriptor shared by every entry point (fn names the caller).
+pa_status check_cache(const pa_cache* c, const char* fn);
+// PA_ERR_HIP with the runtime's message if the last launch failed.
+pa_status launch_status(const char* fn);
+bool aligned16(const void* p);
+// Compute units of the current device (queried once per device).
+int32_t device_cus();
 
 // Blocks of the manager whose reference count is above one (kept up to date).
 int64_t bm_shared_blocks(const pa_bm* bm);

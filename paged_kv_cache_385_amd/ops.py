@@ -174,3 +174,42 @@ def decode_merge(k_cache, v_cache, context_lens, max_context_len: int, out, work
                                     out.data_ptr(), ws, wsb, _stream_ptr(stream, out.device)),
             "pa_decode_merge")
     return out
+
+
+def chunk_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                         total_q: int, max_q_len: int, max_context_len: int) -> int:
+    return int(N.lib().pa_chunk_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, total_q,
+                                               max_q_len, max_context_len))
+
+
+def chunk_attention(k_cache, v_cache, q, q_starts, block_tables, context_lens, max_q_len: int,
+                    max_context_len: int, scale: float, out=None, workspace=None,
+                    stream=None) -> torch.Tensor:
+    """pa_chunk_attention: the last q_len_b tokens of each sequence (rows q_starts[b] ..
+    q_starts[b+1] of the packed q [total, H, D]) attend causally over its cache.
+    Returns out [total, H, D]; allocates the workspace when none is given."""
+    desc = cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q must be [total, H, {desc.head_dim}], got {tuple(q.shape)}")
+    T, H = int(q.shape[0]), int(q.shape[1])
+    B = int(q_starts.shape[0]) - 1
+    _need(q, k_cache.dtype, dev, "q")
+    _need(q_starts, torch.int32, dev, "q_starts", (B + 1,))
+    _need(block_tables, torch.int32, dev, "block_tables")
+    _need(context_lens, torch.int32, dev, "context_lens", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, k_cache.dtype, dev, "out", tuple(q.shape))
+    need = chunk_workspace_size(B, H, desc.num_kv_heads, desc.head_dim, T, max_q_len,
+                                max_context_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
+    N.check(N.lib().pa_chunk_attention(C.byref(desc), q.data_ptr(), q_starts.data_ptr(), B, T,
+                                       max_q_len, H, block_tables.data_ptr(), block_tables.shape[1],
+                                       context_lens.data_ptr(), max_context_len, scale,
+                                       out.data_ptr(), ws, wsb, _stream_ptr(stream, dev)),
+            "pa_chunk_attention")
+    return out

@@ -1,0 +1,162 @@
+"""GPU parity of pa_chunk_attention (several new tokens per sequence) against the oracle.
+
+The cache is built through the library (the workload's set-up trace plus its
+decode step, so every sequence holds ctx_b tokens); the last q_len_b tokens of
+each sequence are the queries.  Outputs within 2e-3 (float16 cache) / 1e-2
+(bfloat16 cache) of the float64 oracle, max absolute error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from tests.gpu_harness import build_device, check_close, run_step, say
+from workloads import custom_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import paged_kv_cache_385_amd._native as N
+    N.lib()
+
+
+def _cache_with_context(wl):
+    """Device cache holding every sequence's ctx_b tokens; tables and lengths on the device."""
+    cache, segs = build_device(wl)
+    _, batch = run_step(wl, cache, segs)
+    return cache, segs, batch.tables_d.clone(), batch.ctx_d.clone()
+
+
+def _starts(q_lens):
+    return np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))]).astype(np.int32)
+
+
+def _run(wl, cache, tables, ctx_d, q_lens, max_q_len=None, max_ctx=None):
+    from paged_kv_cache_385_amd import chunk_attention
+    q = wl.chunk_q(q_lens)
+    starts = _starts(q_lens)
+    dev = cache.device
+    mq = int(max(q_lens)) if max_q_len is None else max_q_len
+    mc = wl.max_context_len if max_ctx is None else max_ctx
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+    chunk_attention(cache.k_cache, cache.v_cache, q.to(dev), torch.from_numpy(starts).to(dev),
+                    tables, ctx_d, mq, mc, wl.scale, out=out)
+    torch.cuda.synchronize()
+    return q, starts, out
+
+
+def _oracle(wl, segs, q, starts, seqs):
+    return OA.chunk_batch(q, starts, lambda b: wl.seq_kv(b, segs), wl.ctx_lens, wl.scale, seqs)
+
+
+def _rows(starts, seqs):
+    return np.concatenate([np.arange(starts[b], starts[b + 1]) for b in seqs])
+
+
+def test_speculative_verify_shape():
+    """70B-shaped GQA-8 bf16 batch, 6 tokens per sequence (5 drafts + 1): key partitions
+    and the merge launch; every sequence's rows compared on a sample of sequences."""
+    wl = make_workload(3)
+    say("workload 3, 6 new tokens per sequence")
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q_lens = np.minimum(6, wl.ctx_lens)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    assert not torch.isnan(out).any()
+    longest = int(np.argmax(wl.ctx_lens))
+    seqs = sorted(set([0, 1, longest, int(np.argmin(wl.ctx_lens))] + list(range(5, 128, 17))))
+    ref = _oracle(wl, segs, q, starts, seqs)
+    check_close(out, ref, wl.dtype, rows=_rows(starts, seqs), label="verify, workload 3")
+
+
+@pytest.mark.parametrize("q_lens,ctx", [
+    ([300, 1024, 40, 1], [700, 1500, 40, 33]),     # chunks, a whole prompt, a decode
+    ([17, 5, 64], [17, 2100, 64]),                  # whole prompts, ragged chunk
+])
+def test_prefill_chunks(q_lens, ctx):
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=len(ctx))
+    say(f"chunks {q_lens} over contexts {ctx}, G=8, bf16")
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label="prefill chunks")
+
+
+@pytest.mark.parametrize("H,Hkv,D,dt", [(8, 8, 64, "f16"), (12, 4, 128, "f16"), (32, 2, 64, "bf16")])
+def test_head_layouts(H, Hkv, D, dt):
+    ctx = [1, 16, 17, 250, 600]
+    q_lens = [1, 16, 3, 130, 9]
+    wl = custom_workload(ctx, H, Hkv, D, dtype=dt, seed=H + D)
+    say(f"H={H} Hkv={Hkv} D={D} {dt}")
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label=f"H={H} Hkv={Hkv} D={D}")
+
+
+def test_partitioned_and_direct_paths_agree_with_the_oracle():
+    """A small max_q_len gives few column tiles, so keys are split and merged; a large
+    bound gives one partition and direct outputs.  Both match the oracle."""
+    ctx = [3000, 2047, 1025, 4000]
+    q_lens = [4, 1, 7, 2]
+    wl = custom_workload(ctx, 8, 1, 128, dtype="f16", seed=77)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), range(len(ctx)))
+    from paged_kv_cache_385_amd import chunk_workspace_size
+    for mq in (max(q_lens), 8192):
+        ws = chunk_workspace_size(len(ctx), 8, 1, 128, sum(q_lens), mq, wl.max_context_len)
+        say(f"max_q_len {mq}: workspace {ws} bytes")
+        _, _, out = _run(wl, cache, tables, ctx_d, q_lens, max_q_len=mq)
+        check_close(out, ref, wl.dtype, label=f"max_q_len {mq}")
+
+
+def test_bad_lengths_poison_only_their_rows_and_empty_chunks_write_nothing():
+    ctx = [40, 50, 60]
+    wl = custom_workload(ctx, 4, 2, 64, dtype="f16", seed=5)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    from paged_kv_cache_385_amd import chunk_attention
+    q_lens = [3, 0, 5]
+    q = wl.chunk_q(q_lens).cuda()
+    starts = torch.from_numpy(_starts(q_lens)).cuda()
+    bad_ctx = ctx_d.clone()
+    bad_ctx[2] = 61                       # beyond max_context_len 60
+    out = torch.zeros_like(q)
+    chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, bad_ctx, 5, 60, wl.scale,
+                    out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[3:]).all()
+    ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), [0])
+    check_close(out, ref, wl.dtype, rows=np.arange(0, 3), label="good sequence")
+
+
+def test_one_new_token_matches_decode():
+    from paged_kv_cache_385_amd import alloc_workspace, decode
+    wl = make_workload(2)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q_lens = np.ones(wl.num_seqs, dtype=np.int64)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ws = alloc_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, wl.max_context_len)
+    d = decode(cache.k_cache, cache.v_cache, q.cuda(), tables, ctx_d, wl.max_context_len,
+               wl.scale, workspace=ws)
+    torch.cuda.synchronize()
+    diff = float((out.float() - d.float()).abs().max())
+    say(f"chunk of one token vs decode: max|diff| = {diff:.3e}")
+    assert diff <= 2e-3
+
+
+def test_block_placement_does_not_change_the_bits():
+    ctx = [900, 130, 2500]
+    q_lens = [64, 7, 33]
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=9)
+    outs = []
+    for order_seed in (0, 1):
+        order = np.random.default_rng(order_seed).permutation(wl.num_blocks).astype(np.int32)
+        cache, segs = build_device(wl, free_order=order)
+        _, batch = run_step(wl, cache, segs)
+        _, _, out = _run(wl, cache, batch.tables_d, batch.ctx_d, q_lens)
+        outs.append(out.clone())
+        del cache, batch
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

@@ -110,6 +110,39 @@ def test_call_validation():
     assert lib.pa_decode_merge(C.byref(c), 2, 4, FAKE, 1000, FAKE, None, 0, None) == N.PA_ERR_WORKSPACE
 
 
+@no_device
+def test_chunk_call_validation():
+    lib = N.lib()
+    c = _cache()                                        # 2 KV heads, head_dim 128
+
+    def call(**k):
+        return lib.pa_chunk_attention(
+            C.byref(c), k.get("q", FAKE), k.get("qs", FAKE), k.get("B", 2), k.get("T", 12),
+            k.get("mq", 6), k.get("H", 4), FAKE, k.get("mb", 200), FAKE, k.get("mc", 3000),
+            k.get("scale", 0.1), k.get("out", FAKE), k.get("ws", None), k.get("wsb", 0), None)
+
+    need = lib.pa_chunk_workspace_size(2, 4, 2, 128, 12, 6, 3000)
+    assert need > 0                                     # few columns: key partitions, merged
+    assert lib.pa_chunk_workspace_size(2, 4, 2, 128, 12, 6, 1000) == 0   # one partition
+    assert call() == N.PA_ERR_WORKSPACE
+    assert call(ws=FAKE, wsb=need - 1) == N.PA_ERR_WORKSPACE
+    assert call(H=3) == N.PA_ERR_INVALID_ARG            # not a multiple of num_kv_heads
+    assert call(mb=8) == N.PA_ERR_INVALID_ARG           # 8 blocks cannot hold 3000 tokens
+    assert call(mq=0) == N.PA_ERR_INVALID_ARG
+    assert call(mc=0) == N.PA_ERR_INVALID_ARG
+    assert call(q=FAKE + 4) == N.PA_ERR_INVALID_ARG
+    assert call(qs=None) == N.PA_ERR_INVALID_ARG
+    assert call(out=None) == N.PA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == N.PA_ERR_INVALID_ARG
+    assert call(B=-1) == N.PA_ERR_INVALID_ARG
+    assert call(B=0) == N.PA_OK and call(T=0) == N.PA_OK     # nothing to do
+    assert lib.pa_chunk_attention(None, FAKE, FAKE, 2, 12, 6, 4, FAKE, 200, FAKE, 3000, 0.1, FAKE,
+                                  None, 0, None) == N.PA_ERR_INVALID_ARG
+    # enough column tiles to fill the device: no partitions, no workspace
+    assert lib.pa_chunk_workspace_size(64, 64, 8, 128, 64 * 1024, 1024, 4096) == 0
+    assert lib.pa_chunk_workspace_size(2, 3, 2, 128, 12, 6, 3000) == 0   # invalid heads
+
+
 def test_workspace_size():
     lib = N.lib()
     assert lib.pa_decode_workspace_size(8, 32, 128, 512) == 0          # one partition: no merge

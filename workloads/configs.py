@@ -41,6 +41,7 @@ _KIND_SEGMENT = 1
 _KIND_Q = 2
 _KIND_STEP_TOKEN = 3
 _KIND_STEP_Q = 4
+_KIND_CHUNK_Q = 5
 
 _DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -110,6 +111,14 @@ class Workload:
         """Query of the step, [B, H, D] in the workload dtype (CPU)."""
         rng = np.random.default_rng(np.random.SeedSequence([self.seed, _KIND_Q]))
         q = rng.standard_normal((self.num_seqs, self.num_heads, self.head_dim), dtype=np.float32)
+        return torch.from_numpy(q).to(self.dtype)
+
+    def chunk_q(self, q_lens: Sequence[int]) -> torch.Tensor:
+        """Queries of the last q_lens[b] tokens of every sequence, packed in sequence
+        order: [sum(q_lens), H, D] in the workload dtype (CPU)."""
+        lens = [int(n) for n in q_lens]
+        rng = np.random.default_rng(np.random.SeedSequence([self.seed, _KIND_CHUNK_Q, *lens]))
+        q = rng.standard_normal((sum(lens), self.num_heads, self.head_dim), dtype=np.float32)
         return torch.from_numpy(q).to(self.dtype)
 
     def kv_bytes(self) -> int:
