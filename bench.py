@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, AMD published (no sparsity)
 METRIC = "paged-attn decode KV GB/s read (% of HBM peak); sequence-steps/s"
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc", "pa_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_traffic.json")
@@ -57,6 +58,10 @@ def parse():
                          "host memory, copied on the step's stream, or copied on a side stream "
                          "(overlapping the previous step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--chunk", choices=("verify", "prefill"),
+                    help="measure pa_chunk_attention instead of the decode step: 'verify' = the "
+                         "70B-shaped batch with 6 new tokens per sequence (HBM-bound), 'prefill' = "
+                         "the last 1024-token chunk of four 4096-token prompts (matrix-core bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -150,8 +155,143 @@ def cpu_baseline(wl, budget_s: float):
                       f"{kv_bytes / 1e6:.1f} MB of K/V, float64 numpy, {t_total:.1f} s"}
 
 
+def chunk_workload(mode):
+    """Workload, new tokens per sequence and a name for a pa_chunk_attention measurement."""
+    from workloads import custom_workload, make_workload
+    if mode == "verify":
+        wl = make_workload(3)
+        return (wl, np.minimum(6, wl.ctx_lens), "70B-shaped GQA-8 speculative verify, 6 new tokens "
+                "per sequence, B=128, lognormal contexts")
+    wl = custom_workload([4096] * 4, 64, 8, 128, dtype="bf16", seed=385)
+    return (wl, np.full(4, 1024), "70B-shaped GQA-8 prefill, last 1024-token chunk of four "
+            "4096-token prompts")
+
+
+def chunk_flops(ctx, q_lens, num_heads, head_dim) -> int:
+    """Matrix flops of the causal chunk: 2 products x 2 flops per multiply-add per visible key."""
+    total = 0
+    for c, n in zip(ctx, q_lens):
+        visible = np.arange(int(c) - int(n), int(c)) + 1
+        total += int(visible.sum()) * 4 * num_heads * head_dim
+    return total
+
+
+def run_chunk(args):
+    import torch
+    from oracle import attention as OA
+    import paged_kv_cache_385_amd as pa
+    from paged_kv_cache_385_amd import _native
+    assert torch.cuda.is_available(), "no HIP device"
+    _native.lib()
+    dev = torch.device("cuda:0")
+    wl, q_lens, name = chunk_workload(args.chunk)
+    B, H, Hkv, D = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim
+    K, W = args.steps, args.warmup
+    log(f"chunk {args.chunk}: {name}; total new tokens {int(q_lens.sum())}")
+    t0 = time.perf_counter()
+    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order)
+    segs = {}
+
+    def tokens(seg, start, n):
+        if seg not in segs:
+            segs[seg] = wl.segment_kv(seg)
+        k, v = segs[seg]
+        return k[start:start + n].contiguous(), v[start:start + n].contiguous()
+
+    cache.apply_trace(wl.setup, tokens)
+    cache.apply_trace(wl.step, tokens)            # every sequence now holds ctx_b tokens
+    segs.clear()
+    sids = [op[1] for op in wl.step]
+    max_blocks = -(-int(wl.ctx_lens.max()) // 16)
+    tables, ctx_d, max_ctx = cache.tables(sids, max_blocks)
+    q = wl.chunk_q(q_lens).to(dev)
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    mq = int(q_lens.max())
+    need = pa.chunk_workspace_size(B, H, Hkv, D, int(q_lens.sum()), mq, max_ctx)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"set-up {time.perf_counter() - t0:.1f} s; workspace {need} bytes "
+        f"({'key partitions + merge launch' if need else 'one partition'})")
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        pa.chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, ctx_d, mq, max_ctx,
+                           wl.scale, out=out, workspace=ws if need else None)
+
+    for _ in range(W):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    per_tok = 2 * Hkv * D * 2
+    kv_bytes = int(wl.ctx_lens.sum()) * per_tok
+    io_bytes = 2 * int(q_lens.sum()) * H * D * 2 + int((-(-wl.ctx_lens // 16)).sum()) * 4 + 8 * B
+    flops = chunk_flops(wl.ctx_lens, q_lens, H, D)
+    log(f"{K} calls: wall {wall * 1e3:.2f} ms, events {us:.1f} us per call")
+    if args.chunk == "verify":
+        metric, unit = "paged-attn verify KV GB/s read (% of HBM peak)", "GB/s"
+        value = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4)}
+    else:
+        metric, unit = "paged-attn prefill-chunk TFLOP/s (% of bf16 matrix peak)", "TFLOP/s"
+        value = flops / (us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFS, 4)}
+    roof.update({"traffic": None, "kernel": f"chunk_attn_kernel<{wl.dtype_name.upper()},{D}>"
+                 + (" + chunk_merge_kernel" if need else ""),
+                 "avg_launch_us": round(us, 2), "bytes_per_launch": kv_bytes + io_bytes,
+                 "flops_per_launch": flops})
+    result = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
+              "warmup": W, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype_name, "data": "synthetic",
+              "config": {"workload": name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
+                         "head_dim": D, "block_size": 16, "kv_dtype": wl.dtype_name,
+                         "new_tokens": int(q_lens.sum()), "max_new_tokens": mq,
+                         "mean_context": round(float(wl.ctx_lens.mean()), 1)},
+              "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline ...")
+        qc = wl.chunk_q(q_lens)
+        st = np.concatenate([[0], np.cumsum(q_lens)])
+        t_total, done_b, done_f = 0.0, 0, 0
+        b = 0
+        while t_total < args.cpu_seconds and b < 4 * B:
+            bb = b % B
+            k, v = wl.seq_kv(bb)
+            n = int(q_lens[bb])
+            rows = slice(int(st[bb]), int(st[bb]) + n)
+            t1 = time.perf_counter()
+            OA.chunk_attention(qc[rows], k, v, wl.scale)
+            t_total += time.perf_counter() - t1
+            done_b += int(wl.ctx_lens[bb]) * per_tok
+            done_f += chunk_flops([wl.ctx_lens[bb]], [n], H, D)
+            b += 1
+        cpu = done_b / t_total / 1e9 if unit == "GB/s" else done_f / t_total / 1e12
+        result["cpu_baseline"] = {"value": cpu, "unit": unit, "cores": 1, "kind": "oracle",
+                                  "sample": f"{b} sequences' chunks, float64 numpy, {t_total:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.chunk:
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+            sys.exit(2)
+        run_chunk(args)
+        return
     if args.summarize_counters:
         summarize_counters(args)
         return
