@@ -97,11 +97,11 @@ def test_head_layouts(H, Hkv, D, dt):
     check_close(out, ref, wl.dtype, label=f"H={H} Hkv={Hkv} D={D}")
 
 
-def test_partitioned_and_direct_paths_agree_with_the_oracle():
+@pytest.mark.parametrize("q_lens", [[4, 1, 7, 2], [8, 3, 8, 6]])
+def test_partitioned_and_direct_paths_agree_with_the_oracle(q_lens):
     """A small max_q_len gives few column tiles, so keys are split and merged; a large
     bound gives one partition and direct outputs.  Both match the oracle."""
     ctx = [3000, 2047, 1025, 4000]
-    q_lens = [4, 1, 7, 2]
     wl = custom_workload(ctx, 8, 1, 128, dtype="f16", seed=77)
     cache, segs, tables, ctx_d = _cache_with_context(wl)
     ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), range(len(ctx)))
@@ -113,23 +113,23 @@ def test_partitioned_and_direct_paths_agree_with_the_oracle():
         check_close(out, ref, wl.dtype, label=f"max_q_len {mq}")
 
 
-def test_bad_lengths_poison_only_their_rows_and_empty_chunks_write_nothing():
+@pytest.mark.parametrize("q_lens", [[3, 0, 5], [40, 0, 50]])
+def test_bad_lengths_poison_only_their_rows_and_empty_chunks_write_nothing(q_lens):
     ctx = [40, 50, 60]
     wl = custom_workload(ctx, 4, 2, 64, dtype="f16", seed=5)
     cache, segs, tables, ctx_d = _cache_with_context(wl)
     from paged_kv_cache_385_amd import chunk_attention
-    q_lens = [3, 0, 5]
     q = wl.chunk_q(q_lens).cuda()
     starts = torch.from_numpy(_starts(q_lens)).cuda()
     bad_ctx = ctx_d.clone()
     bad_ctx[2] = 61                       # beyond max_context_len 60
     out = torch.zeros_like(q)
-    chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, bad_ctx, 5, 60, wl.scale,
-                    out=out)
+    chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, bad_ctx, max(q_lens), 60,
+                    wl.scale, out=out)
     torch.cuda.synchronize()
-    assert torch.isnan(out[3:]).all()
+    assert torch.isnan(out[q_lens[0]:]).all()
     ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), [0])
-    check_close(out, ref, wl.dtype, rows=np.arange(0, 3), label="good sequence")
+    check_close(out, ref, wl.dtype, rows=np.arange(0, q_lens[0]), label="good sequence")
 
 
 def test_one_new_token_matches_decode():
