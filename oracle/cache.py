@@ -92,3 +92,42 @@ def scatter_sequence(kpool: np.ndarray, vpool: np.ndarray, table, k, v
     ctx = k.shape[0]
     slots = [int(table[t // bs]) * bs + t % bs for t in range(ctx)]
     return cache_write(kpool, vpool, k, v, slots)
+
+
+# ---- FP8 pools: E4M3 codes, one float32 scale per KV head for K and one for V --------
+def empty_pool8(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 16,
+                fill: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    return (np.full(shape, fill, dtype=np.uint8), np.full(shape, fill, dtype=np.uint8))
+
+
+def cache_write8(kpool: np.ndarray, vpool: np.ndarray, k, v, slots, k_scales, v_scales,
+                 inplace: bool = False) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 pools with token t's K/V [Hkv, D] quantised (per KV head h: encode(fp32(x) /
+    fp32(scale_h))) at slot ``slots[t]``; copies unless ``inplace``."""
+    from oracle import fp8
+    if not inplace:
+        kpool = kpool.copy()
+        vpool = vpool.copy()
+    kf = k.detach().to("cpu").float().numpy() if hasattr(k, "detach") else np.asarray(k, np.float32)
+    vf = v.detach().to("cpu").float().numpy() if hasattr(v, "detach") else np.asarray(v, np.float32)
+    ks = np.asarray(k_scales, dtype=np.float32)[:, None]
+    vs = np.asarray(v_scales, dtype=np.float32)[:, None]
+    bs = kpool.shape[2]
+    for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), bs)
+        kpool[blk, :, off, :] = fp8.quantize(kf[t], ks)
+        vpool[blk, :, off, :] = fp8.quantize(vf[t], vs)
+    return kpool, vpool
+
+
+def dequant_sequence8(kpool: np.ndarray, vpool: np.ndarray, table, ctx: int, k_scales, v_scales
+                      ) -> tuple[np.ndarray, np.ndarray]:
+    """float64 [ctx, Hkv, D] K and V values of a sequence in FP8 pools (code * scale)."""
+    from oracle import fp8
+    kc, vc = gather_sequence(kpool, vpool, table, ctx)
+    ks = np.asarray(k_scales, dtype=np.float32)[None, :, None]
+    vs = np.asarray(v_scales, dtype=np.float32)[None, :, None]
+    return fp8.dequantize(kc, ks), fp8.dequantize(vc, vs)
