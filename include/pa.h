@@ -34,6 +34,12 @@
  *           token t, dim d of (block b, head h) at [b][h][t/4][d][t%4]
  *   One (block, head) tile of K or V is 16*head_dim contiguous elements; one
  *   physical block of a pool is num_kv_heads*16*head_dim contiguous elements.
+ * FP8 pools (PA_CACHE_FP8): one byte per element, laid out so that one 16-byte
+ * lane load holds the operands of two matrix-core steps:
+ *   K pool: [num_blocks][num_kv_heads][head_dim/64][16][4][2][8]
+ *           token t, dim d at [b][h][d/64][t][(d%32)/8][(d%64)/32][d%8]
+ *   V pool: [num_blocks][num_kv_heads][4][head_dim/64][16][2][2][4]
+ *           token t, dim d at [b][h][t/4][d/64][(d%32)/2][(d%64)/32][d%2][t%4]
  * Slot encoding: slot = physical_block * 16 + position_in_block.
  * Query-to-KV head map: query head h reads KV head h / (num_heads/num_kv_heads).
  */
@@ -71,10 +77,24 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
  * Results are the same bits either way. */
 #define PA_CACHE_SHARED_BLOCKS 1
 
+/* pa_cache.flags: the pools hold 8-bit floating-point codes (OCP E4M3: bias 7,
+ * subnormals, 448 largest, 0x7F NaN) in the FP8 layout above, one float32 scale
+ * per KV head for K (k_scales) and one for V (v_scales).  A stored element is
+ * E4M3(fp32(x) / fp32(scale)), rounded to nearest even, saturated at +-448, NaN
+ * stored as 0x7F; it stands for decode(code) * scale.  The pages only say that
+ * the KV cache can be kept quantised, FP8 among the formats ("理解 vLLM
+ * PagedAttention", version matrix, row "量化"); the format, the per-head scales
+ * and the rounding are this library's reading.  dtype stays the dtype of q,
+ * out and of the k / v given to pa_cache_write.  pa_chunk_attention does not
+ * take FP8 pools (PA_ERR_UNSUPPORTED). */
+#define PA_CACHE_FP8 2
+
 /* A KV pool pair.  k_cache and v_cache are device pointers in the layout above,
- * 16-byte aligned, each num_blocks*num_kv_heads*16*head_dim elements of dtype.
- * block_size must be 16; head_dim must be 64 or 128; flags is 0 or
- * PA_CACHE_SHARED_BLOCKS. */
+ * 16-byte aligned, each num_blocks*num_kv_heads*16*head_dim elements of dtype
+ * (of one byte with PA_CACHE_FP8).  block_size must be 16; head_dim must be 64
+ * or 128; flags is a combination of PA_CACHE_SHARED_BLOCKS and PA_CACHE_FP8.
+ * k_scales / v_scales: device float32[num_kv_heads], 4-byte aligned, positive
+ * finite (caller's contract), required with PA_CACHE_FP8 and ignored without. */
 typedef struct pa_cache {
   void* k_cache;
   void* v_cache;
@@ -83,7 +103,9 @@ typedef struct pa_cache {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;            /* pa_dtype */
-  int32_t flags;            /* PA_CACHE_* hints */
+  int32_t flags;            /* PA_CACHE_* */
+  const float* k_scales;    /* PA_CACHE_FP8: per-KV-head scales of K, else NULL */
+  const float* v_scales;    /* PA_CACHE_FP8: per-KV-head scales of V, else NULL */
 } pa_cache;
 
 /* ---------------------------------------------------------------------------
@@ -92,7 +114,8 @@ typedef struct pa_cache {
  * reuse them ("vLLM 核心概念", section "为什么需要 KV Cache？"), in the block the
  * table names for that position ("vLLM 核心概念", section "按需分配").
  *   k, v          device, [num_tokens][num_kv_heads][head_dim] packed (no padding
- *                 between tokens), cache dtype, 16-byte aligned.
+ *                 between tokens), cache dtype, 16-byte aligned.  FP8 pools store
+ *                 their quantised codes (see PA_CACHE_FP8).
  *   slot_mapping  device, int64[num_tokens]; token i is stored at slot
  *                 slot_mapping[i].  A negative slot skips the token; a slot at or
  *                 beyond num_blocks*16 is skipped too.

@@ -40,28 +40,20 @@ def decode(codes) -> np.ndarray:
 def encode(x) -> np.ndarray:
     """uint8 E4M3 codes of float values: round to nearest even, saturate at 448."""
     v = np.asarray(x, dtype=np.float64)
-    out = np.zeros(v.shape, dtype=np.uint8)
-    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
-    for i, xi in enumerate(flat_v):
-        if np.isnan(xi):
-            flat_o[i] = NAN_CODE
-            continue
-        s = 0x80 if np.signbit(xi) else 0
-        a = min(abs(float(xi)), MAX_FINITE)
-        frac, exp = np.frexp(a)            # a = frac * 2^exp, frac in [0.5, 1)
-        e = int(exp) - 1                   # a = (2 frac) * 2^e, 2 frac in [1, 2)
-        if a == 0.0:
-            flat_o[i] = s
-            continue
-        if e < 1 - BIAS:                   # below 2^-6: subnormal quantum 2^-9
-            m = int(np.rint(a / 2.0 ** (1 - BIAS - 3)))
-            flat_o[i] = s | m if m < 8 else s | (1 << 3)     # m = 8 is the first normal
-            continue
-        m = int(np.rint((a / 2.0 ** e - 1.0) * 8.0))
-        if m == 8:                          # mantissa carry into the exponent
-            e, m = e + 1, 0
-        flat_o[i] = s | ((e + BIAS) << 3) | m
-    return out
+    nan = np.isnan(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.minimum(np.abs(np.where(nan, 0.0, v)), MAX_FINITE)
+    _, exp = np.frexp(a)                       # a = f * 2^exp with f in [0.5, 1)
+    e = exp.astype(np.int64) - 1               # a = (2 f) * 2^e, 2 f in [1, 2)
+    # below 2^-6: subnormal, quantum 2^-9; m = 8 there is the first normal (code 0x08)
+    m_sub = np.rint(a / 2.0 ** (1 - BIAS - 3)).astype(np.int64)
+    # normal: 3-bit mantissa of a / 2^e, rounded half to even, with the carry into e
+    m = np.rint((np.ldexp(a, -e) - 1.0) * 8.0).astype(np.int64)
+    e = np.where(m == 8, e + 1, e)
+    m = np.where(m == 8, 0, m)
+    normal = ((e + BIAS) << 3) | m
+    code = np.where(a < 2.0 ** (1 - BIAS), m_sub, normal) | sign
+    return np.where(nan, NAN_CODE, code).astype(np.uint8)
 
 
 def quantize(x, scale) -> np.ndarray:

@@ -21,6 +21,7 @@ PA_ERR_NOT_FOUND = 6
 PA_F16 = 0
 PA_BF16 = 1
 PA_CACHE_SHARED_BLOCKS = 1
+PA_CACHE_FP8 = 2
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
 
@@ -28,7 +29,8 @@ PARTITION_TOKENS = 512
 class PaCache(C.Structure):
     _fields_ = [("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("num_blocks", C.c_int32),
                 ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("dtype", C.c_int32), ("flags", C.c_int32)]
+                ("dtype", C.c_int32), ("flags", C.c_int32), ("k_scales", C.c_void_p),
+                ("v_scales", C.c_void_p)]
 
 
 class PaBmStats(C.Structure):

@@ -424,6 +424,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   pa::clear_error();
   pa_status st = pa::check_cache(cache, fn);
   if (st != PA_OK) return st;
+  if (cache->flags & PA_CACHE_FP8)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: FP8 pools are not supported here", fn);
   if (num_seqs < 0 || total_q < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d, total_q %d", fn, num_seqs, total_q);
   if (num_seqs == 0 || total_q == 0) return PA_OK;

@@ -26,6 +26,14 @@ constexpr int kBlock = PA_BLOCK_SIZE;                       // tokens per block
 struct F16 {
   using T = _Float16;
   static constexpr uint16_t kNaN = 0x7E00;
+  // E4M3 codes in bytes 0, 1 (hi = false) or 2, 3 (hi = true) of w, as two float16
+  // (every E4M3 value is exact in float16)
+  __device__ static uint32_t from_fp8_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  }
+  __device__ static uint32_t from_fp8_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
   __device__ static f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -45,6 +53,13 @@ struct F16 {
 struct BF16 {
   using T = __bf16;
   static constexpr uint16_t kNaN = 0x7FC0;
+  // E4M3 codes in bytes 0, 1 / 2, 3 of w, as two bfloat16 (exact)
+  __device__ static uint32_t from_fp8_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
+  __device__ static uint32_t from_fp8_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  }
   __device__ static f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -61,13 +76,20 @@ struct BF16 {
   }
 };
 
+// Eight E4M3 codes (two words, in memory order) as eight 16-bit elements: one
+// matrix-core operand, in the element order the 16-bit pools use.
+template <class E>
+__device__ __forceinline__ u32x4 widen_fp8(uint32_t a, uint32_t b) {
+  return u32x4{E::from_fp8_lo(a), E::from_fp8_hi(a), E::from_fp8_lo(b), E::from_fp8_hi(b)};
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 // A buffer resource for `bytes` bytes at p (raw buffer, no swizzle; word 3 is
 // the gfx9 default format).  Loads past `bytes` return zeros without a memory access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 // 16 bytes of a K/V tile.  Tiles are read once per launch unless blocks are
 // shared: the streaming form sets the non-temporal bit, which keeps them from
@@ -80,5 +102,16 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- 8-bit floating point (OCP E4M3) cache codes -----------------------------------
+// Code of x / scale: the division in float32, round to nearest even, saturated at
+// +-448 (the hardware conversion turns larger magnitudes into NaN, so they are
+// clamped first), NaN as 0x7F.
+__device__ __forceinline__ uint32_t fp8_code(float x, float scale) {
+  const float y = x / scale;
+  if (y != y) return 0x7Fu;
+  const float c = fminf(fmaxf(y, -448.f), 448.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xFFu;
+}
 
 }  // namespace pa_dev

@@ -77,6 +77,50 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   for (int i = 0; i < 8; ++i) vdst[4 * i] = vv[i];
 }
 
+// FP8 pools: the same thread map; the 8 dims of a thread are 8 consecutive bytes
+// of the K tile (one 8-byte store) and 8 scattered bytes of the V tile.
+template <class E, int D>
+__global__ __launch_bounds__(256) void cache_write8_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int32_t num_tokens,
+    int32_t hkv, int64_t num_slots) {
+  constexpr int kChunks = D / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = static_cast<int64_t>(hkv) * kChunks;
+  if (idx >= static_cast<int64_t>(num_tokens) * per_token) return;
+  const int64_t t = idx / per_token;
+  const int32_t rem = static_cast<int32_t>(idx - t * per_token);
+  const int32_t h = rem / kChunks;
+  const int32_t c = rem - h * kChunks;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int32_t off = static_cast<int32_t>(slot & 15);
+  const int64_t src = (t * hkv + h) * D + 8 * c;
+  const int64_t tile = (blk * hkv + h) * (kBlock * D);
+  const float ks = k_scales[h], vs = v_scales[h];
+  const u16x8 kv = __builtin_bit_cast(u16x8, load16(k + src));
+  const u16x8 vv = __builtin_bit_cast(u16x8, load16(v + src));
+  // K: dims 8c .. 8c+7 = group c / 8 of 64, quad c % 4, half (c % 8) / 4
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo |= fp8_code(E::to_float(kv[e]), ks) << (8 * e);
+    hi |= fp8_code(E::to_float(kv[e + 4]), ks) << (8 * e);
+  }
+  const int64_t kb = (((static_cast<int64_t>(c / 8) * kBlock + off) * 4 + c % 4) * 2 + (c % 8) / 4) * 8;
+  *reinterpret_cast<uint2*>(k_cache + tile + kb) = uint2{lo, hi};
+  // V: dim d = 8c + e sits at [t/4][d/64][(d%32)/2][(d%64)/32][d%2][t%4]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int32_t d = 8 * c + e;
+    const int64_t vb = ((((static_cast<int64_t>(off >> 2) * (D / 64) + d / 64) * 16 + (d % 32) / 2) * 2 +
+                         (d % 64) / 32) * 2 + (d & 1)) * 4 + (off & 3);
+    v_cache[tile + vb] = static_cast<uint8_t>(fp8_code(E::to_float(vv[e]), vs));
+  }
+}
+
 // ---- block copy ------------------------------------------------------------------
 // grid.y = pair, grid.x strides over the 16-byte vectors of one block in both pools.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
@@ -111,6 +155,8 @@ struct DecodeArgs {
   const uint16_t* k_new;       // [B][Hkv][D] new tokens, or NULL: no fused store
   const uint16_t* v_new;
   const int64_t* new_slots;    // [B]
+  const float* k_scales;       // FP8 pools: [Hkv] scales of K and of V
+  const float* v_scales;
   int32_t* counters; // [B][Hkv] partitions finished, or NULL: the merge is a separate launch
   float2* ws_ml;     // [B][H][P] (max in log2 units, sum)
   float* ws_acc;     // [B][H][P][D] unnormalised output
@@ -304,10 +350,12 @@ __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_
 }
 
 // Three waves per SIMD: 136 registers, no spills, and 3 x 34 KB of LDS per CU.
-template <class E, int D, bool kStream>
+template <class E, int D, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_attn_kernel(DecodeArgs a) {
   constexpr int KK = D / 32;        // 16x16x32 steps for q.K^T; also 16-byte V loads per lane
+  constexpr int LW = kFp8 ? KK / 2 : KK;   // 16-byte loads per lane per tile (FP8: half)
+  constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * (kFp8 ? 1 : 2);
   constexpr int MT = D / 16;        // output tiles of 16 dims
   constexpr int kLdsStride = D + 4; // floats per head row in LDS (staggers banks)
   __shared__ float s_m[kWaves][16];
@@ -356,6 +404,10 @@ void decode_attn_kernel(DecodeArgs a) {
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const int64_t head_off_b = static_cast<int64_t>(kvh) * kTileBytes;
+  const int64_t blk_stride_b = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
+  // FP8 pools: the scales fold into the score (K) and the output (V)
+  const float score_scale = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
 
   // All of the wave's block ids in one load: lane i holds the id of its i-th block,
   // so no table read sits between two tile loads.
@@ -379,7 +431,7 @@ void decode_attn_kernel(DecodeArgs a) {
   uint32_t* st_v = reinterpret_cast<uint32_t*>(&s_acc[w][0]) + 64 * 4 * KK + lane * KK;
   u32x4 kpatch[KK];
   uint32_t vpatch[KK];
-  if (a.new_slots != nullptr && p == nparts - 1) {
+  if (!kFp8 && a.new_slots != nullptr && p == nparts - 1) {
     const int64_t slot = a.new_slots[b];
     const int32_t jl = nblk - 1 - p * PB;       // last block, within the partition
     if (slot >= 0 && (jl & (kWaves - 1)) == w) {
@@ -419,27 +471,37 @@ void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 kb[2][KK], vb[2][KK];
+  u32x4 kb[2][LW], vb[2][LW];     // 16-bit pools: the operands themselves; FP8: raw codes
 
   // Tiles are read with buffer loads whose resource covers exactly the tile; a
   // step past the wave's last block (i >= nw) gets an empty range, so its loads
   // return zeros without touching memory and the loop needs no branch.
   auto load_block = [&](int buf, int32_t i) {
     const int32_t phys = __builtin_amdgcn_readlane(ids, min(i, nw - 1));
-    const int32_t bytes = i < nw ? static_cast<int32_t>(tile_elems * sizeof(uint16_t)) : 0;
-    const auto kr = tile_rsrc(a.k_cache + phys * blk_stride + head_off, bytes);
-    const auto vr = tile_rsrc(a.v_cache + phys * blk_stride + head_off, bytes);
+    const int32_t bytes = i < nw ? static_cast<int32_t>(kTileBytes) : 0;
+    const auto kr = tile_rsrc(reinterpret_cast<const char*>(a.k_cache) + phys * blk_stride_b + head_off_b, bytes);
+    const auto vr = tile_rsrc(reinterpret_cast<const char*>(a.v_cache) + phys * blk_stride_b + head_off_b, bytes);
+    if constexpr (kFp8) {
+      // K: dims 64pp + 8g4 .. +7 and 64pp + 32 + 8g4 .. +7 of token n; V: dims
+      // (64qq + 2n, +1) and (64qq + 32 + 2n, +1) of tokens 4g4 .. +3
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
+      for (int pp = 0; pp < LW; ++pp) kb[buf][pp] = load_tile<kStream>(kr, ((pp * 16 + n) * 4 + g4) * 16);
 #pragma unroll
-    for (int j2 = 0; j2 < KK; ++j2)
-      vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+      for (int qq = 0; qq < LW; ++qq)
+        vb[buf][qq] = load_tile<kStream>(vr, ((g4 * (D / 64) + qq) * 16 + n) * 16);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2)
+        vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+    }
   };
 
   // Block i of the wave; i >= nw is a padding step whose positions are all masked,
   // which leaves m_run, l_run and acc unchanged (m_run is finite by then).
   auto compute_block = [&](int buf, int32_t i) {
-    if (st_on && i == st_i) {
+    if (!kFp8 && st_on && i == st_i) {
       const int32_t phys = __builtin_amdgcn_readlane(ids, i);
       uint16_t* kt = a.k_dst + phys * blk_stride + head_off;
       uint16_t* vt = a.v_dst + phys * blk_stride + head_off;
@@ -465,14 +527,28 @@ void decode_attn_kernel(DecodeArgs a) {
         }
       }
     }
+    // the block's operands: the loaded registers, or the FP8 codes widened exactly
+    u32x4 K[KK], V[KK];
+#pragma unroll
+    for (int t = 0; t < LW; ++t) {
+      if constexpr (kFp8) {
+        K[2 * t] = widen_fp8<E>(kb[buf][t][0], kb[buf][t][1]);
+        K[2 * t + 1] = widen_fp8<E>(kb[buf][t][2], kb[buf][t][3]);
+        V[2 * t] = widen_fp8<E>(vb[buf][t][0], vb[buf][t][1]);
+        V[2 * t + 1] = widen_fp8<E>(vb[buf][t][2], vb[buf][t][3]);
+      } else {
+        K[t] = kb[buf][t];
+        V[t] = vb[buf][t];
+      }
+    }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
+    for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(K[kk], qf[kk], s);
     const int32_t valid = i < nw ? ctx - (first + kWaves * i) * kBlock : 0;   // tokens in context
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = s[r] * a.scale_log2;
+      sv[r] = s[r] * score_scale;
       if (valid < kBlock && 4 * g4 + r >= valid) sv[r] = -INFINITY;
     }
     float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -495,16 +571,16 @@ void decode_attn_kernel(DecodeArgs a) {
       // positions past the context may hold anything (NaN included): zero their V
 #pragma unroll
       for (int j2 = 0; j2 < KK; ++j2) {
-        u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+        u16x8 vv = __builtin_bit_cast(u16x8, V[j2]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (4 * g4 + (e & 3) >= valid) vv[e] = 0;
-        vb[buf][j2] = __builtin_bit_cast(u32x4, vv);
+        V[j2] = __builtin_bit_cast(u32x4, vv);
       }
     }
 #pragma unroll
     for (int j2 = 0; j2 < KK; ++j2) {
-      const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+      const u16x8 vv = __builtin_bit_cast(u16x8, V[j2]);
       const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
       const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
       acc[2 * j2] = E::mfma_pv(lo, pb, acc[2 * j2]);
@@ -579,6 +655,7 @@ void decode_attn_kernel(DecodeArgs a) {
       L += s_l[u][hh] * fast_exp2(s_m[u][hh] - Mh);
       o += *reinterpret_cast<const f32x4*>(&s_acc[u][hh * kLdsStride + d]);
     }
+    if (kFp8) o *= a.v_scales[kvh];        // V codes stand for code * v_scale
     const int64_t row = q_row0 + static_cast<int64_t>(hh) * D;
     if (nparts == 1) {
       u16x4 ov;
@@ -753,8 +830,12 @@ pa_status check_cache(const pa_cache* c, const char* fn) {
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, c->head_dim);
   if (c->dtype != PA_F16 && c->dtype != PA_BF16)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, c->dtype);
-  if (c->flags & ~PA_CACHE_SHARED_BLOCKS)
+  if (c->flags & ~(PA_CACHE_SHARED_BLOCKS | PA_CACHE_FP8))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: unknown cache flags 0x%x", fn, c->flags);
+  if ((c->flags & PA_CACHE_FP8) &&
+      (!c->k_scales || !c->v_scales || (reinterpret_cast<uintptr_t>(c->k_scales) & 3u) ||
+       (reinterpret_cast<uintptr_t>(c->v_scales) & 3u)))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: FP8 pools need aligned k_scales and v_scales", fn);
   return PA_OK;
 }
 
@@ -815,6 +896,7 @@ struct DecodeSetup {
   DecodeArgs args;
   int64_t grid;
   bool shared_blocks;   // read K/V through the caches
+  bool fp8;             // the pools hold E4M3 codes
 };
 
 pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
@@ -878,25 +960,35 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.part_blocks = PT / kBlock;
   a.part_shift = __builtin_ctz(static_cast<unsigned>(PT / kBlock));
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
   su->grid = grid;
   su->shared_blocks = (cache->flags & PA_CACHE_SHARED_BLOCKS) != 0;
+  su->fp8 = (cache->flags & PA_CACHE_FP8) != 0;
   return PA_OK;
 }
 
-template <class E, bool kStream>
+template <class E, bool kStream, bool kFp8>
 void launch_attn_t(const DecodeSetup& su, int d, hipStream_t s) {
   if (d == 64)
-    decode_attn_kernel<E, 64, kStream><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+    decode_attn_kernel<E, 64, kStream, kFp8><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
   else
-    decode_attn_kernel<E, 128, kStream><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+    decode_attn_kernel<E, 128, kStream, kFp8><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
 }
 
 template <class E>
 void launch_attn(const DecodeSetup& su, int d, hipStream_t s) {
-  if (su.shared_blocks)
-    launch_attn_t<E, false>(su, d, s);
-  else
-    launch_attn_t<E, true>(su, d, s);
+  if (su.fp8) {
+    if (su.shared_blocks)
+      launch_attn_t<E, false, true>(su, d, s);
+    else
+      launch_attn_t<E, true, true>(su, d, s);
+  } else {
+    if (su.shared_blocks)
+      launch_attn_t<E, false, false>(su, d, s);
+    else
+      launch_attn_t<E, true, false>(su, d, s);
+  }
 }
 
 template <class E>
@@ -905,6 +997,28 @@ void launch_merge(const MergeArgs& m, int64_t grid, int d, hipStream_t s) {
     decode_merge_kernel<E, 64><<<dim3(grid), dim3(256), 0, s>>>(m);
   else
     decode_merge_kernel<E, 128><<<dim3(grid), dim3(256), 0, s>>>(m);
+}
+
+template <class E>
+void launch_write8_t(const pa_cache* c, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                     int32_t n, int64_t num_slots, int64_t grid, hipStream_t s) {
+  auto kc = static_cast<uint8_t*>(c->k_cache);
+  auto vc = static_cast<uint8_t*>(c->v_cache);
+  if (c->head_dim == 64)
+    cache_write8_kernel<E, 64><<<dim3(grid), dim3(256), 0, s>>>(k, v, slots, kc, vc, c->k_scales,
+                                                                c->v_scales, n, c->num_kv_heads, num_slots);
+  else
+    cache_write8_kernel<E, 128><<<dim3(grid), dim3(256), 0, s>>>(k, v, slots, kc, vc, c->k_scales,
+                                                                 c->v_scales, n, c->num_kv_heads, num_slots);
+}
+
+// The quantising store of new tokens into FP8 pools (grid: one thread per 8 dims).
+void launch_write8(const pa_cache* c, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                   int32_t n, int64_t num_slots, int64_t grid, hipStream_t s) {
+  if (c->dtype == PA_F16)
+    launch_write8_t<F16>(c, k, v, slots, n, num_slots, grid, s);
+  else
+    launch_write8_t<BF16>(c, k, v, slots, n, num_slots, grid, s);
 }
 
 }  // namespace
@@ -948,9 +1062,20 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
     if (!v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
       return pa::fail(PA_ERR_INVALID_ARG, "%s: k_new / v_new / slot_mapping NULL or misaligned", fn);
-    su.args.k_new = static_cast<const uint16_t*>(k_new);
-    su.args.v_new = static_cast<const uint16_t*>(v_new);
-    su.args.new_slots = slot_mapping;
+    if (su.fp8) {
+      // FP8 pools: the quantising store is its own launch, before the attention pass
+      const int64_t grid = (static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
+                            (cache->head_dim / 8) + 255) / 256;
+      launch_write8(cache, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                    slot_mapping, num_seqs, static_cast<int64_t>(cache->num_blocks) * kBlock, grid,
+                    static_cast<hipStream_t>(stream));
+      st = launch_status(fn);
+      if (st != PA_OK) return st;
+    } else {
+      su.args.k_new = static_cast<const uint16_t*>(k_new);
+      su.args.v_new = static_cast<const uint16_t*>(v_new);
+      su.args.new_slots = slot_mapping;
+    }
   }
   const int32_t P = su.args.max_parts;
   if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())
@@ -1007,6 +1132,10 @@ pa_status pa_cache_write(const pa_cache* cache, const void* k, const void* v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto kp = static_cast<const uint16_t*>(k);
   auto vp = static_cast<const uint16_t*>(v);
+  if (cache->flags & PA_CACHE_FP8) {
+    launch_write8(cache, kp, vp, slot_mapping, num_tokens, num_slots, grid, s);
+    return launch_status("pa_cache_write");
+  }
   auto kc = static_cast<uint16_t*>(cache->k_cache);
   auto vc = static_cast<uint16_t*>(cache->v_cache);
   if (D == 64)
@@ -1042,7 +1171,8 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, const int3
     for (int32_t b = 0; b < nb; ++b)
       if (role[b] == 3) return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: block %d is source and destination", b);
   }
-  const int64_t vecs = static_cast<int64_t>(cache->num_kv_heads) * kBlock * cache->head_dim * 2 / 16;
+  const int64_t elem = (cache->flags & PA_CACHE_FP8) ? 1 : 2;
+  const int64_t vecs = static_cast<int64_t>(cache->num_kv_heads) * kBlock * cache->head_dim * elem / 16;
   const int64_t gx = std::min<int64_t>((vecs + 255) / 256, 64);
   copy_blocks_kernel<<<dim3(gx, num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       pairs, static_cast<u32x4*>(cache->k_cache), static_cast<u32x4*>(cache->v_cache), vecs,

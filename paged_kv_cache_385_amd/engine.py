@@ -39,30 +39,46 @@ def _round(n: int) -> int:
 
 
 class PagedKVCache:
+    """K/V pools, their host block manager, and the device operations on them.
+
+    ``dtype`` is the float16/bfloat16 dtype of the tokens written and of q/out.  With
+    ``kv_scales`` = (k_scales, v_scales) -- one positive float per KV head each -- the
+    pools hold 8-bit E4M3 codes of x / scale instead (``PA_CACHE_FP8``)."""
+
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  device="cuda", free_order: Optional[Sequence[int]] = None,
-                 fill_bits: Optional[int] = None):
+                 fill_bits: Optional[int] = None, kv_scales=None):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.dtype = dtype
         self.device = torch.device(device)
+        self.fp8 = kv_scales is not None
+        self.scales = None
+        if self.fp8:
+            self.scales = tuple(torch.as_tensor(np.asarray(s, dtype=np.float32)).reshape(num_kv_heads)
+                                .to(self.device).contiguous() for s in kv_scales)
         self.k_cache, self.v_cache = ops.alloc_pool(num_blocks, num_kv_heads, head_dim, dtype,
-                                                    self.device, fill_bits)
+                                                    self.device, fill_bits, fp8=self.fp8)
         self.bm = BlockManager(num_blocks, N.BLOCK_SIZE, free_order)
+
+    def descriptor(self, shared_blocks: bool = False) -> N.PaCache:
+        return ops.cache_desc(self.k_cache, self.v_cache, shared_blocks, scales=self.scales,
+                              dtype=self.dtype)
 
     # ---- device operations ----------------------------------------------------------
     def write(self, k: torch.Tensor, v: torch.Tensor, slots) -> None:
         if isinstance(slots, np.ndarray):
             slots = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(self.device)
-        ops.cache_write(self.k_cache, self.v_cache, k.to(self.device), v.to(self.device), slots)
+        ops.cache_write(self.k_cache, self.v_cache, k.to(self.device), v.to(self.device), slots,
+                        scales=self.scales)
 
     def copy(self, pairs: np.ndarray) -> None:
         pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
         if len(pairs) == 0:
             return
         ops.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(pairs).to(self.device),
-                        pairs_host=pairs)
+                        pairs_host=pairs, scales=self.scales)
 
     # ---- trace replay ----------------------------------------------------------------
     def apply_trace(self, trace: Iterable[tuple],
@@ -170,7 +186,7 @@ class DecodeBatch:
         self.out = torch.empty((B, num_heads, cache.head_dim), dtype=cache.dtype, device=dev)
         self.workspace = ops.alloc_workspace(B, num_heads, cache.head_dim,
                                              max_blocks_per_seq * N.BLOCK_SIZE, dev)
-        self._desc = ops.cache_desc(cache.k_cache, cache.v_cache)
+        self._desc = cache.descriptor()
         self._info = N.PaStepInfo()
         self._sids_ptr = self.sids.ctypes.data
         self._device = cache.k_cache.device

@@ -26,9 +26,28 @@ def v_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int) -> Tuple[int
     return (num_blocks, num_kv_heads, N.BLOCK_SIZE // 4, head_dim, 4)
 
 
+def k8_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int) -> Tuple[int, ...]:
+    """FP8 K pool: [NB, Hkv, D/64, 16, 4, 2, 8] bytes (see pa.h)."""
+    return (num_blocks, num_kv_heads, head_dim // 64, N.BLOCK_SIZE, 4, 2, 8)
+
+
+def v8_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int) -> Tuple[int, ...]:
+    """FP8 V pool: [NB, Hkv, 4, D/64, 16, 2, 2, 4] bytes (see pa.h)."""
+    return (num_blocks, num_kv_heads, N.BLOCK_SIZE // 4, head_dim // 64, 16, 2, 2, 4)
+
+
 def alloc_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
-               device="cuda", fill_bits: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """K and V pools in the library layout; ``fill_bits`` fills every element with a 16-bit pattern."""
+               device="cuda", fill_bits: Optional[int] = None, fp8: bool = False
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V pools in the library layout; ``fill_bits`` fills every element with a bit
+    pattern (16-bit, or 8-bit for ``fp8`` pools, which are uint8 tensors of E4M3 codes)."""
+    if fp8:
+        k = torch.empty(k8_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=torch.uint8, device=device)
+        v = torch.empty(v8_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=torch.uint8, device=device)
+        if fill_bits is not None:
+            k.fill_(int(fill_bits) & 0xFF)
+            v.fill_(int(fill_bits) & 0xFF)
+        return k, v
     k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=dtype, device=device)
     v = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim), dtype=dtype, device=device)
     if fill_bits is not None:
@@ -43,17 +62,43 @@ def _stream_ptr(stream, device) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
-def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, shared_blocks: bool = False) -> N.PaCache:
-    """Descriptor of a pool pair; ``shared_blocks``: blocks may be shared within one call."""
-    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DT:
-        raise TypeError("pools must both be float16 or both bfloat16")
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, shared_blocks: bool = False,
+               scales: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+               dtype: Optional[torch.dtype] = None) -> N.PaCache:
+    """Descriptor of a pool pair; ``shared_blocks``: blocks may be shared within one call.
+
+    FP8 pools (uint8 tensors of E4M3 codes) need ``scales`` = (k_scales, v_scales),
+    float32 [Hkv] device tensors, and ``dtype``, the float16/bfloat16 dtype of q, out
+    and of the k / v written into them."""
     if not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("pools must be contiguous device tensors")
+    shared = N.PA_CACHE_SHARED_BLOCKS if shared_blocks else 0
+    if k_cache.dtype == torch.uint8:
+        if v_cache.dtype != torch.uint8 or scales is None or dtype not in _DT:
+            raise ValueError("FP8 pools need uint8 K and V, scales=(k_scales, v_scales) and dtype")
+        nb, hkv, dp, bs = (int(x) for x in k_cache.shape[:4])
+        D = dp * 64
+        if (tuple(k_cache.shape) != k8_pool_shape(nb, hkv, D)
+                or tuple(v_cache.shape) != v8_pool_shape(nb, hkv, D)):
+            raise ValueError(f"FP8 pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} "
+                             "do not match the layout")
+        ks, vs = scales
+        for t, name in ((ks, "k_scales"), (vs, "v_scales")):
+            _need(t, torch.float32, k_cache.device, name, (hkv,))
+        return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, D, _DT[dtype],
+                         shared | N.PA_CACHE_FP8, ks.data_ptr(), vs.data_ptr())
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DT:
+        raise TypeError("pools must both be float16 or both bfloat16 (or uint8 FP8 codes)")
     nb, hkv, dc, bs, eight = k_cache.shape
     if eight != 8 or bs != N.BLOCK_SIZE or tuple(v_cache.shape) != v_pool_shape(nb, hkv, dc * 8):
         raise ValueError(f"pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} do not match the layout")
     return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, dc * 8, _DT[k_cache.dtype],
-                     N.PA_CACHE_SHARED_BLOCKS if shared_blocks else 0)
+                     shared, None, None)
+
+
+def _compute_dtype(k_cache: torch.Tensor, t: torch.Tensor) -> torch.dtype:
+    """The float16/bfloat16 dtype of a call: the pool's, or (FP8 pools) the given tensor's."""
+    return t.dtype if k_cache.dtype == torch.uint8 else k_cache.dtype
 
 
 def _need(t: torch.Tensor, dtype, device, name, shape=None):
@@ -63,19 +108,22 @@ def _need(t: torch.Tensor, dtype, device, name, shape=None):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def cache_write(k_cache, v_cache, k, v, slot_mapping, stream=None) -> None:
-    desc = cache_desc(k_cache, v_cache)
+def cache_write(k_cache, v_cache, k, v, slot_mapping, stream=None, scales=None) -> None:
+    dt = _compute_dtype(k_cache, k)
+    desc = cache_desc(k_cache, v_cache, scales=scales, dtype=dt)
     T = k.shape[0]
     shp = (T, desc.num_kv_heads, desc.head_dim)
-    _need(k, k_cache.dtype, k_cache.device, "k", shp)
-    _need(v, k_cache.dtype, k_cache.device, "v", shp)
+    _need(k, dt, k_cache.device, "k", shp)
+    _need(v, dt, k_cache.device, "v", shp)
     _need(slot_mapping, torch.int64, k_cache.device, "slot_mapping", (T,))
     N.check(N.lib().pa_cache_write(C.byref(desc), k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                    T, _stream_ptr(stream, k_cache.device)), "pa_cache_write")
 
 
-def copy_blocks(k_cache, v_cache, pairs, pairs_host: Optional[np.ndarray] = None, stream=None) -> None:
-    desc = cache_desc(k_cache, v_cache)
+def copy_blocks(k_cache, v_cache, pairs, pairs_host: Optional[np.ndarray] = None, stream=None,
+                scales=None) -> None:
+    desc = cache_desc(k_cache, v_cache, scales=scales,
+                      dtype=torch.bfloat16 if k_cache.dtype == torch.uint8 else None)
     n = pairs.shape[0]
     _need(pairs, torch.int32, k_cache.device, "pairs", (n, 2))
     host = None
@@ -104,10 +152,11 @@ def workspace_counter_bytes(num_seqs: int, num_heads: int) -> int:
 
 
 def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace,
-                 shared_blocks=False):
-    desc = cache_desc(k_cache, v_cache, shared_blocks)
+                 shared_blocks=False, scales=None):
+    dt = _compute_dtype(k_cache, q)
+    desc = cache_desc(k_cache, v_cache, shared_blocks, scales=scales, dtype=dt)
     B, H, D = q.shape
-    _need(q, k_cache.dtype, k_cache.device, "q")
+    _need(q, dt, k_cache.device, "q")
     if D != desc.head_dim:
         raise ValueError("q head_dim differs from the pool's")
     _need(block_tables, torch.int32, k_cache.device, "block_tables")
@@ -116,17 +165,18 @@ def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace
     _need(context_lens, torch.int32, k_cache.device, "context_lens", (B,))
     if out is None:
         out = torch.empty_like(q)
-    _need(out, k_cache.dtype, k_cache.device, "out", (B, H, D))
+    _need(out, dt, k_cache.device, "out", (B, H, D))
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     return desc, B, H, out, ws_ptr, ws_bytes
 
 
 def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int, scale: float,
-           out=None, workspace=None, stream=None, shared_blocks: bool = False) -> torch.Tensor:
+           out=None, workspace=None, stream=None, shared_blocks: bool = False,
+           scales=None) -> torch.Tensor:
     """pa_decode: attention pass then log-sum-exp merge; returns out [B, H, D]."""
     desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
-                                            workspace, shared_blocks)
+                                            workspace, shared_blocks, scales)
     N.check(N.lib().pa_decode(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
                               block_tables.shape[1], context_lens.data_ptr(), max_context_len,
                               scale, out.data_ptr(), ws, wsb, _stream_ptr(stream, q.device)),
@@ -136,13 +186,13 @@ def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int
 
 def decode_fused(k_cache, v_cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
                  max_context_len: int, scale: float, out=None, workspace=None,
-                 stream=None) -> torch.Tensor:
+                 stream=None, scales=None) -> torch.Tensor:
     """pa_decode_fused: store each sequence's newest token, then decode; returns out [B, H, D]."""
     desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
-                                            workspace)
+                                            workspace, False, scales)
     shp = (B, desc.num_kv_heads, desc.head_dim)
-    _need(k_new, k_cache.dtype, k_cache.device, "k_new", shp)
-    _need(v_new, k_cache.dtype, k_cache.device, "v_new", shp)
+    _need(k_new, q.dtype, k_cache.device, "k_new", shp)
+    _need(v_new, q.dtype, k_cache.device, "v_new", shp)
     _need(slot_mapping, torch.int64, k_cache.device, "slot_mapping", (B,))
     N.check(N.lib().pa_decode_fused(C.byref(desc), k_new.data_ptr(), v_new.data_ptr(),
                                     slot_mapping.data_ptr(), q.data_ptr(), B, H,
@@ -153,9 +203,10 @@ def decode_fused(k_cache, v_cache, k_new, v_new, slot_mapping, q, block_tables, 
 
 
 def decode_attention(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
-                     scale: float, out=None, workspace=None, stream=None) -> torch.Tensor:
+                     scale: float, out=None, workspace=None, stream=None,
+                     scales=None) -> torch.Tensor:
     desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
-                                            workspace)
+                                            workspace, False, scales)
     N.check(N.lib().pa_decode_attention(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
                                         block_tables.shape[1], context_lens.data_ptr(),
                                         max_context_len, scale, out.data_ptr(), ws, wsb,
@@ -164,8 +215,8 @@ def decode_attention(k_cache, v_cache, q, block_tables, context_lens, max_contex
 
 
 def decode_merge(k_cache, v_cache, context_lens, max_context_len: int, out, workspace=None,
-                 stream=None) -> torch.Tensor:
-    desc = cache_desc(k_cache, v_cache)
+                 stream=None, scales=None) -> torch.Tensor:
+    desc = cache_desc(k_cache, v_cache, scales=scales, dtype=_compute_dtype(k_cache, out))
     B, H, D = out.shape
     _need(context_lens, torch.int32, k_cache.device, "context_lens", (B,))
     ws, wsb = (None, 0) if workspace is None else (workspace.data_ptr(),

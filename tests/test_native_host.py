@@ -78,6 +78,14 @@ def test_cache_flags_validation():
     assert lib.pa_decode(C.byref(c), FAKE, 1, 2, FAKE, 1, FAKE, 16, 0.1, FAKE, FAKE, 4096, None) \
         == N.PA_ERR_INVALID_ARG
     assert b"flags" in lib.pa_last_error()
+    # FP8 pools need both scale arrays, 4-byte aligned
+    for kw in (dict(), dict(k_scales=FAKE), dict(k_scales=FAKE, v_scales=FAKE + 2)):
+        c8 = _cache(flags=N.PA_CACHE_FP8, **kw)
+        assert lib.pa_cache_write(C.byref(c8), FAKE, FAKE, FAKE, 4, None) == N.PA_ERR_INVALID_ARG
+        assert b"scales" in lib.pa_last_error()
+    c8 = _cache(flags=N.PA_CACHE_FP8, k_scales=FAKE, v_scales=FAKE)
+    assert lib.pa_chunk_attention(C.byref(c8), FAKE, FAKE, 2, 12, 6, 4, FAKE, 200, FAKE, 3000, 0.1,
+                                  FAKE, None, 0, None) == N.PA_ERR_UNSUPPORTED
 
 
 @no_device
