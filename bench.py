@@ -58,6 +58,9 @@ def parse():
                          "host memory, copied on the step's stream, or copied on a side stream "
                          "(overlapping the previous step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--kv-dtype", choices=("native", "fp8"), default="native",
+                    help="KV pools in the workload's 16-bit dtype, or as FP8 (E4M3) codes with "
+                         "per-KV-head scales (q and out stay 16-bit)")
     ap.add_argument("--chunk", choices=("verify", "prefill"),
                     help="measure pa_chunk_attention instead of the decode step: 'verify' = the "
                          "70B-shaped batch with 6 new tokens per sequence (HBM-bound), 'prefill' = "
@@ -315,7 +318,12 @@ def main():
 
     # ---- set-up (not timed): replay the history through the library ----
     t0 = time.perf_counter()
-    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order)
+    fp8 = args.kv_dtype == "fp8"
+    # FP8 scales: the synthetic K/V are standard normal, so |x| / 0.0125 reaches the
+    # E4M3 range (448) only past 5.6 sigma
+    kv_scales = (np.full(Hkv, 0.0125, np.float32), np.full(Hkv, 0.0125, np.float32)) if fp8 else None
+    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order,
+                            kv_scales=kv_scales)
     segs = {}
 
     def tokens(seg, start, n):
@@ -347,7 +355,7 @@ def main():
         log(f"calibration copy: 3 x {args.copy_calibration} MiB device-to-device")
         del src, dst
 
-    per_tok = 2 * Hkv * D * 2                     # K and V bytes per cached token
+    per_tok = 2 * Hkv * D * (1 if fp8 else 2)     # K and V bytes per cached token
     base_ctx = wl.ctx_lens.astype(np.int64)
 
     def step_bytes(i):   # algorithmic bytes of the attention pass at step i (0-based)
@@ -397,7 +405,7 @@ def main():
         "dtype": wl.dtype_name,
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": 16, "kv_dtype": wl.dtype_name,
+                   "head_dim": D, "block_size": 16, "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype_name,
                    "context": CONTEXT_TEXT[wl.cfg_id],
                    "mean_context": round(float(base_ctx.mean() + W + (K - 1) / 2), 1),
                    "num_blocks": wl.num_blocks},
@@ -405,8 +413,9 @@ def main():
         "seq_steps_per_s": round(B * K / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload, K, W),
-                     "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}>",
+                     "traffic": None if fp8 else recorded_traffic(args.workload, K, W),
+                     "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}"
+                               + (",FP8>" if fp8 else ">"),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "bytes_per_launch": int(attn_bytes)},
     }
