@@ -91,21 +91,21 @@ class RefBlockManager:
                 if self._lens[sid] % self.block_size:
                     last = self._tables[sid][-1]
                     drop[last] = drop.get(last, 0) + 1
-        if need > len(self._free):
-            raise OutOfBlocks(f"batch needs {need} blocks, {len(self._free)} free")
+        if need > self._available():
+            raise OutOfBlocks(f"batch needs {need} blocks, {self._available()} available")
         slots, cows = [], []
         for sid in sids:
             table = self._tables[sid]
             n = self._lens[sid]
             off = n % self.block_size
             if off == 0:
-                blk = self._free.pop()
+                blk = self._take()
                 self._ref[blk] = 1
                 table.append(blk)
             else:
                 last = table[-1]
                 if self._ref[last] > 1:
-                    blk = self._free.pop()
+                    blk = self._take()
                     self._ref[blk] = 1
                     self._ref[last] -= 1
                     table[-1] = blk
@@ -125,8 +125,8 @@ class RefBlockManager:
         if count and n % self.block_size and self._ref[self._tables[sid][-1]] > 1:
             need += 1                       # the copy of the shared, partly filled last block
         need += blocks_needed(n + count, self.block_size) - blocks_needed(n, self.block_size)
-        if need > len(self._free):
-            raise OutOfBlocks(f"{count} tokens need {need} blocks, {len(self._free)} free")
+        if need > self._available():
+            raise OutOfBlocks(f"{count} tokens need {need} blocks, {self._available()} available")
         slots, cows = [], []
         for _ in range(count):
             s, c = self.append(sid)
@@ -152,7 +152,17 @@ class RefBlockManager:
         for blk in reversed(table):
             self._ref[blk] -= 1
             if self._ref[blk] == 0:
-                self._free.append(blk)
+                self._release(blk)
+
+    # -- where blocks come from and go to (the prefix cache overrides these) ----
+    def _available(self) -> int:
+        return len(self._free)
+
+    def _take(self) -> int:
+        return self._free.pop()
+
+    def _release(self, blk: int) -> None:
+        self._free.append(blk)
 
     # -- queries -----------------------------------------------------------------
     def block_table(self, sid: int) -> List[int]:
