@@ -315,6 +315,68 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
                      int32_t max_blocks, int32_t* ctx_lens, int32_t* max_ctx);
 
 /* ---------------------------------------------------------------------------
+ * Automatic prefix caching (host only).  A request whose leading tokens equal an
+ * earlier request's reuses the blocks computed for them and skips their prefill
+ * ("vLLM 核心概念", section 前缀缓存（Prefix Caching）, automatic matching;
+ * "PagedAttention 实战", section "Prefix Caching：让相同前缀不要反复算"); the
+ * system keeps block references, an index, a lifecycle and an eviction policy
+ * ("理解 vLLM PagedAttention", section 六), with hit-rate statistics, tenant
+ * isolation and invalidation when the model changes ("PagedAttention 实战",
+ * Prefix Caching and its fifth step).  Policies the pages leave open:
+ *   - the unit of reuse is a full block, identified exactly by the tenant and
+ *     the whole token prefix through its last token (a block's K/V depend on
+ *     every earlier token), never by its own 16 tokens alone;
+ *   - a block is indexed when its 16th token id is committed, unless its prefix
+ *     is already indexed (then it stays private) or it is indexed already; an
+ *     indexed block is full and is never written again;
+ *   - a new request matches its prompt's full blocks from the first, stopping
+ *     at the first miss, at most floor((n - 1) / 16) of them, so that at least
+ *     one prompt token is left to compute; each hit takes a reference;
+ *   - an indexed block whose last reference goes keeps its contents and becomes
+ *     evictable; other blocks return to the free stack;
+ *   - allocation pops the free stack first and only then evicts the evictable
+ *     block released longest ago (LRU; a freed sequence releases its tail block
+ *     first, so tails are evicted before heads); eviction drops the index entry;
+ *   - reset (a model change) drops every index entry and pushes the evictable
+ *     blocks onto the free stack, oldest release first.
+ * Capacity checks of the append calls count free and evictable blocks.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_bm_prefix_stats {
+  int64_t requests;          /* pa_bm_add_seq_cached calls */
+  int64_t query_blocks;      /* full blocks they were allowed to look up */
+  int64_t hit_blocks;        /* blocks they reused (hit rate = hit / query) */
+  int64_t cached_blocks;     /* blocks in the index now (any refcount) */
+  int64_t evictable_blocks;  /* indexed blocks with refcount 0 */
+  int64_t evictions;         /* index entries dropped to hand a block out */
+} pa_bm_prefix_stats;
+
+/* Turn prefix caching on; only while no sequence is live (PA_ERR_INVALID_ARG
+ * otherwise).  The calls below return PA_ERR_UNSUPPORTED until it is on. */
+pa_status pa_bm_enable_prefix_cache(pa_bm* bm);
+/* Create sequence seq_id for a prompt of n token ids (host int32[n]) under
+ * tenant >= 0 (a prefix only matches blocks committed under the same tenant).
+ * The sequence starts holding the matched blocks; *cached_tokens receives their
+ * token count (a multiple of 16, < n when n > 0), and those tokens count as
+ * committed.  The caller then appends (pa_bm_append_tokens) and computes the
+ * other n - *cached_tokens tokens. */
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, int64_t tenant, const int32_t* tokens,
+                               int32_t n, int32_t* cached_tokens);
+/* Token ids of a sequence's next `count` appended but uncommitted slots, in
+ * order, once their K/V are written; full blocks enter the index here.  More
+ * ids than uncommitted slots: PA_ERR_INVALID_ARG, nothing changes.  pa_bm_add_seq
+ * sequences commit under tenant 0; forks inherit the parent's tenant and
+ * committed ids. */
+pa_status pa_bm_commit_tokens(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t count);
+/* One id for each of n distinct sequences (a decode step); all or nothing. */
+pa_status pa_bm_commit_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, const int32_t* tokens);
+pa_status pa_bm_prefix_cache_reset(pa_bm* bm);
+pa_status pa_bm_prefix_stats_get(const pa_bm* bm, pa_bm_prefix_stats* out);
+/* Evictable blocks, next to evict first, into out[0..cap); *n = how many. */
+pa_status pa_bm_evictable_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+/* Indexed blocks in ascending order, into out[0..cap); *n = how many. */
+pa_status pa_bm_cached_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+/* ---------------------------------------------------------------------------
  * pa_chunk_attention -- several new tokens per sequence: the last q_len_b of
  * sequence b's context_lens[b] cached tokens are queries, and query i (position
  * context_lens[b] - q_len_b + i) attends over cached positions 0 .. its own.

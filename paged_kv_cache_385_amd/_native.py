@@ -39,6 +39,12 @@ class PaBmStats(C.Structure):
                 ("occupied_slots", C.c_int64), ("waste", C.c_double)]
 
 
+class PaBmPrefixStats(C.Structure):
+    _fields_ = [("requests", C.c_int64), ("query_blocks", C.c_int64), ("hit_blocks", C.c_int64),
+                ("cached_blocks", C.c_int64), ("evictable_blocks", C.c_int64),
+                ("evictions", C.c_int64)]
+
+
 class PaStepInfo(C.Structure):
     _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32)]
 
@@ -89,6 +95,14 @@ SIGNATURES = {
     "pa_bm_free_list": (C.c_int, [_P, _P, _I32, _PI32]),
     "pa_bm_stats_get": (C.c_int, [_P, C.POINTER(PaBmStats)]),
     "pa_bm_step": (C.c_int, [_P, _I32, _P, _P, _P, _I32, _PI32, _P, _I32, _P, _PI32]),
+    "pa_bm_enable_prefix_cache": (C.c_int, [_P]),
+    "pa_bm_add_seq_cached": (C.c_int, [_P, _I64, _I64, _P, _I32, _PI32]),
+    "pa_bm_commit_tokens": (C.c_int, [_P, _I64, _P, _I32]),
+    "pa_bm_commit_batch": (C.c_int, [_P, _I32, _P, _P]),
+    "pa_bm_prefix_cache_reset": (C.c_int, [_P]),
+    "pa_bm_prefix_stats_get": (C.c_int, [_P, C.POINTER(PaBmPrefixStats)]),
+    "pa_bm_evictable_list": (C.c_int, [_P, _P, _I32, _PI32]),
+    "pa_bm_cached_list": (C.c_int, [_P, _P, _I32, _PI32]),
     "pa_chunk_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_chunk_attention": (C.c_int, [C.POINTER(PaCache), _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
                                      _P, _I32, C.c_float, _P, _P, C.c_size_t, _P]),

@@ -15,10 +15,11 @@ def _ptr(a: np.ndarray) -> C.c_void_p:
 
 
 class BlockManager:
-    """Free list, reference counts, fork and copy-on-write; see pa.h for the policies."""
+    """Free list, reference counts, fork and copy-on-write, and (with prefix_caching)
+    automatic prefix caching; pa.h states the policies."""
 
     def __init__(self, num_blocks: int, block_size: int = N.BLOCK_SIZE,
-                 free_order: Optional[Sequence[int]] = None):
+                 free_order: Optional[Sequence[int]] = None, prefix_caching: bool = False):
         self._lib = N.lib()
         h = C.c_void_p()
         order = None
@@ -32,6 +33,8 @@ class BlockManager:
         self._h = h
         self.num_blocks = num_blocks
         self.block_size = block_size
+        if prefix_caching:
+            N.check(self._lib.pa_bm_enable_prefix_cache(self._h), "pa_bm_enable_prefix_cache")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -134,3 +137,47 @@ class BlockManager:
         st = N.PaBmStats()
         N.check(self._lib.pa_bm_stats_get(self._h, C.byref(st)), "pa_bm_stats_get")
         return {f: getattr(st, f) for f, _ in N.PaBmStats._fields_}
+
+    # -- automatic prefix caching ----------------------------------------------------
+    def add_seq_cached(self, sid: int, prompt, tenant: int = 0) -> int:
+        """New sequence holding the cached full blocks of ``prompt``; returns their tokens."""
+        ids = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32).reshape(-1))
+        cached = C.c_int32()
+        N.check(self._lib.pa_bm_add_seq_cached(self._h, sid, tenant, _ptr(ids), ids.shape[0],
+                                               C.byref(cached)), "pa_bm_add_seq_cached")
+        return cached.value
+
+    def commit_tokens(self, sid: int, token_ids) -> None:
+        ids = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32).reshape(-1))
+        N.check(self._lib.pa_bm_commit_tokens(self._h, sid, _ptr(ids), ids.shape[0]),
+                "pa_bm_commit_tokens")
+
+    def commit_batch(self, sids: Sequence[int], token_ids) -> None:
+        s = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
+        ids = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32).reshape(-1))
+        if ids.shape[0] != s.shape[0]:
+            raise ValueError("one token id per sequence")
+        N.check(self._lib.pa_bm_commit_batch(self._h, s.shape[0], _ptr(s), _ptr(ids)),
+                "pa_bm_commit_batch")
+
+    def reset_prefix_cache(self) -> None:
+        N.check(self._lib.pa_bm_prefix_cache_reset(self._h), "pa_bm_prefix_cache_reset")
+
+    def prefix_stats(self) -> dict:
+        st = N.PaBmPrefixStats()
+        N.check(self._lib.pa_bm_prefix_stats_get(self._h, C.byref(st)), "pa_bm_prefix_stats_get")
+        return {f: getattr(st, f) for f, _ in N.PaBmPrefixStats._fields_}
+
+    def _block_list(self, fn) -> List[int]:
+        n = C.c_int32()
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        N.check(getattr(self._lib, fn)(self._h, _ptr(out), self.num_blocks, C.byref(n)), fn)
+        return out[:n.value].tolist()
+
+    def evictable_blocks(self) -> List[int]:
+        """Evictable blocks, next to evict first."""
+        return self._block_list("pa_bm_evictable_list")
+
+    def cached_blocks(self) -> List[int]:
+        """Blocks in the prefix index, ascending."""
+        return self._block_list("pa_bm_cached_list")

@@ -1,12 +1,27 @@
-// Host block manager: free list, reference counts, fork and copy-on-write.
+// Host block manager: free list, reference counts, fork and copy-on-write,
+// and automatic prefix caching.
 //
 // Follows "理解 vLLM PagedAttention" sections 三 (blocks taken from one global
 // pool, appended as a sequence grows, returned when it ends, shared by pointing
 // logical blocks of several sequences at one physical block), 四 (allocation on
 // demand; waste confined to the last block) and 六 (sharing with copy-on-write
-// on divergence), and "vLLM 核心概念" sections "按需分配" and "内存共享".
+// on divergence; reuse of computed blocks for a repeated prefix, with an index,
+// lifecycle and eviction), "vLLM 核心概念" sections "按需分配", "内存共享" and
+// 前缀缓存, and "PagedAttention 实战" section "Prefix Caching" with its fifth
+// step (eviction, tenant isolation, invalidation on a model change).
 // The policies the pages leave open are stated in pa.h next to the pa_bm_*
 // declarations.  Pure host code: no device calls.
+//
+// Prefix index.  A full block is identified by its whole token prefix.  Each
+// distinct prefix that has been committed is a node of a trie keyed by
+// (parent node, the block's 16 token ids); the parent of a first block is a
+// per-tenant root id -(tenant + 1).  A node holds the block indexed for that
+// prefix (or -1) and stays alive while something pins it: its indexed block,
+// a child node, or a live sequence whose committed tokens end on it.  So a
+// prefix keeps its identity while anything below it is still indexed, and a
+// lookup compares keys exactly (no hash collisions can alias two prefixes).
+// Evictable blocks (indexed, refcount 0) sit on an intrusive LRU list in
+// release order.
 
 #include <algorithm>
 #include <cstring>
@@ -21,10 +36,45 @@ namespace {
 
 thread_local std::string g_last_error;
 
+constexpr int kBs = PA_BLOCK_SIZE;
+
 struct Seq {
   std::vector<int32_t> table;  // logical block j -> physical block
   int64_t len = 0;             // tokens stored
+  // prefix caching
+  int64_t tenant = 0;
+  int64_t committed = 0;       // tokens whose ids are known (a prefix of len)
+  int64_t node = -1;           // trie node of the committed full blocks (root id if none)
+  int32_t pend[kBs] = {};      // ids committed into the current partial block
 };
+
+struct PrefixKey {
+  int64_t parent;
+  int32_t tok[kBs];
+  bool operator==(const PrefixKey& o) const {
+    return parent == o.parent && std::memcmp(tok, o.tok, sizeof tok) == 0;
+  }
+};
+
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const {
+    uint64_t h = static_cast<uint64_t>(k.parent) * 0x9E3779B97F4A7C15ull;
+    for (int i = 0; i < kBs; ++i) {
+      h ^= static_cast<uint32_t>(k.tok[i]);
+      h *= 0xBF58476D1CE4E5B9ull;
+      h ^= h >> 29;
+    }
+    return static_cast<size_t>(h);
+  }
+};
+
+struct PrefixNode {
+  PrefixKey key;
+  int32_t block = -1;   // block indexed for this prefix, or -1
+  int32_t pins = 0;     // indexed block + child nodes + sequences ending here
+};
+
+int64_t root_id(int64_t tenant) { return -(tenant + 1); }
 
 }  // namespace
 
@@ -36,6 +86,95 @@ struct pa_bm {
   std::unordered_map<int64_t, Seq> seqs;
   std::unordered_map<int32_t, int32_t> scratch_drop;  // reused by batch planning
   int64_t n_shared = 0;             // blocks with refcount > 1
+
+  // prefix caching (off until pa_bm_enable_prefix_cache)
+  bool prefix_on = false;
+  std::unordered_map<PrefixKey, int64_t, PrefixKeyHash> index;  // key -> node id
+  std::unordered_map<int64_t, PrefixNode> nodes;
+  int64_t next_node = 0;
+  std::vector<int64_t> block_node;  // node a block is indexed under, or -1
+  std::vector<int32_t> lru_prev, lru_next;
+  int32_t lru_head = -1, lru_tail = -1;
+  int64_t n_evictable = 0, n_indexed = 0;
+  int64_t requests = 0, query_blocks = 0, hit_blocks = 0, evictions = 0;
+
+  int64_t available() const { return static_cast<int64_t>(free_stack.size()) + n_evictable; }
+
+  void lru_unlink(int32_t b) {
+    const int32_t p = lru_prev[b], n = lru_next[b];
+    (p >= 0 ? lru_next[p] : lru_head) = n;
+    (n >= 0 ? lru_prev[n] : lru_tail) = p;
+    lru_prev[b] = lru_next[b] = -1;
+    --n_evictable;
+  }
+  void lru_push(int32_t b) {
+    lru_prev[b] = lru_tail;
+    lru_next[b] = -1;
+    (lru_tail >= 0 ? lru_next[lru_tail] : lru_head) = b;
+    lru_tail = b;
+    ++n_evictable;
+  }
+  void pin(int64_t n) {
+    if (n >= 0) ++nodes.at(n).pins;
+  }
+  // Drops one pin; a node left with none leaves the trie and unpins its parent.
+  void unpin(int64_t n) {
+    while (n >= 0) {
+      auto it = nodes.find(n);
+      if (--it->second.pins > 0) return;
+      const int64_t parent = it->second.key.parent;
+      index.erase(it->second.key);
+      nodes.erase(it);
+      n = parent;
+    }
+  }
+  void unindex(int32_t b) {
+    const int64_t n = block_node[b];
+    block_node[b] = -1;
+    nodes.at(n).block = -1;
+    --n_indexed;
+    unpin(n);
+  }
+  // A block whose last reference went away.
+  void release(int32_t b) {
+    if (prefix_on && block_node[b] >= 0)
+      lru_push(b);
+    else
+      free_stack.push_back(b);
+  }
+  // The 16 committed ids of s's newest full block are in s.pend: index it.
+  void index_full_block(Seq& s) {
+    const int32_t blk = s.table[s.committed / kBs - 1];
+    PrefixKey key;
+    key.parent = s.node;
+    std::memcpy(key.tok, s.pend, sizeof key.tok);
+    int64_t id;
+    auto it = index.find(key);
+    if (it == index.end()) {
+      id = next_node++;
+      PrefixNode& nd = nodes[id];
+      nd.key = key;
+      index.emplace(key, id);
+      pin(s.node);                    // the new child pins its parent
+    } else {
+      id = it->second;
+    }
+    PrefixNode& nd = nodes.at(id);
+    if (nd.block < 0 && block_node[blk] < 0) {
+      nd.block = blk;
+      block_node[blk] = id;
+      ++nd.pins;
+      ++n_indexed;
+    }
+    pin(id);
+    unpin(s.node);
+    s.node = id;
+  }
+  void commit_one(Seq& s, int32_t token) {
+    s.pend[s.committed % kBs] = token;
+    ++s.committed;
+    if (s.committed % kBs == 0) index_full_block(s);
+  }
 
   void ref_inc(int32_t b) {
     if (++ref[b] == 2) ++n_shared;
@@ -54,9 +193,19 @@ struct pa_bm {
     auto it = seqs.find(id);
     return it == seqs.end() ? nullptr : &it->second;
   }
+  // The next block to hand out (the caller has checked available()): the free
+  // stack first, then the evictable block released longest ago.
   int32_t pop_free() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = lru_head;
+      lru_unlink(b);
+      unindex(b);
+      ++evictions;
+    }
     ref[b] = 1;
     return b;
   }
@@ -155,7 +304,9 @@ void pa_bm_destroy(pa_bm* bm) { delete bm; }
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: bm is NULL");
   if (bm->find(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
-  bm->seqs.emplace(seq_id, Seq{});
+  Seq s;
+  s.node = root_id(0);
+  bm->seqs.emplace(seq_id, std::move(s));
   return PA_OK;
 }
 
@@ -196,9 +347,9 @@ pa_status pa_bm_append_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64
       }
     }
   }
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_batch: needs %lld blocks, %zu free",
-                    (long long)need, bm->free_stack.size());
+  if (need > bm->available())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_batch: needs %lld blocks, %lld available",
+                    (long long)need, (long long)bm->available());
   int32_t nc = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t src, dst;
@@ -244,9 +395,9 @@ pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t count, int64_t*
   const int64_t first_new_block = (len + bs - 1) / bs;       // blocks held now
   const int64_t blocks_after = (len + count + bs - 1) / bs;
   need += blocks_after - first_new_block;
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_tokens: needs %lld blocks, %zu free",
-                    (long long)need, bm->free_stack.size());
+  if (need > bm->available())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_tokens: needs %lld blocks, %lld available",
+                    (long long)need, (long long)bm->available());
   int32_t nc = 0;
   for (int32_t i = 0; i < count; ++i) {
     int32_t src, dst;
@@ -268,6 +419,7 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (bm->find(child)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: sequence %lld exists", (long long)child);
   Seq c = *p;
   for (int32_t b : c.table) bm->ref_inc(b);
+  bm->pin(c.node);
   bm->seqs.emplace(child, std::move(c));
   return PA_OK;
 }
@@ -278,8 +430,9 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (it == bm->seqs.end()) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_free_seq: no sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& t = it->second.table;
   for (auto r = t.rbegin(); r != t.rend(); ++r) {
-    if (bm->ref_dec(*r) == 0) bm->free_stack.push_back(*r);
+    if (bm->ref_dec(*r) == 0) bm->release(*r);
   }
+  bm->unpin(it->second.node);
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -404,6 +557,152 @@ pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
   out->allocated_slots = used * bs;
   out->occupied_slots = occ;
   out->waste = used ? 1.0 - static_cast<double>(occ) / static_cast<double>(used * bs) : 0.0;
+  return PA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Automatic prefix caching
+// ---------------------------------------------------------------------------
+extern "C" {
+
+pa_status pa_bm_enable_prefix_cache(pa_bm* bm) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_cache: bm is NULL");
+  if (bm->prefix_on) return PA_OK;
+  if (!bm->seqs.empty())
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_cache: %zu sequences are live",
+                    bm->seqs.size());
+  bm->block_node.assign(bm->num_blocks, -1);
+  bm->lru_prev.assign(bm->num_blocks, -1);
+  bm->lru_next.assign(bm->num_blocks, -1);
+  bm->prefix_on = true;
+  return PA_OK;
+}
+
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, int64_t tenant, const int32_t* tokens,
+                               int32_t n, int32_t* cached_tokens) {
+  if (!bm || !cached_tokens || n < 0 || (n > 0 && !tokens) || tenant < 0 || tenant == INT64_MAX)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: bad arguments");
+  *cached_tokens = 0;
+  if (!bm->prefix_on)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_add_seq_cached: prefix caching is off");
+  if (bm->find(seq_id))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: sequence %lld exists", (long long)seq_id);
+  Seq s;
+  s.tenant = tenant;
+  int64_t node = root_id(tenant);
+  const int32_t most = n > 0 ? (n - 1) / kBs : 0;   // one prompt token stays to compute
+  int32_t hits = 0;
+  PrefixKey key;
+  for (; hits < most; ++hits) {
+    key.parent = node;
+    std::memcpy(key.tok, tokens + static_cast<int64_t>(hits) * kBs, sizeof key.tok);
+    auto it = bm->index.find(key);
+    if (it == bm->index.end()) break;
+    const int32_t blk = bm->nodes.at(it->second).block;
+    if (blk < 0) break;
+    if (bm->ref[blk] == 0) bm->lru_unlink(blk);
+    bm->ref_inc(blk);
+    s.table.push_back(blk);
+    node = it->second;
+  }
+  s.len = s.committed = static_cast<int64_t>(hits) * kBs;
+  s.node = node;
+  bm->pin(node);
+  bm->seqs.emplace(seq_id, std::move(s));
+  bm->requests += 1;
+  bm->query_blocks += most;
+  bm->hit_blocks += hits;
+  *cached_tokens = hits * kBs;
+  return PA_OK;
+}
+
+pa_status pa_bm_commit_tokens(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t count) {
+  if (!bm || count < 0 || (count > 0 && !tokens))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_commit_tokens: bad arguments");
+  if (!bm->prefix_on)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_commit_tokens: prefix caching is off");
+  Seq* s = bm->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_commit_tokens: no sequence %lld", (long long)seq_id);
+  if (s->committed + count > s->len)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_commit_tokens: %d ids for %lld uncommitted tokens",
+                    count, (long long)(s->len - s->committed));
+  for (int32_t i = 0; i < count; ++i) bm->commit_one(*s, tokens[i]);
+  return PA_OK;
+}
+
+pa_status pa_bm_commit_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, const int32_t* tokens) {
+  if (!bm || n < 0 || (n > 0 && (!seq_ids || !tokens)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_commit_batch: bad arguments");
+  if (!bm->prefix_on)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_commit_batch: prefix caching is off");
+  std::vector<Seq*> ptr(n);
+  for (int32_t i = 0; i < n; ++i) {
+    ptr[i] = bm->find(seq_ids[i]);
+    if (!ptr[i]) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_commit_batch: no sequence %lld", (long long)seq_ids[i]);
+    if (ptr[i]->committed >= ptr[i]->len)
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_commit_batch: sequence %lld has no uncommitted token",
+                      (long long)seq_ids[i]);
+  }
+  {
+    std::vector<int64_t> ids(seq_ids, seq_ids + n);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end())
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_commit_batch: a sequence appears twice");
+  }
+  for (int32_t i = 0; i < n; ++i) bm->commit_one(*ptr[i], tokens[i]);
+  return PA_OK;
+}
+
+pa_status pa_bm_prefix_cache_reset(pa_bm* bm) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_prefix_cache_reset: bm is NULL");
+  if (!bm->prefix_on)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_prefix_cache_reset: prefix caching is off");
+  while (bm->lru_head >= 0) {                 // oldest release first onto the free stack
+    const int32_t b = bm->lru_head;
+    bm->lru_unlink(b);
+    bm->unindex(b);
+    bm->free_stack.push_back(b);
+  }
+  for (int32_t b = 0; b < bm->num_blocks; ++b)
+    if (bm->block_node[b] >= 0) bm->unindex(b);
+  return PA_OK;
+}
+
+pa_status pa_bm_prefix_stats_get(const pa_bm* bm, pa_bm_prefix_stats* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_prefix_stats_get: NULL argument");
+  out->requests = bm->requests;
+  out->query_blocks = bm->query_blocks;
+  out->hit_blocks = bm->hit_blocks;
+  out->cached_blocks = bm->n_indexed;
+  out->evictable_blocks = bm->n_evictable;
+  out->evictions = bm->evictions;
+  return PA_OK;
+}
+
+pa_status pa_bm_evictable_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_evictable_list: bad arguments");
+  int32_t k = 0;
+  if (bm->prefix_on)
+    for (int32_t b = bm->lru_head; b >= 0; b = bm->lru_next[b], ++k)
+      if (k < cap) out[k] = b;
+  *n = k;
+  return PA_OK;
+}
+
+pa_status pa_bm_cached_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_cached_list: bad arguments");
+  int32_t k = 0;
+  if (bm->prefix_on)
+    for (int32_t b = 0; b < bm->num_blocks; ++b)
+      if (bm->block_node[b] >= 0) {
+        if (k < cap) out[k] = b;
+        ++k;
+      }
+  *n = k;
   return PA_OK;
 }
 
