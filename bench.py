@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--kv-dtype", choices=("native", "fp8"), default="native",
                     help="KV pools in the workload's 16-bit dtype, or as FP8 (E4M3) codes with "
                          "per-KV-head scales (q and out stay 16-bit)")
+    ap.add_argument("--prefix", action="store_true",
+                    help="measure prefix-cached admission: 64 requests sharing a 2000-token system "
+                         "prompt (host block manager + K/V store + pa_chunk_attention), with the "
+                         "same step without prefix caching beside it")
     ap.add_argument("--chunk", choices=("verify", "prefill"),
                     help="measure pa_chunk_attention instead of the decode step: 'verify' = the "
                          "70B-shaped batch with 6 new tokens per sequence (HBM-bound), 'prefill' = "
@@ -287,8 +291,213 @@ def run_chunk(args):
     print(json.dumps(result), flush=True)
 
 
+PREFIX_REQUESTS = 64
+PREFIX_SYSTEM = 2000
+PREFIX_QUERY = (16, 128)
+
+
+def run_prefix(args):
+    """Admission of a batch of requests that share a system prompt, with and without
+    prefix caching.  One step: host admission (match, slots, commit of the ids), the
+    store of the computed tokens' K/V, and pa_chunk_attention of those tokens over the
+    whole context; then every sequence ends.  Each step brings fresh private queries,
+    so only the system prompt is reused (its blocks stay cached between steps)."""
+    import torch
+    import paged_kv_cache_385_amd as pa
+    from paged_kv_cache_385_amd import _native
+    from paged_kv_cache_385_amd.block_manager import BlockManager
+    from workloads.prefix import prompt_ids
+    assert torch.cuda.is_available(), "no HIP device"
+    _native.lib()
+    dev = torch.device("cuda:0")
+    K, W = args.steps, args.warmup
+    B, H, Hkv, D, dt = PREFIX_REQUESTS, 64, 8, 128, torch.bfloat16
+    name = (f"70B-shaped GQA-8 layer, {B} requests sharing a {PREFIX_SYSTEM}-token system prompt, "
+            f"private queries U{{{PREFIX_QUERY[0]}..{PREFIX_QUERY[1]}}} tokens")
+    log(f"prefix: {name}")
+    system = prompt_ids(385, 0, PREFIX_SYSTEM)
+    qrng = np.random.default_rng(np.random.SeedSequence([385, 99]))
+    # token ids as int32 arrays, the form a tokenizer hands over
+    steps_prompts = [[np.asarray(system + prompt_ids(385, 1 + s * B + i,
+                                                     int(qrng.integers(PREFIX_QUERY[0],
+                                                                       PREFIX_QUERY[1] + 1))),
+                                 dtype=np.int32)
+                      for i in range(B)] for s in range(K + W)]
+    flat = [np.concatenate(ps) for ps in steps_prompts]
+    offsets = [np.concatenate([[0], np.cumsum([len(p) for p in ps])]).astype(np.int64)
+               for ps in steps_prompts]
+    longest = max(len(p) for ps in steps_prompts for p in ps)
+    max_blocks = -(-longest // 16)
+    nb = B * (max_blocks + 1) + 64
+    k_cache, v_cache = pa.alloc_pool(nb, Hkv, D, dt, dev, fill_bits=0)
+    scale = D ** -0.5
+    tmax = B * longest
+    g = torch.Generator(device=dev)
+    g.manual_seed(385)
+    k_all = torch.randn((tmax, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+    v_all = torch.randn((tmax, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+    q_all = torch.randn((tmax, H, D), generator=g, device=dev, dtype=torch.float32).to(dt)
+    ws_bytes = pa.chunk_workspace_size(B, H, Hkv, D, tmax, longest, longest)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out_all = torch.empty_like(q_all)
+    stream = torch.cuda.current_stream(dev)
+
+    # per-step pinned staging (never reused within a run), so the host admission of one
+    # step overlaps the kernels of the previous one
+    def pinned(shape, dtype):
+        return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+    def run(cached_on):
+        bm = BlockManager(nb, prefix_caching=cached_on)
+        stage = [(pinned(tmax, torch.int64), pinned((B, max_blocks), torch.int32),
+                  pinned(B, torch.int32), pinned(B + 1, torch.int32)) for _ in range(K + W)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        host_s, shapes = 0.0, []
+        sids = np.arange(B, dtype=np.int64)
+        torch.cuda.synchronize()
+        t_start = None
+        for s in range(K + W):
+            if s == W:
+                torch.cuda.synchronize()
+                t_start = time.perf_counter()
+                st0 = bm.prefix_stats() if cached_on else None
+            prompts = steps_prompts[s]
+            th = time.perf_counter()
+            h_slots, h_tab, h_ctx, h_starts = stage[s]
+            slots = h_slots.numpy()
+            if cached_on:                        # one call: match, slots, commit of the ids
+                c, sl, _ = bm.admit_batch(sids, flat[s], offsets[s], slots_out=slots)
+                new = (np.diff(offsets[s]) - c).tolist()
+                pos = sl.shape[0]
+            else:
+                new, pos = [], 0
+                for i, p in enumerate(prompts):
+                    bm.add_seq(i)
+                    sl, _ = bm.append_tokens(i, len(p))
+                    slots[pos:pos + len(p)] = sl
+                    pos += len(p)
+                    new.append(len(p))
+            tables, ctx = bm.pack(sids, max_blocks, tables_out=h_tab.numpy(),
+                                  ctx_out=h_ctx.numpy())
+            starts = h_starts.numpy()
+            starts[0] = 0
+            np.cumsum(new, out=starts[1:])
+            T = pos
+            slots_d = h_slots[:T].to(dev, non_blocking=True)
+            tables_d = h_tab.to(dev, non_blocking=True)
+            ctx_d = h_ctx.to(dev, non_blocking=True)
+            starts_d = h_starts.to(dev, non_blocking=True)
+            mq, mc = max(new), int(ctx.max())
+            if s >= W:
+                host_s += time.perf_counter() - th
+                shapes.append((ctx.copy(), list(new)))
+            e = ev[s - W] if s >= W else None
+            if e:
+                e[0].record(stream)
+            pa.ops.cache_write(k_cache, v_cache, k_all[:T], v_all[:T], slots_d)
+            if e:
+                e[1].record(stream)
+            pa.chunk_attention(k_cache, v_cache, q_all[:T], starts_d, tables_d, ctx_d, mq, mc,
+                               scale, out=out_all[:T], workspace=ws)
+            if e:
+                e[2].record(stream)
+            for i in range(B):
+                bm.free_seq(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        write_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+        attn_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+        r = {"wall_s": wall, "host_us_per_request": host_s / (K * B) * 1e6,
+             "write_us": write_us, "attn_us": attn_us,
+             "new_tokens": sum(sum(n) for _, n in shapes) / K,
+             "flops": sum(chunk_flops(c, n, H, D) for c, n in shapes) / K}
+        if cached_on:
+            st = bm.prefix_stats()
+            r["hit_rate"] = (st["hit_blocks"] - st0["hit_blocks"]) / max(1, st["query_blocks"] - st0["query_blocks"])
+            r["stats"] = st
+        return r
+
+    cached = run(True)
+    full = run(False)
+    for tag, r in (("prefix caching", cached), ("no prefix caching", full)):
+        log(f"{tag}: {K} steps, wall {r['wall_s'] * 1e3 / K:.3f} ms/step, host "
+            f"{r['host_us_per_request']:.1f} us/request, K/V store {r['write_us']:.1f} us, "
+            f"attention {r['attn_us']:.1f} us, {r['new_tokens']:.0f} tokens computed per step")
+    value = B * K / cached["wall_s"]
+    tfs = cached["flops"] / (cached["attn_us"] * 1e-6) / 1e12
+    result = {"metric": "prefix-cached admission requests/s (shared system prompt)",
+              "value": round(value, 1), "unit": "requests/s", "n_gpus": 1, "steps": K, "warmup": W,
+              "ms_per_step": round(cached["wall_s"] * 1e3 / K, 4), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
+                         "head_dim": D, "block_size": 16, "kv_dtype": "bf16",
+                         "system_prompt": PREFIX_SYSTEM, "query_tokens": list(PREFIX_QUERY)},
+              "hit_rate": round(cached["hit_rate"], 4),
+              "tokens_computed_per_step": round(cached["new_tokens"], 1),
+              "host_us_per_request": round(cached["host_us_per_request"], 2),
+              "uncached": {"requests_per_s": round(B * K / full["wall_s"], 1),
+                           "ms_per_step": round(full["wall_s"] * 1e3 / K, 4),
+                           "tokens_computed_per_step": round(full["new_tokens"], 1),
+                           "attn_us": round(full["attn_us"], 1),
+                           "write_us": round(full["write_us"], 1)},
+              "speedup": round(full["wall_s"] / cached["wall_s"], 2),
+              "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                           "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                           "traffic": None, "kernel": "chunk_attn_kernel<BF16,128>",
+                           "avg_launch_us": round(cached["attn_us"], 2),
+                           "flops_per_launch": int(cached["flops"])}}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefix_cpu_baseline(args, steps_prompts[0], H, Hkv, D, scale)
+    print(json.dumps(result), flush=True)
+
+
+def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
+    """The oracle on a sample of the same step: its prefix cache admits the requests, and
+    its attention computes each admitted request's new tokens (float64 numpy)."""
+    from oracle import attention as OA
+    from oracle.prefix_cache import RefPrefixCache
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B = len(prompts)
+    nb = B * (-(-max(len(p) for p in prompts) // 16) + 1)
+    ref = RefPrefixCache(nb)
+    rng = np.random.default_rng(7)
+    t_total, done = 0.0, 0
+    # warm the cache with the first request (not timed), as the timed steps find it warm
+    c = ref.add_seq_cached(-1, prompts[0])
+    ref.append_tokens(-1, len(prompts[0]) - c)
+    ref.commit_tokens(-1, prompts[0][c:])
+    ref.free_seq(-1)
+    for i, p in enumerate(prompts):
+        if t_total > args.cpu_seconds:
+            break
+        k = rng.standard_normal((len(p), Hkv, D)).astype(np.float32)
+        v = rng.standard_normal((len(p), Hkv, D)).astype(np.float32)
+        t0 = time.perf_counter()
+        c = ref.add_seq_cached(i, p)
+        ref.append_tokens(i, len(p) - c)
+        ref.commit_tokens(i, p[c:])
+        q = rng.standard_normal((len(p) - c, H, D)).astype(np.float32)
+        OA.chunk_attention(q, k, v, scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {"value": done / t_total, "unit": "requests/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of the step's {B} requests: oracle prefix-cache admission and "
+                      f"float64 attention of their new tokens, {t_total:.1f} s"}
+
+
 def main():
     args = parse()
+    if args.prefix:
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+            sys.exit(2)
+        run_prefix(args)
+        return
     if args.chunk:
         if args.gpus != 1:
             print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)

@@ -361,6 +361,22 @@ pa_status pa_bm_enable_prefix_cache(pa_bm* bm);
  * other n - *cached_tokens tokens. */
 pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, int64_t tenant, const int32_t* tokens,
                                int32_t n, int32_t* cached_tokens);
+/* Admission of n requests in one call (what a serving loop does per step): for
+ * each i in order, pa_bm_add_seq_cached(seq_ids[i], tenants[i] (tenants NULL:
+ * all 0), prompt i), pa_bm_append_tokens of the prompt's other tokens and
+ * pa_bm_commit_tokens of their ids.  Prompt i is tokens[offsets[i] ..
+ * offsets[i+1]) (offsets: int64[n + 1], non-decreasing); a later request can
+ * reuse blocks an earlier one of the same call filled, so the caller stores the
+ * new tokens' K/V (one pa_cache_write of all of them) before any attention
+ * reads them.  cached: int32[n] reused tokens per request; slots: the new
+ * tokens' slots, request after request (slot_cap >= offsets[n] - offsets[0]
+ * always suffices).  *admitted receives how many requests (a prefix of the
+ * list) were admitted: on PA_ERR_OUT_OF_BLOCKS request *admitted was not (its
+ * matched blocks are released again) and the ones after it were not tried.
+ * Argument errors are found before anything changes. */
+pa_status pa_bm_admit_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, const int64_t* tenants,
+                            const int32_t* tokens, const int64_t* offsets, int32_t* cached,
+                            int64_t* slots, int64_t slot_cap, int32_t* admitted);
 /* Token ids of a sequence's next `count` appended but uncommitted slots, in
  * order, once their K/V are written; full blocks enter the index here.  More
  * ids than uncommitted slots: PA_ERR_INVALID_ARG, nothing changes.  pa_bm_add_seq

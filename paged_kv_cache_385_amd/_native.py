@@ -97,6 +97,7 @@ SIGNATURES = {
     "pa_bm_step": (C.c_int, [_P, _I32, _P, _P, _P, _I32, _PI32, _P, _I32, _P, _PI32]),
     "pa_bm_enable_prefix_cache": (C.c_int, [_P]),
     "pa_bm_add_seq_cached": (C.c_int, [_P, _I64, _I64, _P, _I32, _PI32]),
+    "pa_bm_admit_batch": (C.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I64, _PI32]),
     "pa_bm_commit_tokens": (C.c_int, [_P, _I64, _P, _I32]),
     "pa_bm_commit_batch": (C.c_int, [_P, _I32, _P, _P]),
     "pa_bm_prefix_cache_reset": (C.c_int, [_P]),

@@ -147,6 +147,38 @@ class BlockManager:
                                                C.byref(cached)), "pa_bm_add_seq_cached")
         return cached.value
 
+    def admit_batch(self, sids: Sequence[int], tokens, offsets, tenants=None,
+                    slots_out: Optional[np.ndarray] = None):
+        """pa_bm_admit_batch: prompts tokens[offsets[i]:offsets[i+1]] (int32, int64[n+1]).
+
+        Returns (cached int32[n], slots int64[new tokens], admitted).  On running out of
+        blocks, OutOfBlocks is raised after the admitted prefix of the list stays admitted;
+        its ``admitted`` attribute says how many."""
+        s = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
+        n = s.shape[0]
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        if off.shape != (n + 1,):
+            raise ValueError("offsets must have n + 1 entries")
+        ten = None
+        if tenants is not None:
+            ten = np.ascontiguousarray(np.asarray(tenants, dtype=np.int64))
+        total = int(off[-1] - off[0]) if n else 0
+        slots = slots_out if slots_out is not None else np.empty(max(total, 1), dtype=np.int64)
+        cached = np.zeros(max(n, 1), dtype=np.int32)
+        adm = C.c_int32()
+        st = self._lib.pa_bm_admit_batch(self._h, n, _ptr(s), None if ten is None else _ptr(ten),
+                                         _ptr(tok) if tok.size else None, _ptr(off), _ptr(cached),
+                                         _ptr(slots), slots.shape[0], C.byref(adm))
+        try:
+            N.check(st, "pa_bm_admit_batch")
+        except N.OutOfBlocks as e:
+            e.admitted = adm.value
+            raise
+        k = adm.value
+        new = int((np.diff(off[:k + 1]) - cached[:k]).sum()) if k else 0
+        return cached[:n], slots[:new], k
+
     def commit_tokens(self, sid: int, token_ids) -> None:
         ids = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32).reshape(-1))
         N.check(self._lib.pa_bm_commit_tokens(self._h, sid, _ptr(ids), ids.shape[0]),

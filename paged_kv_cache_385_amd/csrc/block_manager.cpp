@@ -14,12 +14,13 @@
 //
 // Prefix index.  A full block is identified by its whole token prefix.  Each
 // distinct prefix that has been committed is a node of a trie keyed by
-// (parent node, the block's 16 token ids); the parent of a first block is a
-// per-tenant root id -(tenant + 1).  A node holds the block indexed for that
-// prefix (or -1) and stays alive while something pins it: its indexed block,
-// a child node, or a live sequence whose committed tokens end on it.  So a
-// prefix keeps its identity while anything below it is still indexed, and a
-// lookup compares keys exactly (no hash collisions can alias two prefixes).
+// (parent node id, the block's 16 token ids); the parent of a first block is a
+// per-tenant root id -(tenant + 1).  The nodes live in the hash map itself, so
+// one probe per block resolves a lookup.  A node holds the block indexed for
+// that prefix (or -1) and stays alive while something pins it: its indexed
+// block, a child node, or a live sequence whose committed tokens end on it.
+// So a prefix keeps its identity while anything below it is still indexed, and
+// a lookup compares keys exactly (no hash collision can alias two prefixes).
 // Evictable blocks (indexed, refcount 0) sit on an intrusive LRU list in
 // release order.
 
@@ -38,13 +39,15 @@ thread_local std::string g_last_error;
 
 constexpr int kBs = PA_BLOCK_SIZE;
 
+struct PrefixNode;
+
 struct Seq {
   std::vector<int32_t> table;  // logical block j -> physical block
   int64_t len = 0;             // tokens stored
   // prefix caching
   int64_t tenant = 0;
   int64_t committed = 0;       // tokens whose ids are known (a prefix of len)
-  int64_t node = -1;           // trie node of the committed full blocks (root id if none)
+  PrefixNode* node = nullptr;  // trie node of the committed full blocks (none: root)
   int32_t pend[kBs] = {};      // ids committed into the current partial block
 };
 
@@ -69,9 +72,11 @@ struct PrefixKeyHash {
 };
 
 struct PrefixNode {
-  PrefixKey key;
-  int32_t block = -1;   // block indexed for this prefix, or -1
-  int32_t pins = 0;     // indexed block + child nodes + sequences ending here
+  int64_t id = 0;                 // unique, never reused: the key of the children
+  PrefixNode* parent = nullptr;   // nullptr for a first block
+  const PrefixKey* key = nullptr; // this node's key inside the map
+  int32_t block = -1;             // block indexed for this prefix, or -1
+  int32_t pins = 0;               // indexed block + child nodes + sequences ending here
 };
 
 int64_t root_id(int64_t tenant) { return -(tenant + 1); }
@@ -89,10 +94,9 @@ struct pa_bm {
 
   // prefix caching (off until pa_bm_enable_prefix_cache)
   bool prefix_on = false;
-  std::unordered_map<PrefixKey, int64_t, PrefixKeyHash> index;  // key -> node id
-  std::unordered_map<int64_t, PrefixNode> nodes;
+  std::unordered_map<PrefixKey, PrefixNode, PrefixKeyHash> index;  // the trie's nodes
   int64_t next_node = 0;
-  std::vector<int64_t> block_node;  // node a block is indexed under, or -1
+  std::vector<PrefixNode*> block_node;  // node a block is indexed under, or nullptr
   std::vector<int32_t> lru_prev, lru_next;
   int32_t lru_head = -1, lru_tail = -1;
   int64_t n_evictable = 0, n_indexed = 0;
@@ -114,61 +118,85 @@ struct pa_bm {
     lru_tail = b;
     ++n_evictable;
   }
-  void pin(int64_t n) {
-    if (n >= 0) ++nodes.at(n).pins;
+  static void pin(PrefixNode* n) {
+    if (n) ++n->pins;
   }
   // Drops one pin; a node left with none leaves the trie and unpins its parent.
-  void unpin(int64_t n) {
-    while (n >= 0) {
-      auto it = nodes.find(n);
-      if (--it->second.pins > 0) return;
-      const int64_t parent = it->second.key.parent;
-      index.erase(it->second.key);
-      nodes.erase(it);
+  void unpin(PrefixNode* n) {
+    while (n && --n->pins == 0) {
+      PrefixNode* parent = n->parent;
+      const PrefixKey key = *n->key;   // a copy: erasing frees the original
+      index.erase(key);
       n = parent;
     }
   }
   void unindex(int32_t b) {
-    const int64_t n = block_node[b];
-    block_node[b] = -1;
-    nodes.at(n).block = -1;
+    PrefixNode* n = block_node[b];
+    block_node[b] = nullptr;
+    n->block = -1;
     --n_indexed;
     unpin(n);
   }
   // A block whose last reference went away.
   void release(int32_t b) {
-    if (prefix_on && block_node[b] >= 0)
+    if (prefix_on && block_node[b])
       lru_push(b);
     else
       free_stack.push_back(b);
   }
+  static int64_t parent_id(const Seq& s) { return s.node ? s.node->id : root_id(s.tenant); }
   // The 16 committed ids of s's newest full block are in s.pend: index it.
   void index_full_block(Seq& s) {
     const int32_t blk = s.table[s.committed / kBs - 1];
     PrefixKey key;
-    key.parent = s.node;
+    key.parent = parent_id(s);
     std::memcpy(key.tok, s.pend, sizeof key.tok);
-    int64_t id;
-    auto it = index.find(key);
-    if (it == index.end()) {
-      id = next_node++;
-      PrefixNode& nd = nodes[id];
-      nd.key = key;
-      index.emplace(key, id);
+    auto ins = index.try_emplace(key);
+    PrefixNode& nd = ins.first->second;
+    if (ins.second) {
+      nd.id = next_node++;
+      nd.parent = s.node;
+      nd.key = &ins.first->first;
       pin(s.node);                    // the new child pins its parent
-    } else {
-      id = it->second;
     }
-    PrefixNode& nd = nodes.at(id);
-    if (nd.block < 0 && block_node[blk] < 0) {
+    if (nd.block < 0 && !block_node[blk]) {
       nd.block = blk;
-      block_node[blk] = id;
+      block_node[blk] = &nd;
       ++nd.pins;
       ++n_indexed;
     }
-    pin(id);
+    pin(&nd);
     unpin(s.node);
-    s.node = id;
+    s.node = &nd;
+  }
+  // A new sequence on the longest indexed prefix of tokens[0..n) (full blocks, at
+  // most (n - 1) / 16); arguments already checked.  Returns its cached tokens.
+  int32_t add_cached(int64_t seq_id, int64_t tenant, const int32_t* tokens, int32_t n) {
+    Seq& s = seqs[seq_id];
+    s.tenant = tenant;
+    PrefixNode* node = nullptr;
+    const int32_t most = n > 0 ? (n - 1) / kBs : 0;   // one prompt token stays to compute
+    int32_t hits = 0;
+    PrefixKey key;
+    s.table.reserve((n + kBs - 1) / kBs);
+    for (; hits < most; ++hits) {
+      key.parent = node ? node->id : root_id(tenant);
+      std::memcpy(key.tok, tokens + static_cast<int64_t>(hits) * kBs, sizeof key.tok);
+      auto it = index.find(key);
+      if (it == index.end() || it->second.block < 0) break;
+      const int32_t blk = it->second.block;
+      if (ref[blk] == 0) lru_unlink(blk);
+      ref_inc(blk);
+      s.table.push_back(blk);
+      node = &it->second;
+    }
+    s.len = s.committed = static_cast<int64_t>(hits) * kBs;
+    s.node = node;
+    pin(node);
+    requests += 1;
+    query_blocks += most;
+    hit_blocks += hits;
+    return hits * kBs;
   }
   void commit_one(Seq& s, int32_t token) {
     s.pend[s.committed % kBs] = token;
@@ -304,9 +332,7 @@ void pa_bm_destroy(pa_bm* bm) { delete bm; }
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: bm is NULL");
   if (bm->find(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
-  Seq s;
-  s.node = root_id(0);
-  bm->seqs.emplace(seq_id, std::move(s));
+  bm->seqs.emplace(seq_id, Seq{});
   return PA_OK;
 }
 
@@ -573,7 +599,7 @@ pa_status pa_bm_enable_prefix_cache(pa_bm* bm) {
   if (!bm->seqs.empty())
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_cache: %zu sequences are live",
                     bm->seqs.size());
-  bm->block_node.assign(bm->num_blocks, -1);
+  bm->block_node.assign(bm->num_blocks, nullptr);
   bm->lru_prev.assign(bm->num_blocks, -1);
   bm->lru_next.assign(bm->num_blocks, -1);
   bm->prefix_on = true;
@@ -589,32 +615,58 @@ pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, int64_t tenant, const 
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_add_seq_cached: prefix caching is off");
   if (bm->find(seq_id))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: sequence %lld exists", (long long)seq_id);
-  Seq s;
-  s.tenant = tenant;
-  int64_t node = root_id(tenant);
-  const int32_t most = n > 0 ? (n - 1) / kBs : 0;   // one prompt token stays to compute
-  int32_t hits = 0;
-  PrefixKey key;
-  for (; hits < most; ++hits) {
-    key.parent = node;
-    std::memcpy(key.tok, tokens + static_cast<int64_t>(hits) * kBs, sizeof key.tok);
-    auto it = bm->index.find(key);
-    if (it == bm->index.end()) break;
-    const int32_t blk = bm->nodes.at(it->second).block;
-    if (blk < 0) break;
-    if (bm->ref[blk] == 0) bm->lru_unlink(blk);
-    bm->ref_inc(blk);
-    s.table.push_back(blk);
-    node = it->second;
+  *cached_tokens = bm->add_cached(seq_id, tenant, tokens, n);
+  return PA_OK;
+}
+
+pa_status pa_bm_admit_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, const int64_t* tenants,
+                            const int32_t* tokens, const int64_t* offsets, int32_t* cached,
+                            int64_t* slots, int64_t slot_cap, int32_t* admitted) {
+  if (!bm || n < 0 || !admitted || (n > 0 && (!seq_ids || !offsets || !cached || !slots)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: bad arguments");
+  *admitted = 0;
+  if (!bm->prefix_on)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_admit_batch: prefix caching is off");
+  if (n == 0) return PA_OK;
+  if (offsets[0] < 0 || (offsets[n] > offsets[0] && !tokens))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: bad offsets or tokens");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = offsets[i + 1] - offsets[i];
+    if (len < 0 || len > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: prompt %d has %lld tokens", i, (long long)len);
+    if (tenants && (tenants[i] < 0 || tenants[i] == INT64_MAX))
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: tenant %lld", (long long)tenants[i]);
+    if (bm->find(seq_ids[i]))
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: sequence %lld exists", (long long)seq_ids[i]);
   }
-  s.len = s.committed = static_cast<int64_t>(hits) * kBs;
-  s.node = node;
-  bm->pin(node);
-  bm->seqs.emplace(seq_id, std::move(s));
-  bm->requests += 1;
-  bm->query_blocks += most;
-  bm->hit_blocks += hits;
-  *cached_tokens = hits * kBs;
+  if (slot_cap < offsets[n] - offsets[0])
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: slot_cap %lld < %lld prompt tokens",
+                    (long long)slot_cap, (long long)(offsets[n] - offsets[0]));
+  {
+    std::vector<int64_t> ids(seq_ids, seq_ids + n);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end())
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: a sequence appears twice");
+  }
+  int64_t pos = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t* p = tokens + offsets[i];
+    const int32_t len = static_cast<int32_t>(offsets[i + 1] - offsets[i]);
+    const int32_t c = bm->add_cached(seq_ids[i], tenants ? tenants[i] : 0, p, len);
+    Seq& s = bm->seqs.find(seq_ids[i])->second;
+    // the sequence holds c/16 full blocks: every further block is new
+    const int64_t need = (static_cast<int64_t>(len) + kBs - 1) / kBs - c / kBs;
+    if (need > bm->available()) {
+      pa_bm_free_seq(bm, seq_ids[i]);
+      return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_admit_batch: request %d needs %lld blocks, "
+                      "%lld available", i, (long long)need, (long long)bm->available());
+    }
+    int32_t src, dst;
+    for (int32_t t = c; t < len; ++t) slots[pos++] = bm->append_one(s, &src, &dst);
+    for (int32_t t = c; t < len; ++t) bm->commit_one(s, p[t]);
+    cached[i] = c;
+    *admitted = i + 1;
+  }
   return PA_OK;
 }
 
@@ -666,7 +718,7 @@ pa_status pa_bm_prefix_cache_reset(pa_bm* bm) {
     bm->free_stack.push_back(b);
   }
   for (int32_t b = 0; b < bm->num_blocks; ++b)
-    if (bm->block_node[b] >= 0) bm->unindex(b);
+    if (bm->block_node[b]) bm->unindex(b);
   return PA_OK;
 }
 
@@ -698,7 +750,7 @@ pa_status pa_bm_cached_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t*
   int32_t k = 0;
   if (bm->prefix_on)
     for (int32_t b = 0; b < bm->num_blocks; ++b)
-      if (bm->block_node[b] >= 0) {
+      if (bm->block_node[b]) {
         if (k < cap) out[k] = b;
         ++k;
       }

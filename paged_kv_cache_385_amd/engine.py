@@ -43,11 +43,13 @@ class PagedKVCache:
 
     ``dtype`` is the float16/bfloat16 dtype of the tokens written and of q/out.  With
     ``kv_scales`` = (k_scales, v_scales) -- one positive float per KV head each -- the
-    pools hold 8-bit E4M3 codes of x / scale instead (``PA_CACHE_FP8``)."""
+    pools hold 8-bit E4M3 codes of x / scale instead (``PA_CACHE_FP8``).  With
+    ``prefix_caching`` the block manager indexes committed full blocks and ``admit``
+    reuses them for requests whose prompts share a prefix."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  device="cuda", free_order: Optional[Sequence[int]] = None,
-                 fill_bits: Optional[int] = None, kv_scales=None):
+                 fill_bits: Optional[int] = None, kv_scales=None, prefix_caching: bool = False):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -60,7 +62,7 @@ class PagedKVCache:
                                 .to(self.device).contiguous() for s in kv_scales)
         self.k_cache, self.v_cache = ops.alloc_pool(num_blocks, num_kv_heads, head_dim, dtype,
                                                     self.device, fill_bits, fp8=self.fp8)
-        self.bm = BlockManager(num_blocks, N.BLOCK_SIZE, free_order)
+        self.bm = BlockManager(num_blocks, N.BLOCK_SIZE, free_order, prefix_caching)
 
     def descriptor(self, shared_blocks: bool = False) -> N.PaCache:
         return ops.cache_desc(self.k_cache, self.v_cache, shared_blocks, scales=self.scales,
@@ -108,6 +110,30 @@ class PagedKVCache:
                 self.write(k, v, slots)
             else:
                 raise ValueError(f"unknown operation {op[0]}")
+
+    def admit(self, sid: int, prompt: Sequence[int],
+              token_kv: Callable[[int, int], Tuple[torch.Tensor, torch.Tensor]],
+              tenant: int = 0) -> int:
+        """Admit a request with automatic prefix caching.
+
+        The sequence starts on the cached full blocks of ``prompt``; the other
+        tokens get slots, their K/V ``token_kv(start, n)`` are stored, and their
+        ids are committed so later requests can reuse the blocks they fill.  If
+        the pool cannot hold the rest, the sequence is dropped again and
+        OutOfBlocks propagates.  Returns the number of reused tokens (the
+        caller computes attention for the others only)."""
+        cached = self.bm.add_seq_cached(sid, prompt, tenant)
+        n = len(prompt) - cached
+        try:
+            slots, cows = self.bm.append_tokens(sid, n)
+        except N.OutOfBlocks:
+            self.bm.free_seq(sid)
+            raise
+        self.copy(cows)
+        k, v = token_kv(cached, n)
+        self.write(k, v, slots)
+        self.bm.commit_tokens(sid, list(prompt)[cached:])
+        return cached
 
     def tables(self, sids: Sequence[int], max_blocks: int) -> Tuple[torch.Tensor, torch.Tensor, int]:
         """Device block tables and context lengths for ``sids``, plus the host max context."""

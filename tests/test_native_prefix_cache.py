@@ -230,3 +230,76 @@ def test_hundred_thousand_block_lookups_are_fast():
     st = bm.prefix_stats()
     assert st["hit_blocks"] == 399 * 125 and st["query_blocks"] == 400 * 126
     assert dt < 5.0
+
+
+# -- batched admission -------------------------------------------------------------------
+def oracle_admit(ref, sids, prompts, tenants):
+    """The oracle's admission of a batch, request by request (match, append, commit); stops
+    at the first request that does not fit, releasing its matched blocks."""
+    cached, slots = [], []
+    for sid, p, t in zip(sids, prompts, tenants):
+        c = ref.add_seq_cached(sid, p, t)
+        try:
+            sl, cows = ref.append_tokens(sid, len(p) - c)
+        except RefOutOfBlocks:
+            ref.free_seq(sid)
+            return cached, slots, len(cached)
+        assert not cows
+        ref.commit_tokens(sid, p[c:])
+        cached.append(c)
+        slots += sl
+    return cached, slots, len(cached)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_admit_batch_matches_request_by_request_admission(seed):
+    r = random.Random(seed)
+    nb = 24 if seed % 2 else 300
+    order = list(range(nb))
+    r.shuffle(order)
+    ref, nat = RefPrefixCache(nb, 16, order), native(nb, order)
+    chunks = [P.toks(seed * 13 + i, 16) for i in range(3)]
+    live, nid, ran_out = [], 0, 0
+    for _ in range(40):
+        k = r.randrange(0, 9)
+        prompts = [sum((r.choice(chunks) for _ in range(r.randrange(0, 6))), [])
+                   + P.toks(r.randrange(10 ** 6), r.randrange(1, 30)) for _ in range(k)]
+        tenants = [int(r.random() < 0.25) for _ in range(k)]
+        sids = list(range(nid, nid + k))
+        nid += k
+        want_c, want_s, want_k = oracle_admit(ref, sids, prompts, tenants)
+        flat = np.array([t for p in prompts for t in p], dtype=np.int32)
+        offs = np.concatenate([[0], np.cumsum([len(p) for p in prompts])]).astype(np.int64)
+        try:
+            c, sl, got_k = nat.admit_batch(sids, flat, offs, tenants)
+        except N.OutOfBlocks as e:
+            got_k = e.admitted
+            ran_out += 1
+            assert want_k < k
+        else:
+            assert list(c) == want_c and list(map(int, sl)) == want_s
+        assert got_k == want_k
+        live += sids[:got_k]
+        same_state(ref, nat, live)
+        for sid in r.sample(live, r.randrange(0, len(live) + 1)):
+            live.remove(sid)
+            ref.free_seq(sid)
+            nat.free_seq(sid)
+        same_state(ref, nat, live)
+    if seed % 2:
+        assert ran_out > 0
+    assert nat.prefix_stats()["hit_blocks"] > 0
+
+
+def test_admit_batch_validates_before_changing_anything():
+    bm = native(16)
+    flat = np.arange(40, dtype=np.int32)
+    with pytest.raises(N.PaError):
+        bm.admit_batch([1, 1], flat, [0, 20, 40])          # twice the same sequence
+    with pytest.raises(N.PaError):
+        bm.admit_batch([1, 2], flat, [0, 30, 20])          # offsets go back
+    with pytest.raises(N.PaError):
+        bm.admit_batch([1, 2], flat, [0, 20, 40], tenants=[0, -3])
+    assert bm.prefix_stats()["requests"] == 0 and bm.free_list() == list(range(16))
+    c, sl, k = bm.admit_batch([1, 2], flat, [0, 20, 40])
+    assert (list(c), k, len(sl)) == ([0, 0], 2, 40)
