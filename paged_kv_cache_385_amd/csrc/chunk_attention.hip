@@ -11,15 +11,28 @@
 //                       columns, key partition); a column is one (new token, query
 //                       head of the KV head's group) pair, so a tile holds 16 / G
 //                       tokens of G heads
+//   chunk_wide_kernel   the same for launches with at least 128 columns per
+//                       (sequence, KV head): one workgroup per 128 columns
 //   chunk_merge_kernel  log-sum-exp merge of the key partitions ("PagedAttention
 //                       实战", section "2026 年的新变化": sequence split)
 //
-// The matrix-core mapping is the decode kernel's with the 16 query heads of a KV
-// head replaced by 16 columns: S^T = K.Q^T (16 tokens x 16 columns) with
-// v_mfma_f32_16x16x32, then out^T += V^T.P^T with v_mfma_f32_16x16x16, whose B
-// operand is the S^T register layout.  Lane l owns column l % 16, so the causal
-// mask, the online softmax and the rescale are lane-local.  The 4 waves split a
-// partition's blocks (every 4th) and combine in LDS.
+// chunk_attn_kernel: the matrix-core mapping is the decode kernel's with the 16
+// query heads of a KV head replaced by 16 columns: S^T = K.Q^T (16 tokens x 16
+// columns) with v_mfma_f32_16x16x32, then out^T += V^T.P^T with
+// v_mfma_f32_16x16x16, whose B operand is the S^T register layout.  Lane l owns
+// column l % 16, so the causal mask, the online softmax and the rescale are
+// lane-local.  The 4 waves split a partition's blocks (every 4th) and combine in
+// LDS.  Every K/V tile a workgroup reads serves 16 columns, which suits a few new
+// tokens per sequence (speculative verify) but makes long chunks L2-bound.
+//
+// chunk_wide_kernel: each wave owns 32 columns (two groups of 16) and all four
+// waves walk the same keys, two blocks (32 tokens) per stage, so a K/V tile
+// read from L2 serves 128 columns.  Each stage goes through LDS (double
+// buffered): K as stored, V interleaved as [token quad][dim][block][4 tokens].
+// Both products use v_mfma_f32_16x16x32: S^T of the two blocks is computed per
+// block, and out^T += V^T.P^T takes all 32 tokens at once, with lane l's eight
+// P values (tokens 4g..4g+3 of each block, g = l / 16, from the two S^T tiles)
+// as its B operand and the interleaved V rows as A.
 
 #include <hip/hip_runtime.h>
 
@@ -84,6 +97,7 @@ struct ChunkSeq {
   int32_t qs, n, ctx, cols, pmax;
   bool bad;   // context length outside [1, max_ctx], or more new tokens than cached ones
 };
+template <int kTileCols = kCols>
 __device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& it, ChunkSeq* s) {
   const int32_t qs = a.q_starts[it.b], qe = a.q_starts[it.b + 1];
   if (qs < 0 || qe < qs || qe > a.total) return false;
@@ -91,9 +105,9 @@ __device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& i
   s->n = qe - qs;
   s->ctx = a.ctx_lens[it.b];
   s->cols = s->n * a.group;
-  if (it.tile * kCols >= s->cols) return false;
+  if (it.tile * kTileCols >= s->cols) return false;
   s->bad = s->ctx < 1 || s->ctx > a.max_ctx || s->n > s->ctx;
-  const int32_t last_col = min(it.tile * kCols + kCols - 1, s->cols - 1);
+  const int32_t last_col = min(it.tile * kTileCols + kTileCols - 1, s->cols - 1);
   s->pmax = s->ctx - s->n + last_col / a.group;   // furthest position a tile column sees
   return true;
 }
@@ -328,6 +342,277 @@ void chunk_attn_kernel(ChunkArgs a) {
   }
 }
 
+constexpr int kWideCols = 128;                // columns per workgroup of the wide kernel
+constexpr int kWaveCols = kWideCols / kWaves; // 32 per wave: two groups of 16
+
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void chunk_wide_kernel(ChunkArgs a) {
+  constexpr int KK = D / 32;                 // 32-dim steps of q.K^T
+  constexpr int MT = D / 16;                 // 16-dim tiles of the output
+  constexpr int kTileElems = kBlock * D;     // one block's K (or V) tile
+  constexpr int kKChunks = 2 * kTileElems / 8 / kThreads;   // 16-byte K pieces per thread
+  constexpr int kVPairs = 2 * D;             // (token quad, dim pair) pieces of a stage's V
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][2 * kTileElems];
+
+  ChunkItem it;
+  if (!chunk_item(a, a.parts, &it)) return;
+  ChunkSeq sq;
+  if (!chunk_seq<kWideCols>(a, it, &sq)) return;
+  const int32_t b = __builtin_amdgcn_readfirstlane(it.b);
+  const int32_t kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  const int32_t part = __builtin_amdgcn_readfirstlane(it.part);
+  const int32_t tile = __builtin_amdgcn_readfirstlane(it.tile);
+  const int32_t ctx = __builtin_amdgcn_readfirstlane(sq.ctx);
+  const int32_t pmax = __builtin_amdgcn_readfirstlane(sq.pmax);
+  const int32_t G = a.group;
+  const int32_t H = a.num_heads;
+
+  const int32_t tid = threadIdx.x;
+  const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t lane = tid & 63;
+  const int32_t n = lane & 15;
+  const int32_t g4 = lane >> 4;
+
+  const bool direct = a.parts == 1;
+  const int32_t nblk_t = sq.bad ? 1 : pmax / kBlock + 1;
+  const int32_t pblocks = direct ? nblk_t : kPartBlocks;
+  if (part * pblocks >= nblk_t) return;
+
+  if (sq.bad) {
+    for (int32_t i = tid; i < kWideCols * D; i += kThreads) {
+      const int32_t c = tile * kWideCols + i / D;
+      if (c < sq.cols) {
+        const int64_t row = static_cast<int64_t>(sq.qs + c / G) * H + kvh * G + c % G;
+        a.out[row * D + i % D] = E::kNaN;
+      }
+    }
+    return;
+  }
+
+  // position of the tile's first column: keys up to it are seen by every column
+  const int32_t pmin = ctx - sq.n + (tile * kWideCols) / G;
+  // the lane's two columns (one per group of 16)
+  int32_t pos[2];
+  bool col_ok[2];
+  int64_t hrow[2];
+  u32x4 qf[2][KK];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int32_t col = tile * kWideCols + w * kWaveCols + gi * 16 + n;
+    col_ok[gi] = col < sq.cols;
+    const int32_t ti = col_ok[gi] ? col / G : 0;
+    const int32_t gh = col_ok[gi] ? col - ti * G : 0;
+    pos[gi] = col_ok[gi] ? ctx - sq.n + ti : pmax;        // padding columns: zero q
+    hrow[gi] = static_cast<int64_t>(sq.qs + ti) * H + kvh * G + gh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[gi][kk] = col_ok[gi] ? load16(a.q + hrow[gi] * D + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t jbeg = part * pblocks;
+  const int32_t jend = min(nblk_t, jbeg + pblocks);
+  const int32_t nstage = (jend - jbeg + 1) / 2;
+  const int64_t head_off = static_cast<int64_t>(kvh) * kTileElems;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * kTileElems;
+
+  // block ids in runs of 64: lane i holds the id of block jbeg + 64 r + i
+  int32_t ids = 0;
+  bool bad_blk = false;
+  auto load_ids = [&](int32_t r) {
+    const int32_t j = jbeg + 64 * r + lane;
+    int32_t v = j < jend ? bt[j] : 0;
+    const bool bad = j < jend && (v < 0 || v >= a.num_blocks);
+    if (bad) v = 0;
+    bad_blk = bad_blk || __ballot(bad) != 0;
+    ids = v;
+  };
+
+  // a stage's K and V, global -> registers -> LDS; two register sets, so the loads
+  // of a stage are issued two stages before it is computed
+  using KRegs = u32x4[kKChunks];
+  using VRegs = u32x4[2];
+  // Issued for every step, also past the last stage: the empty ranges of stages
+  // that do not exist read nothing, and no load sits behind a branch (which would
+  // make the compiler copy -- and so wait for -- the loaded registers).
+  auto stage_load = [&](int32_t st, KRegs& kst, VRegs& vst) {
+    const int32_t j0 = jbeg + 2 * st;
+    const int32_t l0 = (2 * st) & 63;                        // index within the id run
+    const int32_t p0 = __builtin_amdgcn_readlane(ids, l0);
+    const int32_t p1 = __builtin_amdgcn_readlane(ids, l0 + 1);
+    const int32_t bytes0 = j0 < jend ? kTileElems * 2 : 0;
+    const int32_t bytes1 = j0 + 1 < jend ? kTileElems * 2 : 0;
+#pragma unroll
+    for (int c = 0; c < kKChunks; ++c) {
+      // the wave's 64 pieces all lie in one block's tile (a tile is 128 or 256 pieces)
+      const int32_t wpiece = __builtin_amdgcn_readfirstlane(w * 64 + c * kThreads);
+      const bool second = wpiece >= kTileElems / 8;
+      const auto kr = tile_rsrc(a.k_cache + (second ? p1 : p0) * blk_stride + head_off,
+                                second ? bytes1 : bytes0);
+      kst[c] = load_tile<false>(kr, ((tid + c * kThreads) % (kTileElems / 8)) * 16);
+    }
+    // V: pieces tid < 2 D of both blocks (whole waves: 2 D is a multiple of 64); the
+    // other waves read an empty range
+    const int32_t vb = __builtin_amdgcn_readfirstlane(w * 64) < kVPairs ? 1 : 0;
+    const auto v0 = tile_rsrc(a.v_cache + p0 * blk_stride + head_off, bytes0 * vb);
+    const auto v1 = tile_rsrc(a.v_cache + p1 * blk_stride + head_off, bytes1 * vb);
+    vst[0] = load_tile<false>(v0, tid * 16);
+    vst[1] = load_tile<false>(v1, tid * 16);
+  };
+  auto stage_store = [&](int32_t st, int buf, const KRegs& kst, const VRegs& vst) {
+#pragma unroll
+    for (int c = 0; c < kKChunks; ++c)
+      *reinterpret_cast<u32x4*>(&s_k[buf][(tid + c * kThreads) * 8]) = kst[c];
+    if (tid < kVPairs) {
+      // piece tid holds token quad tq, dims d and d + 1, 4 tokens each, of one block
+      const int32_t tq = tid / (D / 2);
+      const int32_t d = 2 * (tid - tq * (D / 2));
+      const int32_t t0 = (jbeg + 2 * st) * kBlock + 4 * tq;   // position of the quad's token 0
+      u16x8 x0 = __builtin_bit_cast(u16x8, vst[0]);
+      u16x8 x1 = __builtin_bit_cast(u16x8, vst[1]);
+      // positions past the context may hold anything (NaN included): zero their V
+      if ((jbeg + 2 * st + 2) * kBlock > ctx) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (t0 + (e & 3) >= ctx) x0[e] = 0;
+          if (t0 + kBlock + (e & 3) >= ctx) x1[e] = 0;
+        }
+      }
+      const u16x8 lo = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const u16x8 hi = {x0[4], x0[5], x0[6], x0[7], x1[4], x1[5], x1[6], x1[7]};
+      uint16_t* dst = &s_v[buf][(tq * D + d) * 8];
+      *reinterpret_cast<u16x8*>(dst) = lo;
+      *reinterpret_cast<u16x8*>(dst + 8) = hi;
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[gi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int32_t st, int buf) {
+    f32x4 sc[2][2];   // [group][block]
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) sc[gi][0] = sc[gi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // all K operands first, then four independent accumulation chains per 32-dim step
+    u32x4 kf[2][KK];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kf[blk][kk] =
+            *reinterpret_cast<const u32x4*>(&s_k[buf][blk * kTileElems + (kk * 64 + lane) * 8]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        sc[0][blk] = E::mfma_qk(kf[blk][kk], qf[0][kk], sc[0][blk]);
+        sc[1][blk] = E::mfma_qk(kf[blk][kk], qf[1][kk], sc[1][blk]);
+      }
+    // V operands, read while the softmax runs
+    u32x4 vf[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      vf[t] = *reinterpret_cast<const u32x4*>(&s_v[buf][(g4 * D + 16 * t + n) * 8]);
+    const int32_t t0 = (jbeg + 2 * st) * kBlock;   // position of the stage's first key
+    // a stage wholly at or before the tile's first position needs no causal mask
+    const bool diag = t0 + 2 * kBlock - 1 > pmin;
+    const float c = a.scale_log2;
+    u32x4 pf[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      // raw scores; the running max m_run is kept in scaled log2 units
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = e < 4 ? sc[gi][0][e] : sc[gi][1][e - 4];
+      if (diag) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int32_t key = t0 + (e < 4 ? 4 * g4 + e : kBlock + 4 * g4 + e - 4);
+          if (key > pos[gi]) sv[e] = -INFINITY;
+        }
+      }
+      float bmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      bmax = col_max4(bmax);
+      const float m_new = fmaxf(m_run[gi], bmax * c);    // c > 0: the max commutes
+      // a column may have seen nothing yet: exponentiate against a finite stand-in
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[gi] - m_use);
+      m_run[gi] = m_new;
+      u16x8 pb;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = E::from_float(fast_exp2(__builtin_fmaf(sv[e], c, -m_use)));
+        psum += E::to_float(pb[e]);
+      }
+      l_run[gi] = l_run[gi] * alpha + psum;
+      if (__ballot(alpha != 1.f) != 0) {              // the running max moved somewhere
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[gi][t] *= alpha;
+      }
+      pf[gi] = __builtin_bit_cast(u32x4, pb);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      acc[0][t] = E::mfma_qk(vf[t], pf[0], acc[0][t]);
+      acc[1][t] = E::mfma_qk(vf[t], pf[1], acc[1][t]);
+    }
+  };
+
+  // free: the set that receives stage st + 2; held: the set holding stage st + 1
+  auto step = [&](int32_t st, KRegs& k_free, VRegs& v_free, const KRegs& k_held,
+                  const VRegs& v_held) {
+    if ((2 * (st + 2)) % 64 == 0) load_ids((2 * (st + 2)) / 64);
+    stage_load(st + 2, k_free, v_free);
+    compute(st, st & 1);
+    stage_store(st + 1, (st + 1) & 1, k_held, v_held);   // past the end: never read
+    __syncthreads();
+  };
+  u32x4 kA[kKChunks], vA[2], kB[kKChunks], vB[2];
+  load_ids(0);
+  stage_load(0, kA, vA);
+  stage_load(1, kB, vB);
+  stage_store(0, 0, kA, vA);
+  __syncthreads();
+  for (int32_t st = 0; st < nstage; st += 2) {
+    step(st, kA, vA, kB, vB);
+    if (st + 1 < nstage) step(st + 1, kB, vB, kA, vA);
+  }
+
+  // ---- outputs: lane l holds dims 16 t + 4 g4 .. + 3 of its two columns ----
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const float L = col_sum4(l_run[gi]);
+    if (!col_ok[gi]) continue;
+    if (direct) {
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        u16x4 ov;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = bad_blk ? E::kNaN : E::from_float(acc[gi][t][r] * inv);
+        *reinterpret_cast<u16x4*>(a.out + hrow[gi] * D + 16 * t + 4 * g4) = ov;
+      }
+    } else {
+      const int64_t st = hrow[gi] * a.parts + part;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const f32x4 o = bad_blk ? f32x4{NAN, NAN, NAN, NAN} : acc[gi][t];
+        *reinterpret_cast<f32x4*>(a.ws_acc + st * D + 16 * t + 4 * g4) = o;
+      }
+      if (g4 == 0) a.ws_ml[st] = bad_blk ? float2{0.f, NAN} : float2{m_run[gi], L};
+    }
+  }
+}
+
 // One workgroup per (sequence, KV head, column tile), 4 dims of one column per
 // thread: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
 // the partitions a column's own position reaches (later ones hold nothing for it),
@@ -368,32 +653,54 @@ __global__ __launch_bounds__(kThreads) void chunk_merge_kernel(ChunkArgs a) {
   }
 }
 
-// Key partitions of a launch: one when the column tiles alone give every
-// workgroup slot (three per compute unit) eight items, else partitions of 1024
+// The launch plan.  Launches with at least 128 columns per (sequence, KV head)
+// use the wide kernel.  Key partitions: one when the column tiles alone give
+// every workgroup slot enough items (eight for the narrow kernel at three
+// workgroups per compute unit, two for the wide one), else partitions of 1024
 // tokens, so long contexts with few new tokens still spread over the device and
 // no single workgroup walks a whole long context.
-int32_t chunk_parts(int32_t num_seqs, int32_t num_kv_heads, int32_t col_tiles, int32_t max_ctx) {
-  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * col_tiles;
-  if (items >= 8 * 3 * static_cast<int64_t>(pa::device_cus())) return 1;
-  return (max_ctx + kPartTokens - 1) / kPartTokens;
-}
-
-int32_t chunk_col_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len) {
+struct ChunkPlan {
+  bool wide;
+  int32_t tiles;        // column tiles of the attention launch
+  int32_t merge_tiles;  // 16-column tiles of the merge launch
+  int32_t parts;
+};
+ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len,
+                     int32_t max_ctx) {
+  ChunkPlan p;
   const int64_t cols = static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads);
-  return static_cast<int32_t>((cols + kCols - 1) / kCols);
+  p.wide = cols >= kWideCols;
+  p.merge_tiles = static_cast<int32_t>((cols + kCols - 1) / kCols);
+  p.tiles = p.wide ? static_cast<int32_t>((cols + kWideCols - 1) / kWideCols) : p.merge_tiles;
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * p.tiles;
+  const int64_t slots = (p.wide ? 2 : 8 * 3) * static_cast<int64_t>(pa::device_cus());
+  p.parts = items >= slots ? 1 : (max_ctx + kPartTokens - 1) / kPartTokens;
+  return p;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <class E>
-void launch_chunk(const ChunkArgs& a, int64_t grid, int64_t merge_grid, int d, hipStream_t s) {
-  if (d == 64) {
-    chunk_attn_kernel<E, 64><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
-    if (a.parts > 1) chunk_merge_kernel<E, 64><<<dim3(merge_grid), dim3(kThreads), 0, s>>>(a);
-  } else {
-    chunk_attn_kernel<E, 128><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
-    if (a.parts > 1) chunk_merge_kernel<E, 128><<<dim3(merge_grid), dim3(kThreads), 0, s>>>(a);
+template <class E, int D>
+void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(groups8 * p.tiles * p.parts));
+  if (p.wide)
+    chunk_wide_kernel<E, D><<<grid, dim3(kThreads), 0, s>>>(a);
+  else
+    chunk_attn_kernel<E, D><<<grid, dim3(kThreads), 0, s>>>(a);
+  if (p.parts > 1) {
+    ChunkArgs m = a;                     // the merge works in 16-column tiles
+    m.col_tiles = p.merge_tiles;
+    chunk_merge_kernel<E, D><<<dim3(static_cast<uint32_t>(groups8 * p.merge_tiles)),
+                               dim3(kThreads), 0, s>>>(m);
   }
+}
+
+template <class E>
+void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, hipStream_t s) {
+  if (d == 64)
+    launch_chunk_d<E, 64>(a, p, groups8, s);
+  else
+    launch_chunk_d<E, 128>(a, p, groups8, s);
 }
 
 }  // namespace
@@ -406,8 +713,7 @@ size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
       head_dim <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len <= 0)
     return 0;
-  const int32_t tiles = chunk_col_tiles(num_heads, num_kv_heads, max_q_len);
-  const int32_t P = chunk_parts(num_seqs, num_kv_heads, tiles, max_context_len);
+  const int32_t P = chunk_plan(num_seqs, num_heads, num_kv_heads, max_q_len, max_context_len).parts;
   if (P <= 1) return 0;
   const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
   return round256(static_cast<size_t>(rows) * sizeof(float2)) +
@@ -443,13 +749,14 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
     return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer or q / out not 16-byte aligned", fn);
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   const int32_t G = num_heads / cache->num_kv_heads;
-  const int32_t tiles = chunk_col_tiles(num_heads, cache->num_kv_heads, max_q_len);
-  const int32_t P = chunk_parts(num_seqs, cache->num_kv_heads, tiles, max_context_len);
+  const ChunkPlan plan = chunk_plan(num_seqs, num_heads, cache->num_kv_heads, max_q_len,
+                                    max_context_len);
+  const int32_t P = plan.parts;
   const int64_t groups = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
-  const int64_t per_xcd = (groups + 7) / 8;
-  const int64_t grid = 8 * per_xcd * tiles * P;
-  const int64_t merge_grid = 8 * per_xcd * tiles;
-  if (grid > INT32_MAX || static_cast<int64_t>(total_q) * num_heads * P > INT32_MAX)
+  const int64_t groups8 = 8 * ((groups + 7) / 8);
+  const int64_t grid = groups8 * plan.tiles * P;
+  if (grid > INT32_MAX || groups8 * plan.merge_tiles > INT32_MAX ||
+      static_cast<int64_t>(total_q) * num_heads * P > INT32_MAX)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: launch too large", fn);
   const size_t need = pa_chunk_workspace_size(num_seqs, num_heads, cache->num_kv_heads,
                                               cache->head_dim, total_q, max_q_len, max_context_len);
@@ -477,14 +784,14 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.num_blocks = cache->num_blocks;
-  a.col_tiles = tiles;
+  a.col_tiles = plan.tiles;
   a.parts = P;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->dtype == PA_F16)
-    launch_chunk<F16>(a, grid, merge_grid, cache->head_dim, s);
+    launch_chunk<F16>(a, plan, groups8, cache->head_dim, s);
   else
-    launch_chunk<BF16>(a, grid, merge_grid, cache->head_dim, s);
+    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, s);
   return pa::launch_status(fn);
 }
 

@@ -103,6 +103,36 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 -- the four lanes that hold one
+// column of a 16x16 matrix-core tile -- with gfx950's lane swaps, which stay in
+// the vector ALU.  v_permlane16_swap_b32 a, b exchanges the odd 16-lane rows of a
+// with the even rows of b; v_permlane32_swap_b32 a, b the upper half of a with
+// the lower half of b.  Applied to two copies of x, each leaves x and its partner
+// (x[l ^ 16], resp. x[l ^ 32]) in the pair, in every lane.  Written as inline
+// assembly with both registers as outputs, since the builtins' second result is
+// not kept apart from the first by the compiler; the s_nop gives the wait states
+// the compiler itself puts before these instructions.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float col_max4(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  a = b = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+  swap32(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  a = b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+  swap32(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
 // ---- 8-bit floating point (OCP E4M3) cache codes -----------------------------------
 // Code of x / scale: the division in float32, round to nearest even, saturated at
 // +-448 (the hardware conversion turns larger magnitudes into NaN, so they are

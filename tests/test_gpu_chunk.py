@@ -160,3 +160,38 @@ def test_block_placement_does_not_change_the_bits():
         outs.append(out.clone())
         del cache, batch
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_wide_kernel_with_key_partitions():
+    """At least 128 columns per (sequence, KV head) take the wide kernel; with few
+    sequences it splits the keys into 1024-token partitions and merges them."""
+    from paged_kv_cache_385_amd import chunk_workspace_size
+    ctx = [3000, 2500]
+    q_lens = [64, 20]
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=41)
+    ws = chunk_workspace_size(2, 16, 2, 128, sum(q_lens), max(q_lens), wl.max_context_len)
+    say(f"wide kernel, key partitions: workspace {ws} bytes")
+    assert ws > 0
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label="wide, partitioned")
+
+
+def test_wide_kernel_bad_lengths_and_empty_chunks():
+    ctx = [40, 50, 60]
+    q_lens = [40, 0, 50]
+    wl = custom_workload(ctx, 16, 2, 64, dtype="f16", seed=6)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    from paged_kv_cache_385_amd import chunk_attention
+    q = wl.chunk_q(q_lens).cuda()
+    starts = torch.from_numpy(_starts(q_lens)).cuda()
+    bad_ctx = ctx_d.clone()
+    bad_ctx[2] = 61
+    out = torch.zeros_like(q)
+    chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, bad_ctx, max(q_lens), 60,
+                    wl.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[q_lens[0]:]).all()
+    ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), [0])
+    check_close(out, ref, wl.dtype, rows=np.arange(0, q_lens[0]), label="wide, good sequence")
