@@ -65,6 +65,9 @@ def parse():
                     help="measure prefix-cached admission: 64 requests sharing a 2000-token system "
                          "prompt (host block manager + K/V store + pa_chunk_attention), with the "
                          "same step without prefix caching beside it")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swapping every sequence of the 70B-shaped decode batch out to "
+                         "pinned host memory and back (pa_bm_swap_* + pa_swap_blocks)")
     ap.add_argument("--chunk", choices=("verify", "prefill"),
                     help="measure pa_chunk_attention instead of the decode step: 'verify' = the "
                          "70B-shaped batch with 6 new tokens per sequence (HBM-bound), 'prefill' = "
@@ -490,8 +493,100 @@ def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
                       f"float64 attention of their new tokens, {t_total:.1f} s"}
 
 
+HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16, one direction, theoretical
+
+
+def run_swap(args):
+    """Swap-out then swap-in of every sequence of a decode batch per step: host block
+    manager calls, the pairs' upload and one pa_swap_blocks launch per direction."""
+    import torch
+    from workloads import make_workload
+    import paged_kv_cache_385_amd as pa
+    from paged_kv_cache_385_amd import _native
+    assert torch.cuda.is_available(), "no HIP device"
+    _native.lib()
+    dev = torch.device("cuda:0")
+    K, W = args.steps, args.warmup
+    wl = make_workload(args.workload)
+    B, Hkv, D = wl.num_seqs, wl.num_kv_heads, wl.head_dim
+    log(f"swap: workload {wl.cfg_id} ({wl.name}), {B} sequences, pool {wl.num_blocks} blocks")
+    t0 = time.perf_counter()
+    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order,
+                            host_blocks=wl.num_blocks)
+    segs = {}
+
+    def tokens(seg, start, n):
+        if seg not in segs:
+            segs[seg] = wl.segment_kv(seg)
+        k, v = segs[seg]
+        return k[start:start + n].contiguous(), v[start:start + n].contiguous()
+
+    cache.apply_trace(wl.setup, tokens)
+    segs.clear()
+    sids = [op[1] for op in wl.step]
+    torch.cuda.synchronize()
+    log(f"set-up {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream(dev)
+    block_bytes = 2 * Hkv * 16 * D * 2
+    ev = []
+    n_out = n_in = 0
+    for it in range(K + W):
+        if it == W:
+            torch.cuda.synchronize()
+            t_wall = time.perf_counter()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        po = cache.bm.swap_out(sids)                 # host: the pairs to copy
+        po_d = torch.from_numpy(po).to(dev)
+        e[0].record(stream)
+        pa.ops.swap_blocks(cache.k_cache, cache.v_cache, cache.k_host, cache.v_host,
+                           _native.PA_SWAP_OUT, po_d, pairs_host=po)
+        e[1].record(stream)
+        pi = cache.bm.swap_in(sids)
+        pi_d = torch.from_numpy(pi).to(dev)
+        e[2].record(stream)
+        pa.ops.swap_blocks(cache.k_cache, cache.v_cache, cache.k_host, cache.v_host,
+                           _native.PA_SWAP_IN, pi_d, pairs_host=pi)
+        e[3].record(stream)
+        if it >= W:
+            ev.append(e)
+            n_out, n_in = len(po), len(pi)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    out_us = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev])) * 1e3
+    in_us = float(np.mean([c.elapsed_time(d) for _, _, c, d in ev])) * 1e3
+    out_gbs = n_out * block_bytes / (out_us * 1e-6) / 1e9
+    in_gbs = n_in * block_bytes / (in_us * 1e-6) / 1e9
+    total = (n_out + n_in) * block_bytes
+    value = total / (wall / K) / 1e9
+    log(f"{K} round trips: {n_out} blocks out, {n_in} in ({n_out * block_bytes / 1e6:.1f} MB each "
+        f"way); out {out_us:.0f} us ({out_gbs:.1f} GB/s), in {in_us:.0f} us ({in_gbs:.1f} GB/s), "
+        f"wall {wall * 1e3 / K:.2f} ms per round trip")
+    result = {"metric": "KV swap GB/s over the host link (out + in, whole round trip)",
+              "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+              "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": wl.dtype_name, "data": "synthetic",
+              "config": {"workload": f"swap of every sequence of the {wl.name}", "batch": B,
+                         "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
+                         "kv_dtype": wl.dtype_name, "blocks_each_way": n_out,
+                         "block_bytes": block_bytes},
+              "out_gbs": round(out_gbs, 2), "in_gbs": round(in_gbs, 2),
+              "roofline": {"bound": "host-link", "achieved": round(max(out_gbs, in_gbs), 2),
+                           "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(max(out_gbs, in_gbs) / HOST_LINK_PEAK_GBS, 4),
+                           "traffic": None, "kernel": "block_copy_kernel",
+                           "avg_launch_us": round((out_us + in_us) / 2, 2),
+                           "bytes_per_launch": n_out * block_bytes}}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.swap:
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+            sys.exit(2)
+        run_swap(args)
+        return
     if args.prefix:
         if args.gpus != 1:
             print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)

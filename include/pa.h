@@ -393,6 +393,69 @@ pa_status pa_bm_evictable_list(const pa_bm* bm, int32_t* out, int32_t cap, int32
 pa_status pa_bm_cached_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
 /* ---------------------------------------------------------------------------
+ * Swapping between the device pool and a host tier (host only; the copies are
+ * pa_swap_blocks).  Blocks that do not fit in GPU memory spill to CPU memory and
+ * come back when needed ("vLLM 核心概念", section 内存层次结构); preemption is the
+ * fallback when resources run short ("理解 vLLM PagedAttention", section 五).
+ * Policies the pages leave open:
+ *   - the host tier is a pool of num_host_blocks blocks of the device pool's
+ *     shape, with a LIFO free stack starting as host_free_order (NULL = 0, 1, ..)
+ *     and its own reference counts;
+ *   - pa_bm_swap_out moves the n listed resident sequences to the host tier at
+ *     once: each distinct device block they reference (order of first
+ *     appearance: list order, then logical order) gets one host block, so blocks
+ *     they share stay shared; pairs[i] = (device block, host block) to copy
+ *     (pa_swap_blocks, PA_SWAP_OUT) before the released device blocks are
+ *     written again; then the sequences drop their device references, one after
+ *     the other, last logical block first; a block that a resident sequence
+ *     still references keeps its device copy;
+ *   - pa_bm_swap_in is the mirror image (device blocks taken as an append takes
+ *     them, so cached prefix blocks may be evicted; pairs = (host block, device
+ *     block), to copy with PA_SWAP_IN before the sequences are read);
+ *   - both are all or nothing (PA_ERR_OUT_OF_BLOCKS when the target tier lacks
+ *     blocks); pair_cap must hold the distinct blocks (the listed sequences'
+ *     table lengths summed always suffice), else PA_ERR_INVALID_ARG;
+ *   - a swapped-out sequence is not resident: growing, forking, committing or
+ *     packing it gives PA_ERR_NOT_FOUND; pa_bm_free_seq releases its host blocks
+ *     and pa_bm_seq_len still answers.
+ * ------------------------------------------------------------------------- */
+pa_status pa_bm_enable_swap(pa_bm* bm, int32_t num_host_blocks, const int32_t* host_free_order);
+pa_status pa_bm_swap_out(pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* pairs,
+                         int32_t pair_cap, int32_t* n_pairs);
+pa_status pa_bm_swap_in(pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* pairs,
+                        int32_t pair_cap, int32_t* n_pairs);
+/* *out = 1 when the sequence is swapped out, 0 when resident. */
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* out);
+/* A swapped-out sequence's host blocks, in logical order; *n = how many. */
+pa_status pa_bm_host_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap, int32_t* n);
+pa_status pa_bm_host_refcount(const pa_bm* bm, int32_t block, int32_t* out);
+/* Free host blocks, next-to-pop first. */
+pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+/* ---------------------------------------------------------------------------
+ * pa_swap_blocks -- block copies between the device pools and host pools.
+ * Defined by: KV blocks move between GPU memory and CPU memory ("vLLM 核心概念",
+ * section 内存层次结构).  `host` describes pools of the device pools' layout,
+ * dtype, head count, head size and FP8 scales, whose k_cache / v_cache are
+ * pinned host memory mapped for the device (as hipHostMalloc returns); its
+ * num_blocks is the host pool's size.  For every pair the whole K and V block
+ * (all heads, 16 positions) is copied: PA_SWAP_OUT copies device block
+ * pairs[i][0] to host block pairs[i][1], PA_SWAP_IN host block pairs[i][0] to
+ * device block pairs[i][1].  One kernel moves every pair over the host link.
+ *   pairs       int32[num_pairs][2], device-readable (device or mapped memory).
+ *   pairs_host  optional host copy, checked as in pa_copy_blocks (ids in range
+ *               of their pools, destinations distinct); without it
+ *               out-of-range pairs are skipped on the device.
+ * Errors: PA_ERR_INVALID_ARG (layouts differ, bad direction or pairs),
+ * PA_ERR_UNSUPPORTED (more than 65535 pairs), PA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+#define PA_SWAP_OUT 0
+#define PA_SWAP_IN 1
+pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t direction,
+                         const int32_t* pairs, const int32_t* pairs_host, int32_t num_pairs,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * pa_chunk_attention -- several new tokens per sequence: the last q_len_b of
  * sequence b's context_lens[b] cached tokens are queries, and query i (position
  * context_lens[b] - q_len_b + i) attends over cached positions 0 .. its own.

@@ -22,6 +22,8 @@ PA_F16 = 0
 PA_BF16 = 1
 PA_CACHE_SHARED_BLOCKS = 1
 PA_CACHE_FP8 = 2
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
 
@@ -104,6 +106,14 @@ SIGNATURES = {
     "pa_bm_prefix_stats_get": (C.c_int, [_P, C.POINTER(PaBmPrefixStats)]),
     "pa_bm_evictable_list": (C.c_int, [_P, _P, _I32, _PI32]),
     "pa_bm_cached_list": (C.c_int, [_P, _P, _I32, _PI32]),
+    "pa_bm_enable_swap": (C.c_int, [_P, _I32, _P]),
+    "pa_bm_swap_out": (C.c_int, [_P, _I32, _P, _P, _I32, _PI32]),
+    "pa_bm_swap_in": (C.c_int, [_P, _I32, _P, _P, _I32, _PI32]),
+    "pa_bm_is_swapped": (C.c_int, [_P, _I64, _PI32]),
+    "pa_bm_host_table": (C.c_int, [_P, _I64, _P, _I32, _PI32]),
+    "pa_bm_host_refcount": (C.c_int, [_P, _I32, _PI32]),
+    "pa_bm_host_free_list": (C.c_int, [_P, _P, _I32, _PI32]),
+    "pa_swap_blocks": (C.c_int, [C.POINTER(PaCache), C.POINTER(PaCache), _I32, _P, _P, _I32, _P]),
     "pa_chunk_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_chunk_attention": (C.c_int, [C.POINTER(PaCache), _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
                                      _P, _I32, C.c_float, _P, _P, C.c_size_t, _P]),

@@ -213,3 +213,64 @@ class BlockManager:
     def cached_blocks(self) -> List[int]:
         """Blocks in the prefix index, ascending."""
         return self._block_list("pa_bm_cached_list")
+
+    # -- swapping to a host tier -------------------------------------------------------
+    def enable_swap(self, num_host_blocks: int, host_free_order: Optional[Sequence[int]] = None) -> None:
+        order = None
+        if host_free_order is not None:
+            order = np.ascontiguousarray(np.asarray(host_free_order, dtype=np.int32))
+        N.check(self._lib.pa_bm_enable_swap(self._h, num_host_blocks,
+                                            None if order is None else _ptr(order)),
+                "pa_bm_enable_swap")
+        self.num_host_blocks = num_host_blocks
+
+    def _swap(self, fn: str, sids: Sequence[int]) -> np.ndarray:
+        ids = np.ascontiguousarray(np.asarray(list(sids), dtype=np.int64))
+        cap = 0
+        for sid in ids.tolist():                       # table lengths bound the distinct blocks
+            cap += self.seq_blocks(sid)
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
+        n = C.c_int32()
+        N.check(getattr(self._lib, fn)(self._h, ids.shape[0], _ptr(ids), _ptr(pairs), max(cap, 1),
+                                       C.byref(n)), fn)
+        return pairs[:n.value]
+
+    def swap_out(self, sids: Sequence[int]) -> np.ndarray:
+        """(device block, host block) pairs to copy out, int32 [k, 2]."""
+        return self._swap("pa_bm_swap_out", sids)
+
+    def swap_in(self, sids: Sequence[int]) -> np.ndarray:
+        """(host block, device block) pairs to copy in, int32 [k, 2]."""
+        return self._swap("pa_bm_swap_in", sids)
+
+    def is_swapped(self, sid: int) -> bool:
+        r = C.c_int32()
+        N.check(self._lib.pa_bm_is_swapped(self._h, sid, C.byref(r)), "pa_bm_is_swapped")
+        return bool(r.value)
+
+    def seq_blocks(self, sid: int) -> int:
+        """Blocks a sequence holds in its current tier (0 for an unknown sequence)."""
+        n = C.c_int64()
+        if self._lib.pa_bm_seq_len(self._h, sid, C.byref(n)) != N.PA_OK:
+            return 0
+        return -(-n.value // self.block_size)
+
+    def host_table(self, sid: int) -> List[int]:
+        n = C.c_int32()
+        N.check(self._lib.pa_bm_host_table(self._h, sid, None, 0, C.byref(n)), "pa_bm_host_table")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        N.check(self._lib.pa_bm_host_table(self._h, sid, _ptr(out), n.value, C.byref(n)),
+                "pa_bm_host_table")
+        return out[:n.value].tolist()
+
+    def host_refcount(self, blk: int) -> int:
+        r = C.c_int32()
+        N.check(self._lib.pa_bm_host_refcount(self._h, blk, C.byref(r)), "pa_bm_host_refcount")
+        return r.value
+
+    def host_free_list(self) -> List[int]:
+        n = C.c_int32()
+        out = np.empty(max(getattr(self, "num_host_blocks", 0), 1), dtype=np.int32)
+        N.check(self._lib.pa_bm_host_free_list(self._h, _ptr(out), out.shape[0], C.byref(n)),
+                "pa_bm_host_free_list")
+        return out[:n.value].tolist()

@@ -102,6 +102,13 @@ struct pa_bm {
   int64_t n_evictable = 0, n_indexed = 0;
   int64_t requests = 0, query_blocks = 0, hit_blocks = 0, evictions = 0;
 
+  // host tier for swapping (off until pa_bm_enable_swap)
+  int32_t num_host = 0;
+  std::vector<int32_t> host_free;   // top = back()
+  std::vector<int32_t> host_ref;
+  std::unordered_map<int64_t, Seq> swapped;   // tables hold host blocks
+  std::vector<int32_t> map_scratch;           // per-call block map, -1 when unused
+
   int64_t available() const { return static_cast<int64_t>(free_stack.size()) + n_evictable; }
 
   void lru_unlink(int32_t b) {
@@ -331,7 +338,8 @@ void pa_bm_destroy(pa_bm* bm) { delete bm; }
 
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: bm is NULL");
-  if (bm->find(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
+  if (bm->find(seq_id) || bm->swapped.count(seq_id))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
   bm->seqs.emplace(seq_id, Seq{});
   return PA_OK;
 }
@@ -441,8 +449,9 @@ pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t count, int64_t*
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: bm is NULL");
   const Seq* p = bm->find(parent);
-  if (!p) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_fork: no sequence %lld", (long long)parent);
-  if (bm->find(child)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: sequence %lld exists", (long long)child);
+  if (!p) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_fork: no resident sequence %lld", (long long)parent);
+  if (bm->find(child) || bm->swapped.count(child))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: sequence %lld exists", (long long)child);
   Seq c = *p;
   for (int32_t b : c.table) bm->ref_inc(b);
   bm->pin(c.node);
@@ -452,6 +461,15 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
 
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: bm is NULL");
+  auto sw = bm->swapped.find(seq_id);
+  if (sw != bm->swapped.end()) {            // a swapped-out sequence holds host blocks
+    const std::vector<int32_t>& t = sw->second.table;
+    for (auto r = t.rbegin(); r != t.rend(); ++r)
+      if (--bm->host_ref[*r] == 0) bm->host_free.push_back(*r);
+    bm->unpin(sw->second.node);
+    bm->swapped.erase(sw);
+    return PA_OK;
+  }
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_free_seq: no sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& t = it->second.table;
@@ -466,6 +484,10 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
 pa_status pa_bm_seq_len(const pa_bm* bm, int64_t seq_id, int64_t* len) {
   if (!bm || !len) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_seq_len: NULL argument");
   const Seq* s = bm->find(seq_id);
+  if (!s) {
+    auto sw = bm->swapped.find(seq_id);
+    if (sw != bm->swapped.end()) s = &sw->second;
+  }
   if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_seq_len: no sequence %lld", (long long)seq_id);
   *len = s->len;
   return PA_OK;
@@ -613,7 +635,7 @@ pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, int64_t tenant, const 
   *cached_tokens = 0;
   if (!bm->prefix_on)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_add_seq_cached: prefix caching is off");
-  if (bm->find(seq_id))
+  if (bm->find(seq_id) || bm->swapped.count(seq_id))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: sequence %lld exists", (long long)seq_id);
   *cached_tokens = bm->add_cached(seq_id, tenant, tokens, n);
   return PA_OK;
@@ -636,7 +658,7 @@ pa_status pa_bm_admit_batch(pa_bm* bm, int32_t n, const int64_t* seq_ids, const 
       return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: prompt %d has %lld tokens", i, (long long)len);
     if (tenants && (tenants[i] < 0 || tenants[i] == INT64_MAX))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: tenant %lld", (long long)tenants[i]);
-    if (bm->find(seq_ids[i]))
+    if (bm->find(seq_ids[i]) || bm->swapped.count(seq_ids[i]))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_admit_batch: sequence %lld exists", (long long)seq_ids[i]);
   }
   if (slot_cap < offsets[n] - offsets[0])
@@ -755,6 +777,220 @@ pa_status pa_bm_cached_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t*
         ++k;
       }
   *n = k;
+  return PA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Swapping between the device pool and a host tier
+// ---------------------------------------------------------------------------
+namespace {
+
+// Distinct blocks of the tables, in order of first appearance; map[b] receives
+// its position.  Returns the count.
+int32_t distinct_blocks(const std::vector<const std::vector<int32_t>*>& tables,
+                        std::vector<int32_t>& map, std::vector<int32_t>& order) {
+  order.clear();
+  for (const auto* t : tables)
+    for (int32_t b : *t)
+      if (map[b] < 0) {
+        map[b] = static_cast<int32_t>(order.size());
+        order.push_back(b);
+      }
+  return static_cast<int32_t>(order.size());
+}
+
+pa_status check_list(int32_t n, const int64_t* ids, const char* fn) {
+  std::vector<int64_t> v(ids, ids + n);
+  std::sort(v.begin(), v.end());
+  if (std::adjacent_find(v.begin(), v.end()) != v.end())
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: a sequence appears twice", fn);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_bm_enable_swap(pa_bm* bm, int32_t num_host_blocks, const int32_t* host_free_order) {
+  if (!bm || num_host_blocks <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_swap: bad arguments");
+  if (bm->num_host > 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_swap: already on");
+  std::vector<int32_t> stack(num_host_blocks);
+  if (host_free_order) {
+    std::vector<char> seen(num_host_blocks, 0);
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = host_free_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[b])
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_swap: host_free_order is not a permutation");
+      seen[b] = 1;
+      stack[num_host_blocks - 1 - i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_host_blocks; ++i) stack[num_host_blocks - 1 - i] = i;
+  }
+  bm->num_host = num_host_blocks;
+  bm->host_free = std::move(stack);
+  bm->host_ref.assign(num_host_blocks, 0);
+  bm->map_scratch.assign(std::max(bm->num_blocks, num_host_blocks), -1);
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* pairs,
+                         int32_t pair_cap, int32_t* n_pairs) {
+  const char* fn = "pa_bm_swap_out";
+  if (!bm || n < 0 || !n_pairs || (n > 0 && (!seq_ids || !pairs)))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+  *n_pairs = 0;
+  if (bm->num_host == 0) return pa::fail(PA_ERR_UNSUPPORTED, "%s: swapping is off", fn);
+  if (n == 0) return PA_OK;
+  pa_status st = check_list(n, seq_ids, fn);
+  if (st != PA_OK) return st;
+  std::vector<Seq*> ptr(n);
+  std::vector<const std::vector<int32_t>*> tables(n);
+  for (int32_t i = 0; i < n; ++i) {
+    ptr[i] = bm->find(seq_ids[i]);
+    if (!ptr[i]) return pa::fail(PA_ERR_NOT_FOUND, "%s: no resident sequence %lld", fn, (long long)seq_ids[i]);
+    tables[i] = &ptr[i]->table;
+  }
+  std::vector<int32_t>& map = bm->map_scratch;
+  std::vector<int32_t> order;
+  const int32_t k = distinct_blocks(tables, map, order);
+  auto reset = [&] { for (int32_t b : order) map[b] = -1; };
+  if (k > pair_cap) {
+    reset();
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: %d pairs, pair_cap %d", fn, k, pair_cap);
+  }
+  if (k > static_cast<int32_t>(bm->host_free.size())) {
+    reset();
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "%s: needs %d host blocks, %zu free", fn, k,
+                    bm->host_free.size());
+  }
+  std::vector<int32_t> host_of(k);
+  for (int32_t i = 0; i < k; ++i) {
+    host_of[i] = bm->host_free.back();
+    bm->host_free.pop_back();
+    pairs[2 * i] = order[i];
+    pairs[2 * i + 1] = host_of[i];
+  }
+  std::vector<std::vector<int32_t>> dev_tables(n);
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = *ptr[i];
+    dev_tables[i] = s.table;
+    for (int32_t& b : s.table) {
+      b = host_of[map[b]];
+      ++bm->host_ref[b];
+    }
+    bm->swapped.emplace(seq_ids[i], std::move(s));
+    bm->seqs.erase(seq_ids[i]);
+  }
+  reset();
+  // the listed sequences drop their device references, last logical block first
+  for (int32_t i = 0; i < n; ++i)
+    for (auto r = dev_tables[i].rbegin(); r != dev_tables[i].rend(); ++r)
+      if (bm->ref_dec(*r) == 0) bm->release(*r);
+  *n_pairs = k;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t* pairs,
+                        int32_t pair_cap, int32_t* n_pairs) {
+  const char* fn = "pa_bm_swap_in";
+  if (!bm || n < 0 || !n_pairs || (n > 0 && (!seq_ids || !pairs)))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+  *n_pairs = 0;
+  if (bm->num_host == 0) return pa::fail(PA_ERR_UNSUPPORTED, "%s: swapping is off", fn);
+  if (n == 0) return PA_OK;
+  pa_status st = check_list(n, seq_ids, fn);
+  if (st != PA_OK) return st;
+  std::vector<Seq*> ptr(n);
+  std::vector<const std::vector<int32_t>*> tables(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->swapped.find(seq_ids[i]);
+    if (it == bm->swapped.end())
+      return pa::fail(PA_ERR_NOT_FOUND, "%s: no swapped-out sequence %lld", fn, (long long)seq_ids[i]);
+    ptr[i] = &it->second;
+    tables[i] = &ptr[i]->table;
+  }
+  std::vector<int32_t>& map = bm->map_scratch;
+  std::vector<int32_t> order;
+  const int32_t k = distinct_blocks(tables, map, order);
+  auto reset = [&] { for (int32_t b : order) map[b] = -1; };
+  if (k > pair_cap) {
+    reset();
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: %d pairs, pair_cap %d", fn, k, pair_cap);
+  }
+  if (k > bm->available()) {
+    reset();
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "%s: needs %d blocks, %lld available", fn, k,
+                    (long long)bm->available());
+  }
+  std::vector<int32_t> dev_of(k);
+  for (int32_t i = 0; i < k; ++i) {
+    dev_of[i] = bm->pop_free();
+    bm->ref[dev_of[i]] = 0;            // counted again per reference below
+    pairs[2 * i] = order[i];
+    pairs[2 * i + 1] = dev_of[i];
+  }
+  std::vector<std::vector<int32_t>> host_tables(n);
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = *ptr[i];
+    host_tables[i] = s.table;
+    for (int32_t& b : s.table) {
+      b = dev_of[map[b]];
+      bm->ref_inc(b);
+    }
+    bm->seqs.emplace(seq_ids[i], std::move(s));
+    bm->swapped.erase(seq_ids[i]);
+  }
+  reset();
+  for (int32_t i = 0; i < n; ++i)
+    for (auto r = host_tables[i].rbegin(); r != host_tables[i].rend(); ++r)
+      if (--bm->host_ref[*r] == 0) bm->host_free.push_back(*r);
+  *n_pairs = k;
+  return PA_OK;
+}
+
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_is_swapped: NULL argument");
+  if (bm->swapped.count(seq_id)) {
+    *out = 1;
+  } else if (bm->find(seq_id)) {
+    *out = 0;
+  } else {
+    return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_is_swapped: no sequence %lld", (long long)seq_id);
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_host_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_host_table: bad arguments");
+  auto it = bm->swapped.find(seq_id);
+  if (it == bm->swapped.end())
+    return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_host_table: no swapped-out sequence %lld", (long long)seq_id);
+  const std::vector<int32_t>& t = it->second.table;
+  const int32_t m = static_cast<int32_t>(t.size());
+  std::memcpy(out, t.data(), sizeof(int32_t) * std::min(m, cap));
+  *n = m;
+  return PA_OK;
+}
+
+pa_status pa_bm_host_refcount(const pa_bm* bm, int32_t block, int32_t* out) {
+  if (!bm || !out || block < 0 || block >= bm->num_host)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_host_refcount: bad arguments");
+  *out = bm->host_ref[block];
+  return PA_OK;
+}
+
+pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_host_free_list: bad arguments");
+  const int32_t m = static_cast<int32_t>(bm->host_free.size());
+  const int32_t k = std::min(m, cap);
+  for (int32_t i = 0; i < k; ++i) out[i] = bm->host_free[m - 1 - i];
+  *n = m;
   return PA_OK;
 }
 

@@ -2,7 +2,9 @@
 //
 //   cache_write_kernel   slot-mapped store of new tokens' K/V ("vLLM 核心概念",
 //                        sections "为什么需要 KV Cache？" and "按需分配")
-//   copy_blocks_kernel   copy-on-write block copy ("理解 vLLM PagedAttention", section 六)
+//   block_copy_kernel    whole-block copies: copy-on-write ("理解 vLLM PagedAttention",
+//                        section 六) and swapping to and from host pools ("vLLM 核心概念",
+//                        section 内存层次结构)
 //   decode_attn_kernel   single-query attention over a block-paged context
 //                        ("PagedAttention 实战", section "Decode：逐 token 生成输出";
 //                        "vLLM 核心概念", section "逻辑视图与物理视图分离")
@@ -123,16 +125,19 @@ __global__ __launch_bounds__(256) void cache_write8_kernel(
 
 // ---- block copy ------------------------------------------------------------------
 // grid.y = pair, grid.x strides over the 16-byte vectors of one block in both pools.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(
-    const int32_t* __restrict__ pairs, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
-    int64_t vecs_per_block, int32_t num_blocks) {
+// Whole-block copies from one pool pair to another (the same pools for
+// copy-on-write, device and host pools for swapping): workgroup column y copies
+// pair y, 16 bytes of K and of V per thread per step.
+__global__ __launch_bounds__(256) void block_copy_kernel(
+    const int32_t* __restrict__ pairs, const u32x4* src_k, const u32x4* src_v, u32x4* dst_k,
+    u32x4* dst_v, int64_t vecs_per_block, int32_t src_blocks, int32_t dst_blocks) {
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const u32x4* ks = k_cache + src * vecs_per_block;
-  const u32x4* vs = v_cache + src * vecs_per_block;
-  u32x4* kd = k_cache + dst * vecs_per_block;
-  u32x4* vd = v_cache + dst * vecs_per_block;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4* ks = src_k + src * vecs_per_block;
+  const u32x4* vs = src_v + src * vecs_per_block;
+  u32x4* kd = dst_k + dst * vecs_per_block;
+  u32x4* vd = dst_v + dst * vecs_per_block;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs_per_block;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const u32x4 a = ks[i];
@@ -1174,10 +1179,51 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, const int3
   const int64_t elem = (cache->flags & PA_CACHE_FP8) ? 1 : 2;
   const int64_t vecs = static_cast<int64_t>(cache->num_kv_heads) * kBlock * cache->head_dim * elem / 16;
   const int64_t gx = std::min<int64_t>((vecs + 255) / 256, 64);
-  copy_blocks_kernel<<<dim3(gx, num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      pairs, static_cast<u32x4*>(cache->k_cache), static_cast<u32x4*>(cache->v_cache), vecs,
-      cache->num_blocks);
+  block_copy_kernel<<<dim3(gx, num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      pairs, static_cast<const u32x4*>(cache->k_cache), static_cast<const u32x4*>(cache->v_cache),
+      static_cast<u32x4*>(cache->k_cache), static_cast<u32x4*>(cache->v_cache), vecs,
+      cache->num_blocks, cache->num_blocks);
   return launch_status("pa_copy_blocks");
+}
+
+pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t direction,
+                         const int32_t* pairs, const int32_t* pairs_host, int32_t num_pairs,
+                         void* stream) {
+  const char* fn = "pa_swap_blocks";
+  pa::clear_error();
+  pa_status st = check_cache(device, fn);
+  if (st != PA_OK) return st;
+  st = check_cache(host, fn);
+  if (st != PA_OK) return st;
+  if (device->num_kv_heads != host->num_kv_heads || device->head_dim != host->head_dim ||
+      device->dtype != host->dtype || ((device->flags ^ host->flags) & PA_CACHE_FP8))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: device and host pools differ in layout", fn);
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: direction %d", fn, direction);
+  if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_pairs %d", fn, num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return pa::fail(PA_ERR_INVALID_ARG, "%s: pairs is NULL", fn);
+  if (num_pairs > 65535) return pa::fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 pairs", fn);
+  const pa_cache* src = direction == PA_SWAP_OUT ? device : host;
+  const pa_cache* dst = direction == PA_SWAP_OUT ? host : device;
+  if (pairs_host) {
+    std::vector<uint8_t> taken(dst->num_blocks, 0);
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t s = pairs_host[2 * i], d = pairs_host[2 * i + 1];
+      if (s < 0 || s >= src->num_blocks || d < 0 || d >= dst->num_blocks)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: pair %d (%d, %d) out of range", fn, i, s, d);
+      if (taken[d]) return pa::fail(PA_ERR_INVALID_ARG, "%s: destination %d repeated", fn, d);
+      taken[d] = 1;
+    }
+  }
+  const int64_t elem = (device->flags & PA_CACHE_FP8) ? 1 : 2;
+  const int64_t vecs = static_cast<int64_t>(device->num_kv_heads) * kBlock * device->head_dim * elem / 16;
+  const int64_t gx = std::min<int64_t>((vecs + 255) / 256, 64);
+  block_copy_kernel<<<dim3(gx, num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      pairs, static_cast<const u32x4*>(src->k_cache), static_cast<const u32x4*>(src->v_cache),
+      static_cast<u32x4*>(dst->k_cache), static_cast<u32x4*>(dst->v_cache), vecs, src->num_blocks,
+      dst->num_blocks);
+  return launch_status(fn);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

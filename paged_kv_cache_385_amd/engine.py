@@ -45,11 +45,14 @@ class PagedKVCache:
     ``kv_scales`` = (k_scales, v_scales) -- one positive float per KV head each -- the
     pools hold 8-bit E4M3 codes of x / scale instead (``PA_CACHE_FP8``).  With
     ``prefix_caching`` the block manager indexes committed full blocks and ``admit``
-    reuses them for requests whose prompts share a prefix."""
+    reuses them for requests whose prompts share a prefix.  With ``host_blocks`` > 0 a
+    host tier of that many blocks (pinned host pools of the same layout) takes
+    swapped-out sequences (``swap_out`` / ``swap_in``)."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  device="cuda", free_order: Optional[Sequence[int]] = None,
-                 fill_bits: Optional[int] = None, kv_scales=None, prefix_caching: bool = False):
+                 fill_bits: Optional[int] = None, kv_scales=None, prefix_caching: bool = False,
+                 host_blocks: int = 0):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -63,6 +66,14 @@ class PagedKVCache:
         self.k_cache, self.v_cache = ops.alloc_pool(num_blocks, num_kv_heads, head_dim, dtype,
                                                     self.device, fill_bits, fp8=self.fp8)
         self.bm = BlockManager(num_blocks, N.BLOCK_SIZE, free_order, prefix_caching)
+        self.k_host = self.v_host = None
+        if host_blocks > 0:
+            shp = (ops.k8_pool_shape if self.fp8 else ops.k_pool_shape)(host_blocks, num_kv_heads, head_dim)
+            vshp = (ops.v8_pool_shape if self.fp8 else ops.v_pool_shape)(host_blocks, num_kv_heads, head_dim)
+            pdt = torch.uint8 if self.fp8 else dtype
+            self.k_host = torch.zeros(shp, dtype=pdt, pin_memory=True)
+            self.v_host = torch.zeros(vshp, dtype=pdt, pin_memory=True)
+            self.bm.enable_swap(host_blocks)
 
     def descriptor(self, shared_blocks: bool = False) -> N.PaCache:
         return ops.cache_desc(self.k_cache, self.v_cache, shared_blocks, scales=self.scales,
@@ -134,6 +145,25 @@ class PagedKVCache:
         self.write(k, v, slots)
         self.bm.commit_tokens(sid, list(prompt)[cached:])
         return cached
+
+    # ---- swapping ----------------------------------------------------------------------
+    def _swap(self, pairs: np.ndarray, direction: int) -> np.ndarray:
+        if len(pairs):
+            ops.swap_blocks(self.k_cache, self.v_cache, self.k_host, self.v_host, direction,
+                            torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device),
+                            pairs_host=pairs, scales=self.scales)
+        return pairs
+
+    def swap_out(self, sids: Sequence[int]) -> np.ndarray:
+        """Move the sequences' blocks to the host tier; the copies are enqueued on the
+        current stream before anything later can reuse the released device blocks.
+        Returns the (device, host) pairs."""
+        return self._swap(self.bm.swap_out(sids), N.PA_SWAP_OUT)
+
+    def swap_in(self, sids: Sequence[int]) -> np.ndarray:
+        """Bring swapped-out sequences back into fresh device blocks; returns the (host,
+        device) pairs."""
+        return self._swap(self.bm.swap_in(sids), N.PA_SWAP_IN)
 
     def tables(self, sids: Sequence[int], max_blocks: int) -> Tuple[torch.Tensor, torch.Tensor, int]:
         """Device block tables and context lengths for ``sids``, plus the host max context."""

@@ -64,13 +64,18 @@ def _stream_ptr(stream, device) -> C.c_void_p:
 
 def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, shared_blocks: bool = False,
                scales: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-               dtype: Optional[torch.dtype] = None) -> N.PaCache:
+               dtype: Optional[torch.dtype] = None, host: bool = False) -> N.PaCache:
     """Descriptor of a pool pair; ``shared_blocks``: blocks may be shared within one call.
 
     FP8 pools (uint8 tensors of E4M3 codes) need ``scales`` = (k_scales, v_scales),
     float32 [Hkv] device tensors, and ``dtype``, the float16/bfloat16 dtype of q, out
-    and of the k / v written into them."""
-    if not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
+    and of the k / v written into them.  ``host``: the pools are pinned host tensors
+    (a swap tier), read and written by the device over the host link."""
+    if host:
+        if not (k_cache.is_pinned() and v_cache.is_pinned() and k_cache.is_contiguous()
+                and v_cache.is_contiguous()):
+            raise ValueError("host pools must be contiguous pinned tensors")
+    elif not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("pools must be contiguous device tensors")
     shared = N.PA_CACHE_SHARED_BLOCKS if shared_blocks else 0
     if k_cache.dtype == torch.uint8:
@@ -84,7 +89,7 @@ def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, shared_blocks: bool
                              "do not match the layout")
         ks, vs = scales
         for t, name in ((ks, "k_scales"), (vs, "v_scales")):
-            _need(t, torch.float32, k_cache.device, name, (hkv,))
+            _need(t, torch.float32, ks.device if host else k_cache.device, name, (hkv,))
         return N.PaCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, D, _DT[dtype],
                          shared | N.PA_CACHE_FP8, ks.data_ptr(), vs.data_ptr())
     if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DT:
@@ -134,6 +139,26 @@ def copy_blocks(k_cache, v_cache, pairs, pairs_host: Optional[np.ndarray] = None
         host = C.c_void_p(pairs_host.ctypes.data)
     N.check(N.lib().pa_copy_blocks(C.byref(desc), pairs.data_ptr(), host, n,
                                    _stream_ptr(stream, k_cache.device)), "pa_copy_blocks")
+
+
+def swap_blocks(k_dev, v_dev, k_host, v_host, direction: int, pairs,
+                pairs_host: Optional[np.ndarray] = None, stream=None, scales=None) -> None:
+    """pa_swap_blocks: whole-block copies between device pools and pinned host pools of the
+    same layout; ``direction`` N.PA_SWAP_OUT (pairs (device, host)) or N.PA_SWAP_IN
+    (pairs (host, device)); ``pairs`` int32 [n, 2] on the device."""
+    dt = torch.bfloat16 if k_dev.dtype == torch.uint8 else None
+    dd = cache_desc(k_dev, v_dev, scales=scales, dtype=dt)
+    hd = cache_desc(k_host, v_host, scales=scales, dtype=dt, host=True)
+    n = pairs.shape[0]
+    _need(pairs, torch.int32, k_dev.device, "pairs", (n, 2))
+    host = None
+    if pairs_host is not None:
+        pairs_host = np.ascontiguousarray(pairs_host, dtype=np.int32)
+        if pairs_host.shape != (n, 2):
+            raise ValueError("pairs_host must match pairs")
+        host = C.c_void_p(pairs_host.ctypes.data)
+    N.check(N.lib().pa_swap_blocks(C.byref(dd), C.byref(hd), direction, pairs.data_ptr(), host, n,
+                                   _stream_ptr(stream, k_dev.device)), "pa_swap_blocks")
 
 
 def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:
