@@ -65,6 +65,9 @@ def parse():
                     help="measure prefix-cached admission: 64 requests sharing a 2000-token system "
                          "prompt (host block manager + K/V store + pa_chunk_attention), with the "
                          "same step without prefix caching beside it")
+    ap.add_argument("--block-size", type=int, choices=(16, 32), default=16,
+                    help="tokens per block of the block manager (32: each block is two "
+                         "16-token tiles of the pool; the kernels are the same)")
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping every sequence of the 70B-shaped decode batch out to "
                          "pinned host memory and back (pa_bm_swap_* + pa_swap_blocks)")
@@ -626,8 +629,12 @@ def main():
     # FP8 scales: the synthetic K/V are standard normal, so |x| / 0.0125 reaches the
     # E4M3 range (448) only past 5.6 sigma
     kv_scales = (np.full(Hkv, 0.0125, np.float32), np.full(Hkv, 0.0125, np.float32)) if fp8 else None
-    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order,
-                            kv_scales=kv_scales)
+    if args.block_size == 16:
+        cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order,
+                                kv_scales=kv_scales)
+    else:   # 32-token blocks waste up to 31 tokens per sequence: a larger pool of tile pairs
+        tiles = 2 * -(-int(1.25 * wl.num_blocks) // 2)
+        cache = pa.PagedKVCache(tiles, Hkv, D, wl.dtype, dev, kv_scales=kv_scales, block_size=32)
     segs = {}
 
     def tokens(seg, start, n):
@@ -639,7 +646,8 @@ def main():
     cache.apply_trace(wl.setup, tokens)
     segs.clear()
     sids = [op[1] for op in wl.step]
-    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W) // 16)
+    bsz = args.block_size
+    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W) // bsz) * (bsz // 16)   # in 16-token tiles
     batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, staging=args.staging)
     q = wl.q().to(dev)
     steps_kv = []
@@ -709,15 +717,16 @@ def main():
         "dtype": wl.dtype_name,
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": 16, "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype_name,
+                   "head_dim": D, "block_size": bsz, "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype_name,
                    "context": CONTEXT_TEXT[wl.cfg_id],
                    "mean_context": round(float(base_ctx.mean() + W + (K - 1) / 2), 1),
-                   "num_blocks": wl.num_blocks},
+                   "num_blocks": int(cache.num_blocks)},
+        "pool_waste": round(cache.bm.stats()["waste"], 4),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(B * K / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 else recorded_traffic(args.workload, K, W),
+                     "traffic": None if fp8 or bsz != 16 else recorded_traffic(args.workload, K, W),
                      "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}"
                                + (",FP8>" if fp8 else ">"),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),

@@ -262,6 +262,15 @@ const char* pa_last_error(void);
  *     takes a fresh block and reports (old, new) as a copy-on-write pair; the
  *     old block loses a reference; the last sharer writes in place;
  *   - a failing append or batch changes nothing.
+ * Block size ("vLLM 核心概念", section 块大小（Block Size）的选择: smaller blocks
+ * waste less memory, larger ones need fewer table entries): 16 or 32 tokens.  A
+ * 32-token manager block b is the pool's two 16-token blocks (tiles) 2 b and
+ * 2 b + 1, so the pool holds 2 * num_blocks tiles and the kernels are unchanged:
+ * slots keep their numbering (32 b + i is tile 2 b + i / 16, position i % 16);
+ * pa_bm_pack and pa_bm_step write tables in tiles (max_blocks counts tiles);
+ * copy-on-write pairs from the append calls are in manager blocks, a pair (s, d)
+ * meaning tile copies (2 s, 2 d) and (2 s + 1, 2 d + 1) (pa_decode_step expands
+ * them itself).  Prefix caching and swapping need 16-token blocks.
  * ======================================================================== */
 typedef struct pa_bm pa_bm;
 
@@ -513,7 +522,7 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  *      seq_ids[i]) and the decode, all on `stream`.
  * Staging layout (each part 256-byte aligned, both buffers 256-byte aligned and
  * at least pa_decode_step_staging_bytes() long): int64 slots[n] | int32 ctx[n] |
- * int32 tables[n][max_blocks_per_seq] | int32 pairs[n][2].  staging_host must
+ * int32 tables[n][max_blocks_per_seq] | int32 pairs[2 n][2] (tile pairs).  staging_host must
  * not be rewritten while an earlier copy from it may still be pending, nor
  * staging_dev while kernels of an earlier step may still read it (the caller
  * alternates two buffers of each and waits on events; with copy_stream, it

@@ -308,8 +308,8 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* fr
   if (!out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out is NULL");
   *out = nullptr;
   if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks %d", num_blocks);
-  if (block_size != PA_BLOCK_SIZE)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only 16)", block_size);
+  if (block_size != PA_BLOCK_SIZE && block_size != 2 * PA_BLOCK_SIZE)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (16 or 32)", block_size);
   pa_bm* bm = new (std::nothrow) pa_bm;
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
   bm->num_blocks = num_blocks;
@@ -509,20 +509,28 @@ pa_status pa_bm_pack(const pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t
                      int32_t max_blocks, int32_t* ctx_lens) {
   if (!bm || n < 0 || max_blocks <= 0 || (n > 0 && (!seq_ids || !tables || !ctx_lens)))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_pack: bad arguments");
+  // tables are written in the pool's 16-token tiles: block b of a 32-token manager
+  // is tiles 2 b and 2 b + 1
+  const int32_t f = bm->block_size / PA_BLOCK_SIZE;
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = bm->find(seq_ids[i]);
     if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_pack: no sequence %lld", (long long)seq_ids[i]);
-    const int32_t m = static_cast<int32_t>(s->table.size());
+    const int64_t m = static_cast<int64_t>(s->table.size()) * f;
     if (m > max_blocks || s->len > INT32_MAX)
-      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_pack: sequence %lld holds %d blocks > %d",
-                      (long long)seq_ids[i], m, max_blocks);
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_pack: sequence %lld holds %lld tiles > %d",
+                      (long long)seq_ids[i], (long long)m, max_blocks);
   }
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = bm->find(seq_ids[i]);
     int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
     const int32_t m = static_cast<int32_t>(s->table.size());
-    std::memcpy(row, s->table.data(), sizeof(int32_t) * m);
-    std::fill(row + m, row + max_blocks, -1);
+    if (f == 1) {
+      std::memcpy(row, s->table.data(), sizeof(int32_t) * m);
+    } else {
+      for (int32_t j = 0; j < m; ++j)
+        for (int32_t t = 0; t < f; ++t) row[j * f + t] = s->table[j] * f + t;
+    }
+    std::fill(row + m * f, row + max_blocks, -1);
     ctx_lens[i] = static_cast<int32_t>(s->len);
   }
   return PA_OK;
@@ -540,10 +548,11 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = bm->find(seq_ids[i]);
     if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_step: no sequence %lld", (long long)seq_ids[i]);
-    const int64_t blocks_after = (s->len + bm->block_size) / bm->block_size;
-    if (blocks_after > max_blocks || s->len + 1 > INT32_MAX)
-      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_step: sequence %lld needs %lld blocks > %d",
-                      (long long)seq_ids[i], (long long)blocks_after, max_blocks);
+    const int64_t tiles_after =
+        (s->len + bm->block_size) / bm->block_size * (bm->block_size / PA_BLOCK_SIZE);
+    if (tiles_after > max_blocks || s->len + 1 > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_step: sequence %lld needs %lld tiles > %d",
+                      (long long)seq_ids[i], (long long)tiles_after, max_blocks);
   }
   pa_status st = pa_bm_append_batch(bm, n, seq_ids, slots, cow_pairs, cow_cap, n_cow);
   if (st != PA_OK) return st;
@@ -559,6 +568,7 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
 
 namespace pa {
 int64_t bm_shared_blocks(const pa_bm* bm) { return bm->n_shared; }
+int32_t bm_tiles_per_block(const pa_bm* bm) { return bm->block_size / PA_BLOCK_SIZE; }
 }  // namespace pa
 
 extern "C" {
@@ -618,6 +628,9 @@ extern "C" {
 pa_status pa_bm_enable_prefix_cache(pa_bm* bm) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_cache: bm is NULL");
   if (bm->prefix_on) return PA_OK;
+  if (bm->block_size != PA_BLOCK_SIZE)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_enable_prefix_cache: block_size %d (only 16)",
+                    bm->block_size);
   if (!bm->seqs.empty())
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_cache: %zu sequences are live",
                     bm->seqs.size());
@@ -817,6 +830,8 @@ pa_status pa_bm_enable_swap(pa_bm* bm, int32_t num_host_blocks, const int32_t* h
   if (!bm || num_host_blocks <= 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_swap: bad arguments");
   if (bm->num_host > 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_enable_swap: already on");
+  if (bm->block_size != PA_BLOCK_SIZE)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_enable_swap: block_size %d (only 16)", bm->block_size);
   std::vector<int32_t> stack(num_host_blocks);
   if (host_free_order) {
     std::vector<char> seen(num_host_blocks, 0);

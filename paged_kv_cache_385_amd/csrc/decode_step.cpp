@@ -10,7 +10,8 @@
 //      or on a copy stream that the caller's stream then waits for (the copy
 //      of step i + 1 can run while step i's kernels still run) -- or none: with
 //      no device staging buffer the kernels read the pinned one in place;
-//   3. pa_copy_blocks for the pairs, then pa_decode_fused (the new tokens'
+//   3. pa_copy_blocks for the pairs (two 16-token tiles per copied block of a
+//      32-token manager), then pa_decode_fused (the new tokens'
 //      store and the decode in one attention pass, then the merge) -- all on
 //      the caller's stream.
 
@@ -36,7 +37,8 @@ StagingLayout layout(int32_t n, int32_t max_blocks) {
   l.ctx = l.slots + align_up(sizeof(int64_t) * static_cast<size_t>(n));
   l.tables = l.ctx + align_up(sizeof(int32_t) * static_cast<size_t>(n));
   l.pairs = l.tables + align_up(sizeof(int32_t) * static_cast<size_t>(n) * max_blocks);
-  l.total = l.pairs + align_up(sizeof(int32_t) * 2 * static_cast<size_t>(n));
+  // up to two tile copies per sequence (a 32-token block is two 16-token tiles)
+  l.total = l.pairs + align_up(sizeof(int32_t) * 4 * static_cast<size_t>(n));
   return l;
 }
 
@@ -90,6 +92,18 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   st = pa_bm_step(bm, num_seqs, seq_ids, slots_h, pairs_h, num_seqs, &n_cow, tables_h,
                   max_blocks_per_seq, ctx_h, &max_ctx);
   if (st != PA_OK) return st;
+  const int32_t f = pa::bm_tiles_per_block(bm);
+  if (f == 2) {
+    // each copied 32-token block is two tile copies: expand in place, last pair first
+    for (int32_t i = n_cow - 1; i >= 0; --i) {
+      const int32_t src = pairs_h[2 * i], dst = pairs_h[2 * i + 1];
+      pairs_h[4 * i] = 2 * src;
+      pairs_h[4 * i + 1] = 2 * dst;
+      pairs_h[4 * i + 2] = 2 * src + 1;
+      pairs_h[4 * i + 3] = 2 * dst + 1;
+    }
+    n_cow *= 2;
+  }
   if (info) {
     info->num_cow = n_cow;
     info->max_context_len = max_ctx;

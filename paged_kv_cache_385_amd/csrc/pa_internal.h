@@ -23,6 +23,8 @@ int32_t device_cus();
 
 // Blocks of the manager whose reference count is above one (kept up to date).
 int64_t bm_shared_blocks(const pa_bm* bm);
+// 16-token pool tiles per block of the manager (1, or 2 for 32-token blocks).
+int32_t bm_tiles_per_block(const pa_bm* bm);
 
 // Argument checks of pa_decode for a call whose context lengths are at most
 // max_ctx, with a workspace of at least pa_decode_workspace_size(..., max_ctx)

@@ -52,7 +52,7 @@ class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  device="cuda", free_order: Optional[Sequence[int]] = None,
                  fill_bits: Optional[int] = None, kv_scales=None, prefix_caching: bool = False,
-                 host_blocks: int = 0):
+                 host_blocks: int = 0, block_size: int = N.BLOCK_SIZE):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -65,7 +65,12 @@ class PagedKVCache:
                                 .to(self.device).contiguous() for s in kv_scales)
         self.k_cache, self.v_cache = ops.alloc_pool(num_blocks, num_kv_heads, head_dim, dtype,
                                                     self.device, fill_bits, fp8=self.fp8)
-        self.bm = BlockManager(num_blocks, N.BLOCK_SIZE, free_order, prefix_caching)
+        # a 32-token manager block is two adjacent 16-token tiles of the pool
+        self.tiles_per_block = block_size // N.BLOCK_SIZE
+        if block_size not in (16, 32) or num_blocks % self.tiles_per_block:
+            raise ValueError("block_size must be 16 or 32, dividing num_blocks into tile pairs")
+        self.bm = BlockManager(num_blocks // self.tiles_per_block, block_size, free_order,
+                               prefix_caching)
         self.k_host = self.v_host = None
         if host_blocks > 0:
             shp = (ops.k8_pool_shape if self.fp8 else ops.k_pool_shape)(host_blocks, num_kv_heads, head_dim)
@@ -87,9 +92,12 @@ class PagedKVCache:
                         scales=self.scales)
 
     def copy(self, pairs: np.ndarray) -> None:
+        """Copy-on-write pairs from the block manager (in its blocks)."""
         pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
         if len(pairs) == 0:
             return
+        if self.tiles_per_block == 2:                    # block b = tiles 2 b, 2 b + 1
+            pairs = np.ascontiguousarray(np.stack([2 * pairs, 2 * pairs + 1], 1).reshape(-1, 2))
         ops.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(pairs).to(self.device),
                         pairs_host=pairs, scales=self.scales)
 

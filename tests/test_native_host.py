@@ -177,12 +177,13 @@ def _same_state(nat, ref, sids):
     assert a["waste"] == pytest.approx(b["waste"], abs=1e-12)
 
 
+@pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("seed", range(10))
-def test_native_matches_reference_on_random_traces(seed):
+def test_native_matches_reference_on_random_traces(seed, bs):
     rng = np.random.default_rng(seed)
     nb = int(rng.integers(8, 200))
     order = rng.permutation(nb)
-    nat, ref = BlockManager(nb, 16, order), REF.RefBlockManager(nb, 16, order)
+    nat, ref = BlockManager(nb, bs, order), REF.RefBlockManager(nb, bs, order)
     live, next_id = [], 0
     for step in range(500):
         r = rng.random()
@@ -249,7 +250,7 @@ def test_errors_and_atomicity():
     with pytest.raises(N.PaError):
         BlockManager(4, 16, [0, 1, 1, 2])
     with pytest.raises(N.PaError):
-        BlockManager(4, 32)
+        BlockManager(4, 64)
 
 
 def test_pack_tables():
@@ -294,14 +295,37 @@ def test_workload_traces_match(cfg):
     _same_state(nat, ref, sids)
 
 
+def tiles(table, bs):
+    """A table in the pool's 16-token tiles: 32-token block b is tiles 2 b, 2 b + 1."""
+    f = bs // 16
+    return [b * f + t for b in table for t in range(f)]
+
+
+def test_pack_tables_of_32_token_blocks():
+    nat = BlockManager(8, 32, list(range(7, -1, -1)))
+    for s, n in ((0, 1), (1, 40), (2, 32)):
+        nat.add_seq(s)
+        nat.append_tokens(s, n)
+    tab, ctx = nat.pack([2, 0, 1], 6)
+    assert ctx.tolist() == [32, 1, 40]
+    # blocks: seq 0 -> 7, seq 1 -> 6, 5, seq 2 -> 4
+    assert tab.tolist() == [[8, 9, -1, -1, -1, -1], [14, 15, -1, -1, -1, -1],
+                            [12, 13, 10, 11, -1, -1]]
+    slot, _ = nat.append(1)                 # token 40 of sequence 1: block 5, offset 8
+    assert slot == 5 * 32 + 8 == 10 * 16 + 8
+    with pytest.raises(N.PaError):
+        nat.pack([1], 3)                    # 2 blocks are 4 tiles
+
+
 # ---- the step entry points ---------------------------------------------------------------
+@pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("seed", range(4))
-def test_bm_step_matches_reference(seed):
+def test_bm_step_matches_reference(seed, bs):
     """pa_bm_step = append one token to each sequence, then pack, against the oracle's manager."""
     rng = np.random.default_rng(50 + seed)
     nb = 300
     order = rng.permutation(nb)
-    nat, ref = BlockManager(nb, 16, order), REF.RefBlockManager(nb, 16, order)
+    nat, ref = BlockManager(nb, bs, order), REF.RefBlockManager(nb, bs, order)
     for s in range(6):
         nat.add_seq(s)
         ref.add_seq(s)
@@ -319,7 +343,7 @@ def test_bm_step_matches_reference(seed):
         assert slots.tolist() == s_ref and [tuple(p) for p in cows.tolist()] == c_ref
         assert ctx.tolist() == [ref.seq_len(s) for s in sids] and mx == max(ctx.tolist())
         for i, s in enumerate(sids):
-            t = ref.block_table(s)
+            t = tiles(ref.block_table(s), bs)
             assert tabs[i, :len(t)].tolist() == t and (tabs[i, len(t):] == -1).all()
         _same_state(nat, ref, sids)
 
