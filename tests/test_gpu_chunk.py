@@ -195,3 +195,15 @@ def test_wide_kernel_bad_lengths_and_empty_chunks():
     assert torch.isnan(out[q_lens[0]:]).all()
     ref = _oracle(wl, segs, wl.chunk_q(q_lens), _starts(q_lens), [0])
     check_close(out, ref, wl.dtype, rows=np.arange(0, q_lens[0]), label="wide, good sequence")
+
+
+@pytest.mark.parametrize("q_lens,dt", [([2, 4, 3], "bf16"), ([4, 4, 1], "f16")])
+def test_two_column_groups_per_workgroup(q_lens, dt):
+    """17 to 32 columns per (sequence, KV head): one workgroup holds two groups of 16
+    columns and applies each K/V block it loads to both."""
+    ctx = [1500, 300, 2100]
+    wl = custom_workload(ctx, 16, 2, 128, dtype=dt, seed=len(q_lens) + q_lens[0])
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label=f"two groups, {q_lens}")
