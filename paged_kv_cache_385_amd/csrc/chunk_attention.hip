@@ -343,6 +343,7 @@ void chunk_attn_kernel(ChunkArgs a) {
 }
 
 constexpr int kWideCols = 128;                // columns per workgroup of the wide kernel
+constexpr float kLazyMax = 8.f;               // log2 headroom before the reference max moves
 constexpr int kWaveCols = kWideCols / kWaves; // 32 per wave: two groups of 16
 
 template <class E, int D>
@@ -541,7 +542,12 @@ void chunk_wide_kernel(ChunkArgs a) {
       float bmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       bmax = col_max4(bmax);
-      const float m_new = fmaxf(m_run[gi], bmax * c);    // c > 0: the max commutes
+      // The reference max moves only when a score exceeds it by more than 2^8 (c > 0:
+      // the max commutes with the scale).  Exponents stay <= 8, so P <= 256, which the
+      // 16-bit P and the float32 sums hold at full relative precision, and most stages
+      // skip the rescale of the accumulators.  The normalisation and the partition
+      // merge are exact for any reference.
+      const float m_new = bmax * c > m_run[gi] + kLazyMax ? bmax * c : m_run[gi];
       // a column may have seen nothing yet: exponentiate against a finite stand-in
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[gi] - m_use);
