@@ -264,7 +264,8 @@ def run_chunk(args):
         value = flops / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFS, 4)}
-    roof.update({"traffic": None, "kernel": f"chunk_attn_kernel<{wl.dtype_name.upper()},{D}>"
+    kname = "chunk_wide_kernel" if mq * (H // Hkv) >= 128 else "chunk_attn_kernel"
+    roof.update({"traffic": None, "kernel": f"{kname}<{wl.dtype_name.upper()},{D}>"
                  + (" + chunk_merge_kernel" if need else ""),
                  "avg_launch_us": round(us, 2), "bytes_per_launch": kv_bytes + io_bytes,
                  "flops_per_launch": flops})

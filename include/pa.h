@@ -481,14 +481,17 @@ pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t d
  *   block_tables, context_lens, max_context_len, max_blocks_per_seq: as pa_decode.
  *   workspace        device, >= pa_chunk_workspace_size(...) bytes, 16-byte aligned
  *                    (NULL when that size is 0).
- * One workgroup per (sequence, KV head, 16 (token, head) columns, key partition);
- * when the column tiles alone do not fill the device, keys are split into
- * partitions of 1024 tokens whose states are merged by log-sum-exp in a second
- * launch ("PagedAttention 实战", section "2026 年的新变化").  A sequence whose rows
+ * One workgroup per (sequence, KV head, 16-48 (token, head) columns, key
+ * partition); when the column groups alone do not fill the device, keys are split
+ * into partitions of 1024, 2048 or 4096 tokens (the longest that still gives
+ * every workgroup slot two items).  A sequence whose context fits one partition
+ * is written directly; the partition states of the others are merged by
+ * log-sum-exp in a second launch ("PagedAttention 实战", section "2026 年的新变化").
+ * A sequence whose rows
  * fall outside [0, total_q] is skipped (nothing written); one with a context
  * length outside [1, max_context_len] or more new tokens than cached ones gets
  * NaN rows; a block id outside [0, num_blocks) poisons (NaN) the rows of every
- * 16-column tile that reads it.
+ * column group that reads it.
  * Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
  * ------------------------------------------------------------------------- */
 size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -7,7 +7,7 @@
 // the queries; query i, at position ctx_b - n_b + i, attends over cached positions
 // 0 .. ctx_b - n_b + i.
 //
-//   chunk_attn_kernel   one workgroup per (sequence, KV head, tile of 16 query
+//   chunk_attn_kernel   one workgroup per (sequence, KV head, 1-3 tiles of 16 query
 //                       columns, key partition); a column is one (new token, query
 //                       head of the KV head's group) pair, so a tile holds 16 / G
 //                       tokens of G heads
@@ -22,8 +22,8 @@
 // v_mfma_f32_16x16x16, whose B operand is the S^T register layout.  Lane l owns
 // column l % 16, so the causal mask, the online softmax and the rescale are
 // lane-local.  The 4 waves split a partition's blocks (every 4th) and combine in
-// LDS.  Every K/V tile a workgroup reads serves 16 columns, which suits a few new
-// tokens per sequence (speculative verify) but makes long chunks L2-bound.
+// LDS.  Every K/V tile a workgroup reads serves its 16-48 columns, which suits a
+// few new tokens per sequence (speculative verify) but makes long chunks L2-bound.
 //
 // chunk_wide_kernel: each wave owns 32 columns (two groups of 16) and all four
 // waves walk the same keys, two blocks (32 tokens) per stage, so a K/V tile
@@ -50,8 +50,9 @@ using namespace pa_dev;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kCols = 16;                       // query columns per workgroup
-constexpr int kPartBlocks = 64;                 // blocks per key partition (1024 tokens)
-constexpr int kPartTokens = kPartBlocks * kBlock;
+constexpr float kLazyMax = 8.f;                 // log2 headroom before the reference max moves
+constexpr int kMinPartTokens = 1024;            // key partitions: 1024 .. 4096 tokens
+constexpr int kMaxPartTokens = 4096;
 
 struct ChunkArgs {
   const uint16_t* q;            // [total][H][D]
@@ -65,8 +66,9 @@ struct ChunkArgs {
   float* ws_acc;                // [total][H][P][D] unnormalised output
   int32_t num_seqs, total, num_heads, num_kv_heads, group;
   int32_t max_blocks, max_ctx, num_blocks;
-  int32_t col_tiles;            // column tiles per (sequence, KV head) in the grid
-  int32_t parts;                // key partitions per column tile in the grid (P)
+  int32_t col_tiles;            // column groups per (sequence, KV head) in the grid
+  int32_t parts;                // key partitions per column group in the grid (P)
+  int32_t part_blocks;          // blocks per key partition when P > 1
   float scale_log2;             // scale * log2(e)
 };
 
@@ -112,25 +114,32 @@ __device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& i
   return true;
 }
 
-template <class E, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// NT column tiles of 16 per workgroup (NT * 16 columns): every K/V tile a wave
+// loads serves all of them, so a launch with up to 48 columns per (sequence, KV
+// head) reads each tile once.  Three tiles at head dim 128 keep their q fragments
+// in LDS (the registers hold the accumulators and two blocks of K/V).  kStream:
+// each tile is read by one workgroup only, so the loads are non-temporal.
+template <class E, int D, int NT, bool kStream>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT * D > 192 ? 2 : 3)))
 void chunk_attn_kernel(ChunkArgs a) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   constexpr int kLdsStride = D + 4;
-  __shared__ float s_m[kWaves][kCols];
-  __shared__ float s_l[kWaves][kCols];
+  constexpr bool kQLds = NT * D > 256;
+  __shared__ u32x4 s_q[kQLds ? NT * KK * 64 : 1];
+  __shared__ float s_m[NT][kWaves][kCols];
+  __shared__ float s_l[NT][kWaves][kCols];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kCols * kLdsStride];
   __shared__ int s_bad;
 
   ChunkItem it;
   if (!chunk_item(a, a.parts, &it)) return;
   ChunkSeq sq;
-  if (!chunk_seq(a, it, &sq)) return;
+  if (!chunk_seq<NT * kCols>(a, it, &sq)) return;
   const int32_t b = __builtin_amdgcn_readfirstlane(it.b);
   const int32_t kvh = __builtin_amdgcn_readfirstlane(it.kvh);
   const int32_t part = __builtin_amdgcn_readfirstlane(it.part);
-  const int32_t tile = __builtin_amdgcn_readfirstlane(it.tile);
+  const int32_t col0 = __builtin_amdgcn_readfirstlane(it.tile) * (NT * kCols);
   const int32_t ctx = __builtin_amdgcn_readfirstlane(sq.ctx);
   const int32_t pmax = __builtin_amdgcn_readfirstlane(sq.pmax);
   const int32_t G = a.group;
@@ -139,20 +148,21 @@ void chunk_attn_kernel(ChunkArgs a) {
   const int32_t tid = threadIdx.x;
   const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t lane = tid & 63;
-  const int32_t n = lane & 15;       // column of this lane
+  const int32_t n = lane & 15;       // column of this lane within each 16-column tile
   const int32_t g4 = lane >> 4;      // token quad within a block
 
-  // Blocks the tile reads: 0 .. pmax / 16, in partitions of kPartBlocks -- or all
-  // in one when the launch has a single partition (outputs written directly).
-  const bool direct = a.parts == 1;
+  // Blocks the workgroup reads: 0 .. pmax / 16, in partitions of part_blocks -- or
+  // all in one, with the outputs written directly, when the launch has a single
+  // partition or the sequence's whole context fits one.
+  const bool direct = a.parts == 1 || (!sq.bad && ctx <= a.part_blocks * kBlock);
   const int32_t nblk_t = sq.bad ? 1 : pmax / kBlock + 1;
-  const int32_t pblocks = direct ? nblk_t : kPartBlocks;
+  const int32_t pblocks = direct ? nblk_t : a.part_blocks;
   if (part * pblocks >= nblk_t) return;
 
   if (sq.bad) {
-    // NaN in every row of the tile (once: partition 0 writes it, the merge keeps it)
-    for (int32_t i = tid; i < kCols * D; i += kThreads) {
-      const int32_t c = tile * kCols + i / D;
+    // NaN in every row of the columns (once: partition 0 writes it, the merge keeps it)
+    for (int32_t i = tid; i < NT * kCols * D; i += kThreads) {
+      const int32_t c = col0 + i / D;
       if (c < sq.cols) {
         const int64_t row = static_cast<int64_t>(sq.qs + c / G) * H + kvh * G + c % G;
         a.out[row * D + i % D] = E::kNaN;
@@ -161,17 +171,31 @@ void chunk_attn_kernel(ChunkArgs a) {
     return;
   }
 
-  // This lane's column: token ti of the chunk, head gh of the group, position pos.
-  const int32_t col = tile * kCols + n;
-  const bool col_ok = col < sq.cols;
-  const int32_t ti = col_ok ? col / G : 0;
-  const int32_t gh = col_ok ? col - ti * G : 0;
-  const int32_t pos = col_ok ? ctx - sq.n + ti : pmax;   // padding columns: zero q, no mask
-  const int64_t q_row = (static_cast<int64_t>(sq.qs + ti) * H + kvh * G + gh) * D;
-  u32x4 qf[KK];
+  // This lane's column in tile t: token ti of the chunk, head gh of the group,
+  // position pos[t].  Padding columns load zero q and mask nothing.
+  int32_t pos[NT];
+  u32x4 qf[kQLds ? 1 : NT][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+  for (int t = 0; t < NT; ++t) {
+    const int32_t col = col0 + t * kCols + n;
+    const bool col_ok = col < sq.cols;
+    const int32_t ti = col_ok ? col / G : 0;
+    const int32_t gh = col_ok ? col - ti * G : 0;
+    pos[t] = col_ok ? ctx - sq.n + ti : pmax;
+    const int64_t q_row = (static_cast<int64_t>(sq.qs + ti) * H + kvh * G + gh) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if constexpr (kQLds) {
+        // wave w stores the fragments (t, kk) with (t * KK + kk) % 4 == w
+        if ((t * KK + kk) % kWaves == w)
+          s_q[(t * KK + kk) * 64 + lane] =
+              col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+      } else {
+        qf[t][kk] = col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  if constexpr (kQLds) __syncthreads();
 
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
   const int32_t jbeg = part * pblocks;
@@ -183,60 +207,51 @@ void chunk_attn_kernel(ChunkArgs a) {
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
 
   bool bad_blk = false;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[MT];
+  float m_run[NT], l_run[NT];
+  f32x4 acc[NT][MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   u32x4 kb[2][KK], vb[2][KK];
   // The wave's blocks go in runs of up to 64: lane i holds the id of the run's i-th.
   int32_t ids = 0, i0 = 0, cnt = 0;
 
   // Bounded buffer loads as in the decode pass; a step past the run's last block
-  // has an empty range and reads nothing.  The tiles of one partition are read by
-  // every column tile of the group, so they go through the caches.
+  // has an empty range and reads nothing.  With several column groups per
+  // (sequence, KV head) each tile is read by all of them, so it goes through the
+  // caches; with one (kStream) it is read once.
   auto load_block = [&](int buf, int32_t i) {
     const int32_t phys = __builtin_amdgcn_readlane(ids, min(i, cnt - 1));
     const int32_t bytes = i < cnt ? static_cast<int32_t>(tile_elems * sizeof(uint16_t)) : 0;
     const auto kr = tile_rsrc(a.k_cache + phys * blk_stride + head_off, bytes);
     const auto vr = tile_rsrc(a.v_cache + phys * blk_stride + head_off, bytes);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<false>(kr, (kk * 64 + lane) * 16);
+    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
 #pragma unroll
     for (int j2 = 0; j2 < KK; ++j2)
-      vb[buf][j2] = load_tile<false>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+      vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
   };
 
   auto compute_block = [&](int buf, int32_t i) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s[NT];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(kb[buf][kk], qf[kk], s);
+    for (int t = 0; t < NT; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 qv;
+        if constexpr (kQLds)
+          qv = s_q[(t * KK + kk) * 64 + lane];
+        else
+          qv = qf[t][kk];
+        s[t] = E::mfma_qk(kb[buf][kk], qv, s[t]);
+      }
+    }
     const int32_t t0 = (first + kWaves * (i0 + i)) * kBlock; // position of the block's token 0
-    const int32_t seen = i < cnt ? pos - t0 : -1;           // this column sees tokens 0 .. seen
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = s[r] * a.scale_log2;
-      if (4 * g4 + r > seen) sv[r] = -INFINITY;
-    }
-    float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    // a column may have seen nothing yet: exponentiate against a finite stand-in
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    u16x4 pb;
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pb[r] = E::from_float(fast_exp2(sv[r] - m_use));
-      psum += E::to_float(pb[r]);
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] *= alpha;
     const int32_t valid = i < cnt ? ctx - t0 : 0;            // tokens of the block in context
     if (valid < kBlock) {
       // positions past the context may hold anything (NaN included): zero their V
@@ -250,12 +265,43 @@ void chunk_attn_kernel(ChunkArgs a) {
       }
     }
 #pragma unroll
-    for (int j2 = 0; j2 < KK; ++j2) {
-      const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
-      const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
-      const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
-      acc[2 * j2] = E::mfma_pv(lo, pb, acc[2 * j2]);
-      acc[2 * j2 + 1] = E::mfma_pv(hi, pb, acc[2 * j2 + 1]);
+    for (int t = 0; t < NT; ++t) {
+      const int32_t seen = i < cnt ? pos[t] - t0 : -1;        // this column sees tokens 0 .. seen
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = s[t][r] * a.scale_log2;
+        if (4 * g4 + r > seen) sv[r] = -INFINITY;
+      }
+      float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bmax = col_max4(bmax);
+      // The reference max moves only when a score passes it by more than kLazyMax
+      // (log2 units), so P <= 2^kLazyMax and most blocks skip the rescale.
+      const float m_new = bmax > m_run[t] + kLazyMax ? bmax : m_run[t];
+      // a column may have seen nothing yet: exponentiate against a finite stand-in
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[t] - m_use);
+      m_run[t] = m_new;
+      u16x4 pb;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = E::from_float(fast_exp2(sv[r] - m_use));
+        psum += E::to_float(pb[r]);
+      }
+      l_run[t] = l_run[t] * alpha + psum;
+      if (__ballot(alpha != 1.f) != 0) {              // the reference moved somewhere
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[t][j] *= alpha;
+      }
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2) {
+        const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+        const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
+        const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
+        acc[t][2 * j2] = E::mfma_pv(lo, pb, acc[t][2 * j2]);
+        acc[t][2 * j2 + 1] = E::mfma_pv(hi, pb, acc[t][2 * j2 + 1]);
+      }
     }
   };
 
@@ -277,73 +323,79 @@ void chunk_attn_kernel(ChunkArgs a) {
     }
   }
 
-  // ---- combine the four waves in LDS ----
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (g4 == 0) {
-    s_m[w][n] = m_run;
-    s_l[w][n] = l_run;
+  // ---- combine the four waves in LDS, one 16-column tile at a time ----
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    l_run[t] += __shfl_xor(l_run[t], 16);
+    l_run[t] += __shfl_xor(l_run[t], 32);
+    if (g4 == 0) {
+      s_m[t][w][n] = m_run[t];
+      s_l[t][w][n] = l_run[t];
+    }
   }
   if (tid == 0) s_bad = 0;
   __syncthreads();
   if (bad_blk) s_bad = 1;
-  float M = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][n]);
-  const float wscale = fast_exp2(m_run - (M == -INFINITY ? 0.f : M));
-  {
-    float* row = &s_acc[w][n * kLdsStride];
+  for (int t = 0; t < NT; ++t) {
+    if (t > 0) __syncthreads();   // the previous tile's reads of s_acc are done
+    float M = -INFINITY;
 #pragma unroll
-    for (int j2 = 0; j2 < KK; ++j2) {
-      const f32x4 e = acc[2 * j2] * wscale;
-      const f32x4 o = acc[2 * j2 + 1] * wscale;
-      float* dst = row + 32 * j2 + 8 * g4;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], o[0], e[1], o[1]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[2], o[2], e[3], o[3]};
-    }
-  }
-  __syncthreads();
-  const bool poisoned = s_bad != 0;
-
-  // each thread finishes 4 consecutive dims of one column
-  for (int32_t i4 = tid; i4 < kCols * (D / 4); i4 += kThreads) {
-    const int32_t c = i4 / (D / 4);
-    const int32_t d = (i4 - c * (D / 4)) * 4;
-    const int32_t gc = tile * kCols + c;
-    if (gc >= sq.cols) continue;
-    float Mc = -INFINITY;
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[t][v][n]);
+    const float wscale = fast_exp2(m_run[t] - (M == -INFINITY ? 0.f : M));
+    {
+      float* row = &s_acc[w][n * kLdsStride];
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) Mc = fmaxf(Mc, s_m[v][c]);
-    const float Mu = Mc == -INFINITY ? 0.f : Mc;
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      L += s_l[v][c] * fast_exp2(s_m[v][c] - Mu);
-      o += *reinterpret_cast<const f32x4*>(&s_acc[v][c * kLdsStride + d]);
-    }
-    const int64_t hrow = static_cast<int64_t>(sq.qs + gc / G) * H + kvh * G + gc % G;
-    if (direct) {
-      u16x4 ov;
-      if (poisoned) {
-        ov = u16x4{E::kNaN, E::kNaN, E::kNaN, E::kNaN};
-      } else {
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+      for (int j2 = 0; j2 < KK; ++j2) {
+        const f32x4 e = acc[t][2 * j2] * wscale;
+        const f32x4 o = acc[t][2 * j2 + 1] * wscale;
+        float* dst = row + 32 * j2 + 8 * g4;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], o[0], e[1], o[1]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[2], o[2], e[3], o[3]};
       }
-      *reinterpret_cast<u16x4*>(a.out + hrow * D + d) = ov;
-    } else {
-      const int64_t st = hrow * a.parts + part;
-      if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
-      *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
-      if (d == 0) a.ws_ml[st] = poisoned ? float2{0.f, NAN} : float2{Mc, L};
+    }
+    __syncthreads();
+    const bool poisoned = s_bad != 0;
+
+    // each thread finishes 4 consecutive dims of one column
+    for (int32_t i4 = tid; i4 < kCols * (D / 4); i4 += kThreads) {
+      const int32_t c = i4 / (D / 4);
+      const int32_t d = (i4 - c * (D / 4)) * 4;
+      const int32_t gc = col0 + t * kCols + c;
+      if (gc >= sq.cols) continue;
+      float Mc = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) Mc = fmaxf(Mc, s_m[t][v][c]);
+      const float Mu = Mc == -INFINITY ? 0.f : Mc;
+      float L = 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        L += s_l[t][v][c] * fast_exp2(s_m[t][v][c] - Mu);
+        o += *reinterpret_cast<const f32x4*>(&s_acc[v][c * kLdsStride + d]);
+      }
+      const int64_t hrow = static_cast<int64_t>(sq.qs + gc / G) * H + kvh * G + gc % G;
+      if (direct) {
+        u16x4 ov;
+        if (poisoned) {
+          ov = u16x4{E::kNaN, E::kNaN, E::kNaN, E::kNaN};
+        } else {
+          const float inv = 1.f / L;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
+        }
+        *reinterpret_cast<u16x4*>(a.out + hrow * D + d) = ov;
+      } else {
+        const int64_t st = hrow * a.parts + part;
+        if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
+        *reinterpret_cast<f32x4*>(a.ws_acc + st * D + d) = o;
+        if (d == 0) a.ws_ml[st] = poisoned ? float2{0.f, NAN} : float2{Mc, L};
+      }
     }
   }
 }
 
 constexpr int kWideCols = 128;                // columns per workgroup of the wide kernel
-constexpr float kLazyMax = 8.f;               // log2 headroom before the reference max moves
 constexpr int kWaveCols = kWideCols / kWaves; // 32 per wave: two groups of 16
 
 template <class E, int D>
@@ -376,9 +428,9 @@ void chunk_wide_kernel(ChunkArgs a) {
   const int32_t n = lane & 15;
   const int32_t g4 = lane >> 4;
 
-  const bool direct = a.parts == 1;
+  const bool direct = a.parts == 1 || (!sq.bad && ctx <= a.part_blocks * kBlock);
   const int32_t nblk_t = sq.bad ? 1 : pmax / kBlock + 1;
-  const int32_t pblocks = direct ? nblk_t : kPartBlocks;
+  const int32_t pblocks = direct ? nblk_t : a.part_blocks;
   if (part * pblocks >= nblk_t) return;
 
   if (sq.bad) {
@@ -619,8 +671,8 @@ void chunk_wide_kernel(ChunkArgs a) {
   }
 }
 
-// One workgroup per (sequence, KV head, column tile), 4 dims of one column per
-// thread: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
+// One workgroup per (sequence, KV head, column tile) of the sequences whose context
+// spans several partitions, 4 dims of one column per thread: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
 // the partitions a column's own position reaches (later ones hold nothing for it),
 // in partition order.
 template <class E, int D>
@@ -630,6 +682,8 @@ __global__ __launch_bounds__(kThreads) void chunk_merge_kernel(ChunkArgs a) {
   ChunkSeq sq;
   if (!chunk_seq(a, it, &sq)) return;
   if (sq.bad) return;                       // the attention pass wrote NaN
+  const int32_t part_tokens = a.part_blocks * kBlock;
+  if (sq.ctx <= part_tokens) return;        // one partition: written directly
   const int32_t G = a.group;
   const int32_t H = a.num_heads;
   for (int32_t i4 = threadIdx.x; i4 < kCols * (D / 4); i4 += kThreads) {
@@ -638,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void chunk_merge_kernel(ChunkArgs a) {
     const int32_t gc = it.tile * kCols + c;
     if (gc >= sq.cols) continue;
     const int32_t pos = sq.ctx - sq.n + gc / G;
-    const int32_t np = pos / kPartTokens + 1;
+    const int32_t np = pos / part_tokens + 1;
     const int64_t hrow = static_cast<int64_t>(sq.qs + gc / G) * H + it.kvh * G + gc % G;
     const int64_t st0 = hrow * a.parts;
     float M = -INFINITY;
@@ -660,39 +714,74 @@ __global__ __launch_bounds__(kThreads) void chunk_merge_kernel(ChunkArgs a) {
 }
 
 // The launch plan.  Launches with at least 128 columns per (sequence, KV head)
-// use the wide kernel.  Key partitions: one when the column tiles alone give
-// every workgroup slot enough items (eight for the narrow kernel at three
-// workgroups per compute unit, two for the wide one), else partitions of 1024
-// tokens, so long contexts with few new tokens still spread over the device and
-// no single workgroup walks a whole long context.
+// use the wide kernel; narrower ones the narrow kernel with up to three 16-column
+// tiles per workgroup.
+// Key partitions: one when the column groups alone give every workgroup slot
+// enough items (eight for the narrow kernel, two for the wide one); else the
+// longest of 4096, 2048 and 1024 tokens for which even the longest possible item
+// list (every sequence at the longest context) gives every slot two items, so
+// long contexts with few new tokens still spread over the device while each item
+// stays long enough to amortise its start-up.
+constexpr int kMaxNarrowTiles = 3;
 struct ChunkPlan {
   bool wide;
-  int32_t tiles;        // column tiles of the attention launch
+  int32_t nt;           // 16-column tiles per workgroup of the narrow kernel
+  int32_t tiles;        // column groups of the attention launch
   int32_t merge_tiles;  // 16-column tiles of the merge launch
   int32_t parts;
+  int32_t part_blocks;
 };
-ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len,
-                     int32_t max_ctx) {
+ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t max_q_len, int32_t max_ctx) {
   ChunkPlan p;
   const int64_t cols = static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads);
   p.wide = cols >= kWideCols;
   p.merge_tiles = static_cast<int32_t>((cols + kCols - 1) / kCols);
-  p.tiles = p.wide ? static_cast<int32_t>((cols + kWideCols - 1) / kWideCols) : p.merge_tiles;
+  p.nt = p.wide ? 1 : std::min(p.merge_tiles, kMaxNarrowTiles);
+  p.tiles = p.wide ? static_cast<int32_t>((cols + kWideCols - 1) / kWideCols)
+                   : (p.merge_tiles + p.nt - 1) / p.nt;
   const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * p.tiles;
-  const int64_t slots = (p.wide ? 2 : 8 * 3) * static_cast<int64_t>(pa::device_cus());
-  p.parts = items >= slots ? 1 : (max_ctx + kPartTokens - 1) / kPartTokens;
+  // workgroups per compute unit: the wide kernel and the multi-tile narrow one at
+  // head dim 128 run two, the others three or more
+  const int64_t per_cu = (p.wide || p.nt * head_dim > 192) ? 2 : 3;
+  const int64_t slots = per_cu * static_cast<int64_t>(pa::device_cus());
+  p.part_blocks = kMinPartTokens / kBlock;
+  if (items >= (p.wide ? 1 : 8) * slots) {
+    p.parts = 1;
+    return p;
+  }
+  for (int32_t pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2)
+    if (items * ((max_ctx + pt - 1) / pt) >= 2 * slots) {
+      p.part_blocks = pt / kBlock;
+      break;
+    }
+  const int32_t part_tokens = p.part_blocks * kBlock;
+  p.parts = (max_ctx + part_tokens - 1) / part_tokens;
   return p;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+template <class E, int D, bool kStream>
+void launch_narrow(const ChunkArgs& a, int32_t nt, dim3 grid, hipStream_t s) {
+  if (nt == 1)
+    chunk_attn_kernel<E, D, 1, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+  else if (nt == 2)
+    chunk_attn_kernel<E, D, 2, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+  else
+    chunk_attn_kernel<E, D, 3, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+}
+
 template <class E, int D>
-void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, hipStream_t s) {
+void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, bool stream,
+                    hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(groups8 * p.tiles * p.parts));
   if (p.wide)
     chunk_wide_kernel<E, D><<<grid, dim3(kThreads), 0, s>>>(a);
+  else if (stream)
+    launch_narrow<E, D, true>(a, p.nt, grid, s);
   else
-    chunk_attn_kernel<E, D><<<grid, dim3(kThreads), 0, s>>>(a);
+    launch_narrow<E, D, false>(a, p.nt, grid, s);
   if (p.parts > 1) {
     ChunkArgs m = a;                     // the merge works in 16-column tiles
     m.col_tiles = p.merge_tiles;
@@ -702,11 +791,12 @@ void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, hip
 }
 
 template <class E>
-void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, hipStream_t s) {
+void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, bool stream,
+                  hipStream_t s) {
   if (d == 64)
-    launch_chunk_d<E, 64>(a, p, groups8, s);
+    launch_chunk_d<E, 64>(a, p, groups8, stream, s);
   else
-    launch_chunk_d<E, 128>(a, p, groups8, s);
+    launch_chunk_d<E, 128>(a, p, groups8, stream, s);
 }
 
 }  // namespace
@@ -719,7 +809,8 @@ size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
       head_dim <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len <= 0)
     return 0;
-  const int32_t P = chunk_plan(num_seqs, num_heads, num_kv_heads, max_q_len, max_context_len).parts;
+  const int32_t P =
+      chunk_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_q_len, max_context_len).parts;
   if (P <= 1) return 0;
   const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
   return round256(static_cast<size_t>(rows) * sizeof(float2)) +
@@ -755,8 +846,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
     return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer or q / out not 16-byte aligned", fn);
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   const int32_t G = num_heads / cache->num_kv_heads;
-  const ChunkPlan plan = chunk_plan(num_seqs, num_heads, cache->num_kv_heads, max_q_len,
-                                    max_context_len);
+  const ChunkPlan plan = chunk_plan(num_seqs, num_heads, cache->num_kv_heads, cache->head_dim,
+                                    max_q_len, max_context_len);
   const int32_t P = plan.parts;
   const int64_t groups = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
   const int64_t groups8 = 8 * ((groups + 7) / 8);
@@ -792,12 +883,16 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   a.num_blocks = cache->num_blocks;
   a.col_tiles = plan.tiles;
   a.parts = P;
+  a.part_blocks = plan.part_blocks;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // one column group per (sequence, KV head) reads each tile once, unless blocks
+  // are shared between sequences
+  const bool once = plan.tiles == 1 && !(cache->flags & PA_CACHE_SHARED_BLOCKS);
   if (cache->dtype == PA_F16)
-    launch_chunk<F16>(a, plan, groups8, cache->head_dim, s);
+    launch_chunk<F16>(a, plan, groups8, cache->head_dim, once, s);
   else
-    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, s);
+    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, once, s);
   return pa::launch_status(fn);
 }
 

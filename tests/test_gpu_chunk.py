@@ -207,3 +207,35 @@ def test_two_column_groups_per_workgroup(q_lens, dt):
     q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
     ref = _oracle(wl, segs, q, starts, range(len(ctx)))
     check_close(out, ref, wl.dtype, label=f"two groups, {q_lens}")
+
+
+@pytest.mark.parametrize("q_lens,H,D,dt", [([12, 10, 9, 11], 8, 64, "f16"),
+                                           ([7, 12, 1, 12], 8, 64, "bf16"),
+                                           ([5, 3, 4, 5], 16, 128, "bf16"),
+                                           ([6, 6, 2, 5], 16, 128, "f16")])
+def test_three_column_groups_per_workgroup(q_lens, H, D, dt):
+    """33 to 48 columns per (sequence, KV head): one workgroup holds three groups of
+    16 columns, the last one ragged (q fragments in LDS at head dim 128)."""
+    ctx = [1500, 300, 2100, 700]
+    wl = custom_workload(ctx, H, 2, D, dtype=dt, seed=sum(q_lens) + D)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label=f"three groups, {q_lens}")
+
+
+def test_single_partition_sequences_bypass_the_merge():
+    """Key partitions in one launch: sequences whose context fits one partition (here
+    1024 tokens) write their outputs directly, the others go through the merge."""
+    from paged_kv_cache_385_amd import chunk_workspace_size
+    ctx = [1024, 5000, 300, 2049, 1025, 16]
+    q_lens = [3, 4, 2, 4, 1, 4]
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=23)
+    ws = chunk_workspace_size(len(ctx), 16, 2, 128, sum(q_lens), max(q_lens), wl.max_context_len)
+    say(f"mixed direct and merged sequences: workspace {ws} bytes")
+    assert ws > 0
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    assert not torch.isnan(out).any()
+    ref = _oracle(wl, segs, q, starts, range(len(ctx)))
+    check_close(out, ref, wl.dtype, label="direct and merged")
