@@ -453,7 +453,8 @@ def run_prefix(args):
               "speedup": round(full["wall_s"] / cached["wall_s"], 2),
               "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
                            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                           "traffic": None, "kernel": "chunk_attn_kernel<BF16,128>",
+                           "traffic": None, "kernel": "chunk_wide_kernel<BF16,128>",
+                           "write_us": round(cached["write_us"], 1),
                            "avg_launch_us": round(cached["attn_us"], 2),
                            "flops_per_launch": int(cached["flops"])}}
     if not args.no_cpu_baseline:
