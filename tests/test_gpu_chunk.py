@@ -58,8 +58,9 @@ def _rows(starts, seqs):
 
 
 def test_speculative_verify_shape():
-    """70B-shaped GQA-8 bf16 batch, 6 tokens per sequence (5 drafts + 1): key partitions
-    and the merge launch; every sequence's rows compared on a sample of sequences."""
+    """70B-shaped GQA-8 bf16 batch, 6 tokens per sequence (5 drafts + 1): the 48 columns
+    of a (sequence, KV head) in one workgroup, in the launch configuration the bench
+    times; every row of a sample of sequences compared."""
     wl = make_workload(3)
     say("workload 3, 6 new tokens per sequence")
     cache, segs, tables, ctx_d = _cache_with_context(wl)
