@@ -73,6 +73,32 @@ def test_speculative_verify_shape():
     check_close(out, ref, wl.dtype, rows=_rows(starts, seqs), label="verify, workload 3")
 
 
+def test_prefill_chunk_shape():
+    """The prefill-chunk measurement's launch: the last 1024-token chunk of four 4096-token
+    prompts in a 70B-shaped GQA-8 bf16 layer (wide kernel, one partition).  Sampled rows:
+    windows of 32 queries at the start, middle and end of every chunk; a window ending
+    at position e is a chunk of its own over the keys up to e, which is what its rows
+    attend to."""
+    wl = custom_workload([4096] * 4, 64, 8, 128, dtype="bf16", seed=385)
+    say("four 4096-token prompts, last 1024-token chunk, G=8, bf16")
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    n = 1024
+    q_lens = np.full(4, n)
+    q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
+    assert not torch.isnan(out).any()
+    ref = np.full(q.shape, np.nan)
+    rows = []
+    for b in range(4):
+        k, v = wl.seq_kv(b, segs)
+        ctx = int(wl.ctx_lens[b])
+        for r0 in (0, n // 2 - 16, n - 32):
+            lo = int(starts[b]) + r0
+            end = ctx - n + r0 + 32                  # keys of the window's last query
+            ref[lo:lo + 32] = OA.chunk_attention(q[lo:lo + 32], k[:end], v[:end], wl.scale)
+            rows.extend(range(lo, lo + 32))
+    check_close(out, ref, wl.dtype, rows=np.asarray(rows), label="prefill chunk shape")
+
+
 @pytest.mark.parametrize("q_lens,ctx", [
     ([300, 1024, 40, 1], [700, 1500, 40, 33]),     # chunks, a whole prompt, a decode
     ([17, 5, 64], [17, 2100, 64]),                  # whole prompts, ragged chunk
