@@ -37,8 +37,16 @@ EVENT_EVERY = 5                # timed steps whose attention pass carries a timi
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, AMD published (no sparsity)
 METRIC = "paged-attn decode KV GB/s read (% of HBM peak); sequence-steps/s"
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc", "pa_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_traffic.json")
+CSRC = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc")
+# per measured leg: the counter summary file, the kernel source it is stamped with and
+# the kernel names that make up one call
+TRAFFIC = {
+    "decode": (os.path.join(ROOT, "profiles", "decode_attn_traffic.json"),
+               os.path.join(CSRC, "pa_kernels.hip"), ("decode_attn_kernel",)),
+    "chunk": (os.path.join(ROOT, "profiles", "chunk_attn_traffic_{mode}.json"),
+              os.path.join(CSRC, "chunk_attention.hip"),
+              ("chunk_attn_kernel", "chunk_wide_kernel", "chunk_merge_kernel")),
+}
 CONTEXT_TEXT = {
     1: "17, 33, 64, 100 tokens",
     2: "uniform in [128, 2048]",
@@ -85,58 +93,88 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha256() -> str:
+def source_sha256(path: str) -> str:
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def traffic_leg(args):
+    """(summary file, stamped source, kernel names, workload key) of the measured leg."""
+    if args.chunk:
+        path, src, names = TRAFFIC["chunk"]
+        return path.format(mode=args.chunk), src, names, f"chunk-{args.chunk}"
+    path, src, names = TRAFFIC["decode"]
+    return path, src, names, args.workload
+
+
 def summarize_counters(args):
-    """Per-launch HBM traffic of the attention kernel from two counter runs.
+    """Per-call HBM traffic of the measured leg's kernels from two counter runs.
 
     Each counter is scaled by what it reads for the calibration copy (a plain
     device copy of known size run by the same command): bytes moved / counter.
-    The timed launches are the last ``--steps`` attention dispatches.
+    The timed calls are the last ``--steps`` ones; a call is every launch of the
+    leg's kernels (a chunk call may add a merge launch).
     """
     import csv
-    out = {"kernel": None, "workload": args.workload, "steps": args.steps, "warmup": args.warmup,
+    path_out, src, names, key = traffic_leg(args)
+    out = {"kernel": None, "workload": key, "steps": args.steps, "warmup": args.warmup,
            "copy_bytes": args.copy_calibration << 20}
     for name, path in (("fetch", args.summarize_counters[0]), ("write", args.summarize_counters[1])):
         rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
-        attn = [r for r in rows if "decode_attn_kernel" in r["Kernel_Name"]]
+        attn = [r for r in rows if any(k in r["Kernel_Name"] for k in names)]
         first = int(attn[0]["Dispatch_Id"])
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first]
         calib = copies[-3:]                       # the three calibration copies come last
         kib = float(np.mean([float(r["Counter_Value"]) for r in calib]))
         scale = out["copy_bytes"] / (kib * 1024.0)
-        timed = attn[-args.steps:]
-        mean_kib = float(np.mean([float(r["Counter_Value"]) for r in timed]))
+        per_call = len(attn) // (args.steps + args.warmup)
+        timed = attn[-args.steps * per_call:]
+        mean_kib = float(np.sum([float(r["Counter_Value"]) for r in timed])) / args.steps
         out[f"{name}_counter"] = timed[0]["Counter_Name"]
         out[f"{name}_copy_kib"] = kib
         out[f"{name}_scale"] = round(scale, 4)
         out[f"{name}_kib_per_launch"] = round(mean_kib, 1)
         out[f"{name}_bytes_per_launch"] = int(mean_kib * 1024.0 * scale)
-        out["kernel"] = timed[0]["Kernel_Name"]
+        out["kernel"] = " + ".join(sorted({r["Kernel_Name"] for r in timed}))
         out["launches"] = len(timed)
     out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    out["source_sha256"] = source_sha256()
-    with open(TRAFFIC_FILE, "w") as f:
+    out["source_sha256"] = source_sha256(src)
+    with open(path_out, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
 
 
-def recorded_traffic(workload: int, steps: int, warmup: int):
-    """Traffic per launch from the counter file, if it was taken on this kernel source and run."""
+def recorded_traffic(args, steps: int, warmup: int):
+    """Traffic per call from the leg's counter file, if it was taken on this kernel source
+    and run."""
+    path, src, _, key = traffic_leg(args)
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if (t.get("source_sha256") != source_sha256() or t.get("workload") != workload
+    if (t.get("source_sha256") != source_sha256(src) or t.get("workload") != key
             or t.get("steps") != steps or t.get("warmup") != warmup):
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def calibration_copy(args, dev):
+    """Three device-to-device copies of --copy-calibration MiB, right before the timed
+    launches: the counter runs scale FETCH_SIZE and WRITE_SIZE by what they read here."""
+    import torch
+    if not args.copy_calibration:
+        return
+    n = args.copy_calibration << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: 3 x {args.copy_calibration} MiB device-to-device")
+    del src, dst
 
 
 def log(msg):
@@ -229,6 +267,7 @@ def run_chunk(args):
     log(f"set-up {time.perf_counter() - t0:.1f} s; workspace {need} bytes "
         f"({'key partitions + merge launch' if need else 'one partition'})")
     stream = torch.cuda.current_stream(dev)
+    calibration_copy(args, dev)
 
     def call():
         pa.chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, ctx_d, mq, max_ctx,
@@ -265,7 +304,8 @@ def run_chunk(args):
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFS, 4)}
     kname = "chunk_wide_kernel" if mq * (H // Hkv) >= 128 else "chunk_attn_kernel"
-    roof.update({"traffic": None, "kernel": f"{kname}<{wl.dtype_name.upper()},{D}>"
+    roof.update({"traffic": recorded_traffic(args, K, W),
+                 "kernel": f"{kname}<{wl.dtype_name.upper()},{D}>"
                  + (" + chunk_merge_kernel" if need else ""),
                  "avg_launch_us": round(us, 2), "bytes_per_launch": kv_bytes + io_bytes,
                  "flops_per_launch": flops})
@@ -588,6 +628,9 @@ def run_swap(args):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.swap:
         if args.gpus != 1:
             print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -605,9 +648,6 @@ def main():
             print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
             sys.exit(2)
         run_chunk(args)
-        return
-    if args.summarize_counters:
-        summarize_counters(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -661,15 +701,7 @@ def main():
     torch.cuda.synchronize()
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: 3 x {args.copy_calibration} MiB device-to-device")
-        del src, dst
+    calibration_copy(args, dev)
 
     per_tok = 2 * Hkv * D * (1 if fp8 else 2)     # K and V bytes per cached token
     base_ctx = wl.ctx_lens.astype(np.int64)
@@ -735,7 +767,7 @@ def main():
         "seq_steps_per_s": round(B * K / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 or bsz != 16 else recorded_traffic(args.workload, K, W),
+                     "traffic": None if fp8 or bsz != 16 else recorded_traffic(args, K, W),
                      "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}"
                                + (",FP8>" if fp8 else ">"),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
