@@ -24,6 +24,8 @@
 // lane-local.  The 4 waves split a partition's blocks (every 4th) and combine in
 // LDS.  Every K/V tile a workgroup reads serves its 16-48 columns, which suits a
 // few new tokens per sequence (speculative verify) but makes long chunks L2-bound.
+// Its workgroups take the sequences longest first (a counting sort over classes
+// of context length), so the longest items do not start last.
 //
 // chunk_wide_kernel: each wave owns 32 columns (two groups of 16) and all four
 // waves walk the same keys, two blocks (32 tokens) per stage, so a K/V tile
@@ -93,6 +95,98 @@ __device__ __forceinline__ bool chunk_item(const ChunkArgs& a, int32_t parts, Ch
   return true;
 }
 
+// Largest-first order of the sequences: a counting sort over 16 classes of context
+// length (in steps of 1/16 of the longest), from the longest class down, ascending
+// sequence index within a class.  Long items start first and short ones fill the
+// tail; in the order the sequences come, a long one may start last and set the
+// launch's length.  A length outside [1, max_ctx] is class 0 (its rows become NaN).
+constexpr int kOrderClasses = 16;
+constexpr int kOrderChunks = 4;          // context lengths kept in registers: 4 x 64
+__device__ __forceinline__ int32_t order_class(int32_t ctx, int32_t max_ctx) {
+  if (ctx < 1 || ctx > max_ctx) return 0;
+  return static_cast<int32_t>(static_cast<int64_t>(ctx) * kOrderClasses /
+                              (static_cast<int64_t>(max_ctx) + 1));
+}
+// Lane of the k-th (from 0) set bit of mask.
+__device__ __forceinline__ int32_t kth_lane(uint64_t mask, int32_t k, int32_t lane) {
+  const bool mine = ((mask >> lane) & 1) && __popcll(mask & ((1ull << lane) - 1)) == k;
+  return __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+}
+__device__ __forceinline__ void load_order_chunk(const ChunkArgs& a, int32_t c0, int32_t lane,
+                                                 int32_t cl[kOrderChunks]) {
+#pragma unroll
+  for (int u = 0; u < kOrderChunks; ++u) {
+    const int32_t i = c0 + 64 * u + lane;
+    cl[u] = i < a.num_seqs ? order_class(a.ctx_lens[i], a.max_ctx) : -1;
+  }
+}
+// Sequence of rank r (0 <= r < num_seqs) in that order; every lane gets it.
+__device__ int32_t seq_of_rank(const ChunkArgs& a, int32_t r, int32_t lane) {
+  constexpr int32_t kGroup = 64 * kOrderChunks;
+  int32_t cl0[kOrderChunks];             // the first group, kept for the second pass
+  int32_t cnt = 0;                       // lane c: sequences of class c
+  for (int32_t c0 = 0; c0 < a.num_seqs; c0 += kGroup) {
+    int32_t cl[kOrderChunks];
+    load_order_chunk(a, c0, lane, cl);
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kOrderChunks; ++u) cl0[u] = cl[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kOrderChunks; ++u) {
+      if (c0 + 64 * u >= a.num_seqs) break;     // no sequence in this or later chunks
+#pragma unroll 1
+      for (int32_t c = 0; c < kOrderClasses; ++c) {
+        const int32_t nc = __popcll(__ballot(cl[u] == c));
+        cnt += lane == c ? nc : 0;
+      }
+    }
+  }
+  int32_t cls = 0, k = r;
+  for (int32_t c = kOrderClasses - 1; c >= 0; --c) {
+    const int32_t cc = __builtin_amdgcn_readlane(cnt, c);
+    if (k < cc) {
+      cls = c;
+      break;
+    }
+    k -= cc;
+  }
+  for (int32_t c0 = 0; c0 < a.num_seqs; c0 += kGroup) {
+    int32_t cl[kOrderChunks];
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kOrderChunks; ++u) cl[u] = cl0[u];
+    } else {
+      load_order_chunk(a, c0, lane, cl);
+    }
+#pragma unroll
+    for (int u = 0; u < kOrderChunks; ++u) {
+      const uint64_t m = __ballot(cl[u] == cls);
+      const int32_t pc = __popcll(m);
+      if (k < pc) return c0 + 64 * u + kth_lane(m, k, lane);
+      k -= pc;
+    }
+  }
+  return -1;    // not reached: the classes count every sequence
+}
+// chunk_item with the groups taken in largest-first order of their sequences: group
+// rank g = (sequence rank) * Hkv + KV head, placed on XCD g % 8 as above.
+__device__ __forceinline__ bool chunk_item_ordered(const ChunkArgs& a, int32_t lane,
+                                                   ChunkItem* it) {
+  const int32_t per_group = a.col_tiles * a.parts;
+  const int32_t x = blockIdx.x & 7;
+  const int32_t k = blockIdx.x >> 3;
+  const int32_t g = x + 8 * (k / per_group);
+  if (g >= a.num_seqs * a.num_kv_heads) return false;
+  const int32_t r = k - (k / per_group) * per_group;
+  it->part = r / a.col_tiles;
+  it->tile = r - it->part * a.col_tiles;
+  const int32_t srank = g / a.num_kv_heads;
+  it->kvh = g - srank * a.num_kv_heads;
+  it->b = seq_of_rank(a, srank, lane);
+  return it->b >= 0;
+}
+
 // The sequence's rows and the tile's columns.  Returns false when nothing may be
 // written (rows outside [0, total]) or the tile holds no column.
 struct ChunkSeq {
@@ -133,7 +227,7 @@ void chunk_attn_kernel(ChunkArgs a) {
   __shared__ int s_bad;
 
   ChunkItem it;
-  if (!chunk_item(a, a.parts, &it)) return;
+  if (!chunk_item_ordered(a, threadIdx.x & 63, &it)) return;
   ChunkSeq sq;
   if (!chunk_seq<NT * kCols>(a, it, &sq)) return;
   const int32_t b = __builtin_amdgcn_readfirstlane(it.b);
@@ -171,6 +265,16 @@ void chunk_attn_kernel(ChunkArgs a) {
     return;
   }
 
+  // The wave's blocks: first, first + 4, ... below jend.  The ids of the first run
+  // of 64 are requested before the q fragments (whose LDS store ends in a barrier).
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t jbeg = part * pblocks;
+  const int32_t jend = min(nblk_t, jbeg + pblocks);
+  const int32_t first = jbeg + w;
+  const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
+  int32_t ids0 = 0;
+  if (lane < min(64, nw)) ids0 = bt[first + kWaves * lane];
+
   // This lane's column in tile t: token ti of the chunk, head gh of the group,
   // position pos[t].  Padding columns load zero q and mask nothing.
   int32_t pos[NT];
@@ -197,11 +301,6 @@ void chunk_attn_kernel(ChunkArgs a) {
   }
   if constexpr (kQLds) __syncthreads();
 
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
-  const int32_t jbeg = part * pblocks;
-  const int32_t jend = min(nblk_t, jbeg + pblocks);
-  const int32_t first = jbeg + w;
-  const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
@@ -307,8 +406,12 @@ void chunk_attn_kernel(ChunkArgs a) {
 
   for (i0 = 0; i0 < nw; i0 += 64) {
     cnt = min(64, nw - i0);
-    ids = 0;
-    if (lane < cnt) ids = bt[first + kWaves * (i0 + lane)];
+    if (i0 == 0) {
+      ids = ids0;
+    } else {
+      ids = 0;
+      if (lane < cnt) ids = bt[first + kWaves * (i0 + lane)];
+    }
     const bool id_bad = lane < cnt && (ids < 0 || ids >= a.num_blocks);
     if (id_bad) ids = 0;
     bad_blk = bad_blk || __ballot(id_bad) != 0;
