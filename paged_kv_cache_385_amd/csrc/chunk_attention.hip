@@ -170,9 +170,14 @@ __device__ int32_t seq_of_rank(const ChunkArgs& a, int32_t r, int32_t lane) {
   return -1;    // not reached: the classes count every sequence
 }
 // chunk_item with the groups taken in largest-first order of their sequences: group
-// rank g = (sequence rank) * Hkv + KV head, placed on XCD g % 8 as above.
+// rank g = (sequence rank) * Hkv + KV head, placed on XCD g % 8 as above.  The
+// order costs every workgroup two passes over the lengths, so batches of more than
+// kMaxOrderedSeqs sequences (many items per slot, which balance by themselves)
+// keep the plain order.
+constexpr int32_t kMaxOrderedSeqs = 1024;
 __device__ __forceinline__ bool chunk_item_ordered(const ChunkArgs& a, int32_t lane,
                                                    ChunkItem* it) {
+  if (a.num_seqs > kMaxOrderedSeqs) return chunk_item(a, a.parts, it);
   const int32_t per_group = a.col_tiles * a.parts;
   const int32_t x = blockIdx.x & 7;
   const int32_t k = blockIdx.x >> 3;

@@ -268,20 +268,21 @@ def test_single_partition_sequences_bypass_the_merge():
     check_close(out, ref, wl.dtype, label="direct and merged")
 
 
-@pytest.mark.parametrize("H,q_max", [(8, 4), (32, 9)])
-def test_many_sequences_in_largest_first_order(H, q_max):
-    """300 sequences of mixed lengths: the workgroups take the sequences longest first
-    (a counting sort over 16 length classes, past the 256 lengths kept in registers);
-    every row of every sequence compared.  H=8 over 2 KV heads runs the narrow kernel,
-    H=32 with up to 9 new tokens (144 columns) the wide one."""
-    rng = np.random.default_rng(H)
-    ctx = rng.integers(1, 600, size=300)
-    q_lens = np.minimum(rng.integers(1, q_max + 1, size=300), ctx)
+@pytest.mark.parametrize("B,H,q_max", [(300, 8, 4), (300, 32, 9), (1100, 8, 4)])
+def test_many_sequences_in_largest_first_order(B, H, q_max):
+    """Many sequences of mixed lengths; every row of every sequence compared.  H=8 over 2
+    KV heads runs the narrow kernel, whose workgroups take the sequences longest first
+    (a counting sort over 16 length classes; 300 goes past the 256 lengths kept in
+    registers, 1100 past the batch size up to which the order is kept).  H=32 with up
+    to 9 new tokens (144 columns) runs the wide kernel."""
+    rng = np.random.default_rng(H + B)
+    ctx = rng.integers(1, 600 if B < 1000 else 200, size=B)
+    q_lens = np.minimum(rng.integers(1, q_max + 1, size=B), ctx)
     q_lens[:3] = np.minimum(q_max, ctx[:3])
     wl = custom_workload(list(ctx), H, 2, 64, dtype="f16", seed=H + 1)
-    say(f"300 sequences, H={H}, up to {q_max} new tokens")
+    say(f"{B} sequences, H={H}, up to {q_max} new tokens")
     cache, segs, tables, ctx_d = _cache_with_context(wl)
     q, starts, out = _run(wl, cache, tables, ctx_d, q_lens)
     assert not torch.isnan(out).any()
     ref = _oracle(wl, segs, q, starts, range(len(ctx)))
-    check_close(out, ref, wl.dtype, label=f"300 sequences, H={H}")
+    check_close(out, ref, wl.dtype, label=f"{B} sequences, H={H}")
