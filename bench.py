@@ -181,14 +181,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def blas_threads() -> int:
+    """Threads the oracle's numpy products may use (the largest BLAS pool)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return 1
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle, as it stands, on the first sequences of the workload until the budget is spent."""
     from oracle import attention as OA
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     q = wl.q()
     t_total, kv_bytes, seqs = 0.0, 0, 0
     per_tok = 2 * wl.num_kv_heads * wl.head_dim * 2
@@ -335,7 +340,7 @@ def run_chunk(args):
             done_f += chunk_flops([wl.ctx_lens[bb]], [n], H, D)
             b += 1
         cpu = done_b / t_total / 1e9 if unit == "GB/s" else done_f / t_total / 1e12
-        result["cpu_baseline"] = {"value": cpu, "unit": unit, "cores": 1, "kind": "oracle",
+        result["cpu_baseline"] = {"value": cpu, "unit": unit, "cores": blas_threads(), "kind": "oracle",
                                   "sample": f"{b} sequences' chunks, float64 numpy, {t_total:.1f} s"}
     print(json.dumps(result), flush=True)
 
@@ -507,11 +512,7 @@ def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
     its attention computes each admitted request's new tokens (float64 numpy)."""
     from oracle import attention as OA
     from oracle.prefix_cache import RefPrefixCache
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     B = len(prompts)
     nb = B * (-(-max(len(p) for p in prompts) // 16) + 1)
     ref = RefPrefixCache(nb)
