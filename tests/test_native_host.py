@@ -148,6 +148,22 @@ def test_chunk_call_validation():
                                   None, 0, None) == N.PA_ERR_INVALID_ARG
     # enough column tiles to fill the device: no partitions, no workspace
     assert lib.pa_chunk_workspace_size(64, 64, 8, 128, 64 * 1024, 1024, 4096) == 0
+
+    # Key partition length (no device here: 256 compute units assumed).  Workspace =
+    # (max, sum) float2 per (row, partition), rounded up to 256 bytes, then a float row
+    # of D per (row, partition).
+    def ws(rows, P, D):
+        ml = rows * P * 8
+        return ((ml + 255) // 256) * 256 + rows * P * D * 4
+    # 128 sequences x 8 KV heads, 48 columns each (one group of three tiles): 1024 items
+    # at 4096 tokens still give the 512 slots two each, so 4096-token partitions.
+    assert lib.pa_chunk_workspace_size(128, 64, 8, 128, 768, 6, 4096) == 0      # one partition
+    assert lib.pa_chunk_workspace_size(128, 64, 8, 128, 768, 6, 4097) == ws(768 * 64, 2, 128)
+    # 4 sequences, 64 columns (two groups): 8 items, too few for longer partitions: 1024
+    assert lib.pa_chunk_workspace_size(4, 8, 1, 128, 22, 8, 4000) == ws(22 * 8, 4, 128)
+    # 256 sequences x 2 KV heads, 16 columns, head dim 64 (three workgroups per unit,
+    # 768 slots): 512 items x ceil(5000 / 2048) = 1536 >= 1536 -> 2048-token partitions
+    assert lib.pa_chunk_workspace_size(256, 16, 2, 64, 512, 2, 5000) == ws(512 * 16, 3, 64)
     assert lib.pa_chunk_workspace_size(2, 3, 2, 128, 12, 6, 3000) == 0   # invalid heads
 
 
