@@ -247,7 +247,10 @@ def run_chunk(args):
     K, W = args.steps, args.warmup
     log(f"chunk {args.chunk}: {name}; total new tokens {int(q_lens.sum())}")
     t0 = time.perf_counter()
-    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order)
+    fp8 = args.kv_dtype == "fp8"
+    kv_scales = (np.full(Hkv, 0.0125, np.float32), np.full(Hkv, 0.0125, np.float32)) if fp8 else None
+    cache = pa.PagedKVCache(wl.num_blocks, Hkv, D, wl.dtype, dev, free_order=wl.free_order,
+                            kv_scales=kv_scales)
     segs = {}
 
     def tokens(seg, start, n):
@@ -276,7 +279,7 @@ def run_chunk(args):
 
     def call():
         pa.chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, ctx_d, mq, max_ctx,
-                           wl.scale, out=out, workspace=ws if need else None)
+                           wl.scale, out=out, workspace=ws if need else None, scales=cache.scales)
 
     for _ in range(W):
         call()
@@ -293,7 +296,7 @@ def run_chunk(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    per_tok = 2 * Hkv * D * 2
+    per_tok = 2 * Hkv * D * (1 if fp8 else 2)     # K and V bytes per cached token
     kv_bytes = int(wl.ctx_lens.sum()) * per_tok
     io_bytes = 2 * int(q_lens.sum()) * H * D * 2 + int((-(-wl.ctx_lens // 16)).sum()) * 4 + 8 * B
     flops = chunk_flops(wl.ctx_lens, q_lens, H, D)
@@ -309,8 +312,8 @@ def run_chunk(args):
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFS, 4)}
     kname = "chunk_wide_kernel" if mq * (H // Hkv) >= 128 else "chunk_attn_kernel"
-    roof.update({"traffic": recorded_traffic(args, K, W),
-                 "kernel": f"{kname}<{wl.dtype_name.upper()},{D}>"
+    roof.update({"traffic": None if fp8 else recorded_traffic(args, K, W),
+                 "kernel": f"{kname}<{wl.dtype_name.upper()},{D}" + (",FP8>" if fp8 else ">")
                  + (" + chunk_merge_kernel" if need else ""),
                  "avg_launch_us": round(us, 2), "bytes_per_launch": kv_bytes + io_bytes,
                  "flops_per_launch": flops})
@@ -318,7 +321,8 @@ def run_chunk(args):
               "warmup": W, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype_name, "data": "synthetic",
               "config": {"workload": name, "batch": B, "num_heads": H, "num_kv_heads": Hkv,
-                         "head_dim": D, "block_size": 16, "kv_dtype": wl.dtype_name,
+                         "head_dim": D, "block_size": 16,
+                         "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype_name,
                          "new_tokens": int(q_lens.sum()), "max_new_tokens": mq,
                          "mean_context": round(float(wl.ctx_lens.mean()), 1)},
               "roofline": roof}

@@ -85,8 +85,9 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
  * the KV cache can be kept quantised, FP8 among the formats ("理解 vLLM
  * PagedAttention", version matrix, row "量化"); the format, the per-head scales
  * and the rounding are this library's reading.  dtype stays the dtype of q,
- * out and of the k / v given to pa_cache_write.  pa_chunk_attention does not
- * take FP8 pools (PA_ERR_UNSUPPORTED). */
+ * out and of the k / v given to pa_cache_write.  The attention calls widen the
+ * codes exactly to dtype and fold k_scales into the score scale and v_scales
+ * into the output. */
 #define PA_CACHE_FP8 2
 
 /* A KV pool pair.  k_cache and v_cache are device pointers in the layout above,
@@ -473,8 +474,9 @@ pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t d
  * or the tokens of a speculative verify ("vLLM 核心概念", section "推测解码
  * （Speculative Decoding）"); with q_len 1 it is the decode of pa_decode.  The new
  * tokens' K/V must be in the cache already (pa_cache_write).
- *   q, out           device, [total_q][num_heads][head_dim], cache dtype, 16-byte
- *                    aligned; sequence b owns rows q_starts[b] .. q_starts[b+1].
+ *   q, out           device, [total_q][num_heads][head_dim], cache dtype (FP8
+ *                    pools: the descriptor's dtype), 16-byte aligned; sequence b
+ *                    owns rows q_starts[b] .. q_starts[b+1].
  *   q_starts         device, int32[num_seqs + 1], non-decreasing, q_starts[0] >= 0,
  *                    q_starts[num_seqs] <= total_q; every q_len at most max_q_len
  *                    (rows past max_q_len of a longer one are not written).

@@ -64,6 +64,8 @@ struct ChunkArgs {
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* ctx_lens;      // [B]
   uint16_t* out;                // [total][H][D]
+  const float* k_scales;        // FP8 pools: per-KV-head scales of K and V, else unused
+  const float* v_scales;
   float2* ws_ml;                // [total][H][P] (max in log2 units, sum), when P > 1
   float* ws_acc;                // [total][H][P][D] unnormalised output
   int32_t num_seqs, total, num_heads, num_kv_heads, group;
@@ -218,10 +220,12 @@ __device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& i
 // head) reads each tile once.  Three tiles at head dim 128 keep their q fragments
 // in LDS (the registers hold the accumulators and two blocks of K/V).  kStream:
 // each tile is read by one workgroup only, so the loads are non-temporal.
-template <class E, int D, int NT, bool kStream>
+template <class E, int D, int NT, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT * D > 192 ? 2 : 3)))
 void chunk_attn_kernel(ChunkArgs a) {
   constexpr int KK = D / 32;
+  constexpr int LW = kFp8 ? KK / 2 : KK;   // 16-byte loads per lane per tile (FP8: half)
+  constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * (kFp8 ? 1 : 2);
   constexpr int MT = D / 16;
   constexpr int kLdsStride = D + 4;
   constexpr bool kQLds = NT * D > 256;
@@ -306,9 +310,11 @@ void chunk_attn_kernel(ChunkArgs a) {
   }
   if constexpr (kQLds) __syncthreads();
 
-  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
-  const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
-  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const int64_t head_off_b = static_cast<int64_t>(kvh) * kTileBytes;
+  const int64_t blk_stride_b = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
+  // FP8 pools: the K scale folds into the score scale, the V scale into the output
+  const float score_scale = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
+  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
 
   bool bad_blk = false;
   float m_run[NT], l_run[NT];
@@ -320,7 +326,7 @@ void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  u32x4 kb[2][KK], vb[2][KK];
+  u32x4 kb[2][LW], vb[2][LW];     // 16-bit pools: the operands themselves; FP8: raw codes
   // The wave's blocks go in runs of up to 64: lane i holds the id of the run's i-th.
   int32_t ids = 0, i0 = 0, cnt = 0;
 
@@ -330,17 +336,42 @@ void chunk_attn_kernel(ChunkArgs a) {
   // caches; with one (kStream) it is read once.
   auto load_block = [&](int buf, int32_t i) {
     const int32_t phys = __builtin_amdgcn_readlane(ids, min(i, cnt - 1));
-    const int32_t bytes = i < cnt ? static_cast<int32_t>(tile_elems * sizeof(uint16_t)) : 0;
-    const auto kr = tile_rsrc(a.k_cache + phys * blk_stride + head_off, bytes);
-    const auto vr = tile_rsrc(a.v_cache + phys * blk_stride + head_off, bytes);
+    const int32_t bytes = i < cnt ? static_cast<int32_t>(kTileBytes) : 0;
+    const auto kr = tile_rsrc(reinterpret_cast<const char*>(a.k_cache) + phys * blk_stride_b + head_off_b, bytes);
+    const auto vr = tile_rsrc(reinterpret_cast<const char*>(a.v_cache) + phys * blk_stride_b + head_off_b, bytes);
+    if constexpr (kFp8) {
+      // the decode pass's FP8 operand loads: K dims 64pp + 8g4 .. +7 and 64pp + 32 +
+      // 8g4 .. +7 of token n; V dims (64qq + 2n, +1) and (64qq + 32 + 2n, +1) of
+      // tokens 4g4 .. +3
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
+      for (int pp = 0; pp < LW; ++pp) kb[buf][pp] = load_tile<kStream>(kr, ((pp * 16 + n) * 4 + g4) * 16);
 #pragma unroll
-    for (int j2 = 0; j2 < KK; ++j2)
-      vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+      for (int qq = 0; qq < LW; ++qq)
+        vb[buf][qq] = load_tile<kStream>(vr, ((g4 * (D / 64) + qq) * 16 + n) * 16);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kb[buf][kk] = load_tile<kStream>(kr, (kk * 64 + lane) * 16);
+#pragma unroll
+      for (int j2 = 0; j2 < KK; ++j2)
+        vb[buf][j2] = load_tile<kStream>(vr, ((g4 * D) + 32 * j2 + 2 * n) * 8);
+    }
   };
 
   auto compute_block = [&](int buf, int32_t i) {
+    // the block's operands: the loaded registers, or the FP8 codes widened exactly
+    u32x4 K[KK], V[KK];
+#pragma unroll
+    for (int t = 0; t < LW; ++t) {
+      if constexpr (kFp8) {
+        K[2 * t] = widen_fp8<E>(kb[buf][t][0], kb[buf][t][1]);
+        K[2 * t + 1] = widen_fp8<E>(kb[buf][t][2], kb[buf][t][3]);
+        V[2 * t] = widen_fp8<E>(vb[buf][t][0], vb[buf][t][1]);
+        V[2 * t + 1] = widen_fp8<E>(vb[buf][t][2], vb[buf][t][3]);
+      } else {
+        K[t] = kb[buf][t];
+        V[t] = vb[buf][t];
+      }
+    }
     f32x4 s[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -352,7 +383,7 @@ void chunk_attn_kernel(ChunkArgs a) {
           qv = s_q[(t * KK + kk) * 64 + lane];
         else
           qv = qf[t][kk];
-        s[t] = E::mfma_qk(kb[buf][kk], qv, s[t]);
+        s[t] = E::mfma_qk(K[kk], qv, s[t]);
       }
     }
     const int32_t t0 = (first + kWaves * (i0 + i)) * kBlock; // position of the block's token 0
@@ -361,11 +392,11 @@ void chunk_attn_kernel(ChunkArgs a) {
       // positions past the context may hold anything (NaN included): zero their V
 #pragma unroll
       for (int j2 = 0; j2 < KK; ++j2) {
-        u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+        u16x8 vv = __builtin_bit_cast(u16x8, V[j2]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (4 * g4 + (e & 3) >= valid) vv[e] = 0;
-        vb[buf][j2] = __builtin_bit_cast(u32x4, vv);
+        V[j2] = __builtin_bit_cast(u32x4, vv);
       }
     }
 #pragma unroll
@@ -374,7 +405,7 @@ void chunk_attn_kernel(ChunkArgs a) {
       float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[r] = s[t][r] * a.scale_log2;
+        sv[r] = s[t][r] * score_scale;
         if (4 * g4 + r > seen) sv[r] = -INFINITY;
       }
       float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -400,7 +431,7 @@ void chunk_attn_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int j2 = 0; j2 < KK; ++j2) {
-        const u16x8 vv = __builtin_bit_cast(u16x8, vb[buf][j2]);
+        const u16x8 vv = __builtin_bit_cast(u16x8, V[j2]);
         const u16x4 lo = {vv[0], vv[1], vv[2], vv[3]};
         const u16x4 hi = {vv[4], vv[5], vv[6], vv[7]};
         acc[t][2 * j2] = E::mfma_pv(lo, pb, acc[t][2 * j2]);
@@ -450,7 +481,7 @@ void chunk_attn_kernel(ChunkArgs a) {
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[t][v][n]);
-    const float wscale = fast_exp2(m_run[t] - (M == -INFINITY ? 0.f : M));
+    const float wscale = fast_exp2(m_run[t] - (M == -INFINITY ? 0.f : M)) * out_scale;
     {
       float* row = &s_acc[w][n * kLdsStride];
 #pragma unroll
@@ -506,14 +537,19 @@ void chunk_attn_kernel(ChunkArgs a) {
 constexpr int kWideCols = 128;                // columns per workgroup of the wide kernel
 constexpr int kWaveCols = kWideCols / kWaves; // 32 per wave: two groups of 16
 
-template <class E, int D>
+template <class E, int D, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void chunk_wide_kernel(ChunkArgs a) {
   constexpr int KK = D / 32;                 // 32-dim steps of q.K^T
   constexpr int MT = D / 16;                 // 16-dim tiles of the output
   constexpr int kTileElems = kBlock * D;     // one block's K (or V) tile
-  constexpr int kKChunks = 2 * kTileElems / 8 / kThreads;   // 16-byte K pieces per thread
+  constexpr int kTileBytes = kTileElems * (kFp8 ? 1 : 2);
+  // 16-byte pieces of a stage's K per thread (FP8: 16 codes a piece; at head dim 64
+  // only the first two waves hold one)
+  constexpr int kKChunks = kFp8 ? 1 : 2 * kTileElems / 8 / kThreads;
+  constexpr int kKPieces8 = 2 * kTileElems / 16;              // FP8 K pieces of a stage
   constexpr int kVPairs = 2 * D;             // (token quad, dim pair) pieces of a stage's V
+  constexpr int kVPieces8 = kTileElems / 16; // FP8 V pieces of one block
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][2 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][2 * kTileElems];
 
@@ -576,8 +612,13 @@ void chunk_wide_kernel(ChunkArgs a) {
   const int32_t jbeg = part * pblocks;
   const int32_t jend = min(nblk_t, jbeg + pblocks);
   const int32_t nstage = (jend - jbeg + 1) / 2;
-  const int64_t head_off = static_cast<int64_t>(kvh) * kTileElems;
-  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * kTileElems;
+  const int64_t head_off_b = static_cast<int64_t>(kvh) * kTileBytes;
+  const int64_t blk_stride_b = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
+  // FP8 pools: the K scale folds into the score scale, the V scale into the output
+  const float score_scale = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
+  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
 
   // block ids in runs of 64: lane i holds the id of block jbeg + 64 r + i
   int32_t ids = 0;
@@ -603,49 +644,91 @@ void chunk_wide_kernel(ChunkArgs a) {
     const int32_t l0 = (2 * st) & 63;                        // index within the id run
     const int32_t p0 = __builtin_amdgcn_readlane(ids, l0);
     const int32_t p1 = __builtin_amdgcn_readlane(ids, l0 + 1);
-    const int32_t bytes0 = j0 < jend ? kTileElems * 2 : 0;
-    const int32_t bytes1 = j0 + 1 < jend ? kTileElems * 2 : 0;
+    const int32_t bytes0 = j0 < jend ? kTileBytes : 0;
+    const int32_t bytes1 = j0 + 1 < jend ? kTileBytes : 0;
+    const int32_t wp = __builtin_amdgcn_readfirstlane(w * 64);
+    if constexpr (kFp8) {
+      // K: FP8 piece tid % (kKPieces8 / 2) of block tid / (kKPieces8 / 2); V: FP8 piece
+      // tid < kVPieces8 of both blocks.  Waves past the pieces read empty ranges.
+      const bool second = wp >= kKPieces8 / 2;
+      const int32_t kbytes = wp < kKPieces8 ? (second ? bytes1 : bytes0) : 0;
+      const auto kr = tile_rsrc(kc + (second ? p1 : p0) * blk_stride_b + head_off_b, kbytes);
+      kst[0] = load_tile<false>(kr, (tid % (kKPieces8 / 2)) * 16);
+      const int32_t vb = wp < kVPieces8 ? 1 : 0;
+      const auto v0 = tile_rsrc(vc + p0 * blk_stride_b + head_off_b, bytes0 * vb);
+      const auto v1 = tile_rsrc(vc + p1 * blk_stride_b + head_off_b, bytes1 * vb);
+      vst[0] = load_tile<false>(v0, tid * 16);
+      vst[1] = load_tile<false>(v1, tid * 16);
+    } else {
 #pragma unroll
-    for (int c = 0; c < kKChunks; ++c) {
-      // the wave's 64 pieces all lie in one block's tile (a tile is 128 or 256 pieces)
-      const int32_t wpiece = __builtin_amdgcn_readfirstlane(w * 64 + c * kThreads);
-      const bool second = wpiece >= kTileElems / 8;
-      const auto kr = tile_rsrc(a.k_cache + (second ? p1 : p0) * blk_stride + head_off,
-                                second ? bytes1 : bytes0);
-      kst[c] = load_tile<false>(kr, ((tid + c * kThreads) % (kTileElems / 8)) * 16);
+      for (int c = 0; c < kKChunks; ++c) {
+        // the wave's 64 pieces all lie in one block's tile (a tile is 128 or 256 pieces)
+        const int32_t wpiece = __builtin_amdgcn_readfirstlane(w * 64 + c * kThreads);
+        const bool second = wpiece >= kTileElems / 8;
+        const auto kr = tile_rsrc(kc + (second ? p1 : p0) * blk_stride_b + head_off_b,
+                                  second ? bytes1 : bytes0);
+        kst[c] = load_tile<false>(kr, ((tid + c * kThreads) % (kTileElems / 8)) * 16);
+      }
+      // V: pieces tid < 2 D of both blocks (whole waves: 2 D is a multiple of 64); the
+      // other waves read an empty range
+      const int32_t vb = wp < kVPairs ? 1 : 0;
+      const auto v0 = tile_rsrc(vc + p0 * blk_stride_b + head_off_b, bytes0 * vb);
+      const auto v1 = tile_rsrc(vc + p1 * blk_stride_b + head_off_b, bytes1 * vb);
+      vst[0] = load_tile<false>(v0, tid * 16);
+      vst[1] = load_tile<false>(v1, tid * 16);
     }
-    // V: pieces tid < 2 D of both blocks (whole waves: 2 D is a multiple of 64); the
-    // other waves read an empty range
-    const int32_t vb = __builtin_amdgcn_readfirstlane(w * 64) < kVPairs ? 1 : 0;
-    const auto v0 = tile_rsrc(a.v_cache + p0 * blk_stride + head_off, bytes0 * vb);
-    const auto v1 = tile_rsrc(a.v_cache + p1 * blk_stride + head_off, bytes1 * vb);
-    vst[0] = load_tile<false>(v0, tid * 16);
-    vst[1] = load_tile<false>(v1, tid * 16);
+  };
+  // (token quad tq, dims d and d + 1, 4 tokens each) of the stage's two blocks into the
+  // interleaved V layout, positions past the context zeroed (they may hold anything,
+  // NaN included)
+  auto store_v = [&](int32_t st, int buf, int32_t tq, int32_t d, u16x8 x0, u16x8 x1) {
+    const int32_t t0 = (jbeg + 2 * st) * kBlock + 4 * tq;   // position of the quad's token 0
+    if ((jbeg + 2 * st + 2) * kBlock > ctx) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (t0 + (e & 3) >= ctx) x0[e] = 0;
+        if (t0 + kBlock + (e & 3) >= ctx) x1[e] = 0;
+      }
+    }
+    const u16x8 lo = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    const u16x8 hi = {x0[4], x0[5], x0[6], x0[7], x1[4], x1[5], x1[6], x1[7]};
+    uint16_t* dst = &s_v[buf][(tq * D + d) * 8];
+    *reinterpret_cast<u16x8*>(dst) = lo;
+    *reinterpret_cast<u16x8*>(dst + 8) = hi;
   };
   auto stage_store = [&](int32_t st, int buf, const KRegs& kst, const VRegs& vst) {
-#pragma unroll
-    for (int c = 0; c < kKChunks; ++c)
-      *reinterpret_cast<u32x4*>(&s_k[buf][(tid + c * kThreads) * 8]) = kst[c];
-    if (tid < kVPairs) {
-      // piece tid holds token quad tq, dims d and d + 1, 4 tokens each, of one block
-      const int32_t tq = tid / (D / 2);
-      const int32_t d = 2 * (tid - tq * (D / 2));
-      const int32_t t0 = (jbeg + 2 * st) * kBlock + 4 * tq;   // position of the quad's token 0
-      u16x8 x0 = __builtin_bit_cast(u16x8, vst[0]);
-      u16x8 x1 = __builtin_bit_cast(u16x8, vst[1]);
-      // positions past the context may hold anything (NaN included): zero their V
-      if ((jbeg + 2 * st + 2) * kBlock > ctx) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (t0 + (e & 3) >= ctx) x0[e] = 0;
-          if (t0 + kBlock + (e & 3) >= ctx) x1[e] = 0;
-        }
+    if constexpr (kFp8) {
+      // K piece: dims 64pp + 8g8 .. +7 and 64pp + 32 + 8g8 .. +7 of token n8, widened
+      // exactly and stored where the 16-bit layout keeps them
+      if (tid < kKPieces8) {
+        const int32_t blk = tid / (kKPieces8 / 2);
+        const int32_t p8 = tid - blk * (kKPieces8 / 2);
+        const int32_t g8 = p8 & 3, n8 = (p8 >> 2) & 15, pp = p8 >> 6;
+        uint16_t* kt = &s_k[buf][blk * kTileElems];
+        *reinterpret_cast<u32x4*>(kt + ((8 * pp + g8) * 16 + n8) * 8) =
+            widen_fp8<E>(kst[0][0], kst[0][1]);
+        *reinterpret_cast<u32x4*>(kt + ((8 * pp + 4 + g8) * 16 + n8) * 8) =
+            widen_fp8<E>(kst[0][2], kst[0][3]);
       }
-      const u16x8 lo = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      const u16x8 hi = {x0[4], x0[5], x0[6], x0[7], x1[4], x1[5], x1[6], x1[7]};
-      uint16_t* dst = &s_v[buf][(tq * D + d) * 8];
-      *reinterpret_cast<u16x8*>(dst) = lo;
-      *reinterpret_cast<u16x8*>(dst + 8) = hi;
+      // V piece: dims (64qq + 2n, +1) and (64qq + 32 + 2n, +1) of token quad tq
+      if (tid < kVPieces8) {
+        const int32_t nv = tid & 15, qq = (tid >> 4) % (D / 64), tq = (tid >> 4) / (D / 64);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          store_v(st, buf, tq, 64 * qq + 32 * h + 2 * nv,
+                  __builtin_bit_cast(u16x8, widen_fp8<E>(vst[0][2 * h], vst[0][2 * h + 1])),
+                  __builtin_bit_cast(u16x8, widen_fp8<E>(vst[1][2 * h], vst[1][2 * h + 1])));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kKChunks; ++c)
+        *reinterpret_cast<u32x4*>(&s_k[buf][(tid + c * kThreads) * 8]) = kst[c];
+      if (tid < kVPairs) {
+        // piece tid holds token quad tq, dims d and d + 1, 4 tokens each, of one block
+        const int32_t tq = tid / (D / 2);
+        store_v(st, buf, tq, 2 * (tid - tq * (D / 2)), __builtin_bit_cast(u16x8, vst[0]),
+                __builtin_bit_cast(u16x8, vst[1]));
+      }
     }
   };
 
@@ -684,7 +767,7 @@ void chunk_wide_kernel(ChunkArgs a) {
     const int32_t t0 = (jbeg + 2 * st) * kBlock;   // position of the stage's first key
     // a stage wholly at or before the tile's first position needs no causal mask
     const bool diag = t0 + 2 * kBlock - 1 > pmin;
-    const float c = a.scale_log2;
+    const float c = score_scale;
     u32x4 pf[2];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
@@ -759,7 +842,7 @@ void chunk_wide_kernel(ChunkArgs a) {
     const float L = col_sum4(l_run[gi]);
     if (!col_ok[gi]) continue;
     if (direct) {
-      const float inv = 1.f / L;
+      const float inv = out_scale / L;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         u16x4 ov;
@@ -771,7 +854,7 @@ void chunk_wide_kernel(ChunkArgs a) {
       const int64_t st = hrow[gi] * a.parts + part;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const f32x4 o = bad_blk ? f32x4{NAN, NAN, NAN, NAN} : acc[gi][t];
+        const f32x4 o = bad_blk ? f32x4{NAN, NAN, NAN, NAN} : acc[gi][t] * out_scale;
         *reinterpret_cast<f32x4*>(a.ws_acc + st * D + 16 * t + 4 * g4) = o;
       }
       if (g4 == 0) a.ws_ml[st] = bad_blk ? float2{0.f, NAN} : float2{m_run[gi], L};
@@ -870,26 +953,26 @@ ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, 
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <class E, int D, bool kStream>
+template <class E, int D, bool kStream, bool kFp8>
 void launch_narrow(const ChunkArgs& a, int32_t nt, dim3 grid, hipStream_t s) {
   if (nt == 1)
-    chunk_attn_kernel<E, D, 1, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+    chunk_attn_kernel<E, D, 1, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
   else if (nt == 2)
-    chunk_attn_kernel<E, D, 2, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+    chunk_attn_kernel<E, D, 2, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
   else
-    chunk_attn_kernel<E, D, 3, kStream><<<grid, dim3(kThreads), 0, s>>>(a);
+    chunk_attn_kernel<E, D, 3, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
 }
 
-template <class E, int D>
+template <class E, int D, bool kFp8>
 void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, bool stream,
                     hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(groups8 * p.tiles * p.parts));
   if (p.wide)
-    chunk_wide_kernel<E, D><<<grid, dim3(kThreads), 0, s>>>(a);
+    chunk_wide_kernel<E, D, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
   else if (stream)
-    launch_narrow<E, D, true>(a, p.nt, grid, s);
+    launch_narrow<E, D, true, kFp8>(a, p.nt, grid, s);
   else
-    launch_narrow<E, D, false>(a, p.nt, grid, s);
+    launch_narrow<E, D, false, kFp8>(a, p.nt, grid, s);
   if (p.parts > 1) {
     ChunkArgs m = a;                     // the merge works in 16-column tiles
     m.col_tiles = p.merge_tiles;
@@ -899,12 +982,19 @@ void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, boo
 }
 
 template <class E>
-void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, bool stream,
-                  hipStream_t s) {
-  if (d == 64)
-    launch_chunk_d<E, 64>(a, p, groups8, stream, s);
-  else
-    launch_chunk_d<E, 128>(a, p, groups8, stream, s);
+void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, bool fp8,
+                  bool stream, hipStream_t s) {
+  if (d == 64) {
+    if (fp8)
+      launch_chunk_d<E, 64, true>(a, p, groups8, stream, s);
+    else
+      launch_chunk_d<E, 64, false>(a, p, groups8, stream, s);
+  } else {
+    if (fp8)
+      launch_chunk_d<E, 128, true>(a, p, groups8, stream, s);
+    else
+      launch_chunk_d<E, 128, false>(a, p, groups8, stream, s);
+  }
 }
 
 }  // namespace
@@ -935,8 +1025,6 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   pa::clear_error();
   pa_status st = pa::check_cache(cache, fn);
   if (st != PA_OK) return st;
-  if (cache->flags & PA_CACHE_FP8)
-    return pa::fail(PA_ERR_UNSUPPORTED, "%s: FP8 pools are not supported here", fn);
   if (num_seqs < 0 || total_q < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d, total_q %d", fn, num_seqs, total_q);
   if (num_seqs == 0 || total_q == 0) return PA_OK;
@@ -972,6 +1060,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(cache->k_cache);
   a.v_cache = static_cast<const uint16_t*>(cache->v_cache);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
   a.q_starts = q_starts;
   a.block_tables = block_tables;
   a.ctx_lens = context_lens;
@@ -997,10 +1087,11 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   // one column group per (sequence, KV head) reads each tile once, unless blocks
   // are shared between sequences
   const bool once = plan.tiles == 1 && !(cache->flags & PA_CACHE_SHARED_BLOCKS);
+  const bool fp8 = (cache->flags & PA_CACHE_FP8) != 0;
   if (cache->dtype == PA_F16)
-    launch_chunk<F16>(a, plan, groups8, cache->head_dim, once, s);
+    launch_chunk<F16>(a, plan, groups8, cache->head_dim, fp8, once, s);
   else
-    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, once, s);
+    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, fp8, once, s);
   return pa::launch_status(fn);
 }
 

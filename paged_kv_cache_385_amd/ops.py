@@ -260,23 +260,25 @@ def chunk_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_
 
 def chunk_attention(k_cache, v_cache, q, q_starts, block_tables, context_lens, max_q_len: int,
                     max_context_len: int, scale: float, out=None, workspace=None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, scales=None) -> torch.Tensor:
     """pa_chunk_attention: the last q_len_b tokens of each sequence (rows q_starts[b] ..
     q_starts[b+1] of the packed q [total, H, D]) attend causally over its cache.
-    Returns out [total, H, D]; allocates the workspace when none is given."""
-    desc = cache_desc(k_cache, v_cache)
+    Returns out [total, H, D]; allocates the workspace when none is given.  FP8 pools
+    take ``scales`` = (k_scales, v_scales); q and out are then float16 or bfloat16."""
+    dt = _compute_dtype(k_cache, q)
+    desc = cache_desc(k_cache, v_cache, scales=scales, dtype=dt)
     dev = k_cache.device
     if q.dim() != 3 or q.shape[2] != desc.head_dim:
         raise ValueError(f"q must be [total, H, {desc.head_dim}], got {tuple(q.shape)}")
     T, H = int(q.shape[0]), int(q.shape[1])
     B = int(q_starts.shape[0]) - 1
-    _need(q, k_cache.dtype, dev, "q")
+    _need(q, dt, dev, "q")
     _need(q_starts, torch.int32, dev, "q_starts", (B + 1,))
     _need(block_tables, torch.int32, dev, "block_tables")
     _need(context_lens, torch.int32, dev, "context_lens", (B,))
     if out is None:
         out = torch.empty_like(q)
-    _need(out, k_cache.dtype, dev, "out", tuple(q.shape))
+    _need(out, dt, dev, "out", tuple(q.shape))
     need = chunk_workspace_size(B, H, desc.num_kv_heads, desc.head_dim, T, max_q_len,
                                 max_context_len)
     if workspace is None and need > 0:

@@ -119,3 +119,59 @@ def test_fp8_long_contexts_merge():
     out, _ = _step(wl, cache, segs)
     ref = _oracle_out(wl, segs, ks, vs, [0, 7])
     check_close(out, ref, wl.dtype, rows=np.array([0, 7]), label="fp8 workload 5")
+
+
+# ---- pa_chunk_attention on FP8 pools: several new tokens per sequence ----------------
+
+def _chunk_fp8(wl, q_lens, seqs, label):
+    """Every sequence holds its ctx_b tokens (set-up trace and step replayed as stores);
+    the last q_len_b of them are the queries.  Against the oracle's causal attention
+    over the dequantised K/V."""
+    from paged_kv_cache_385_amd import chunk_attention
+    ks, vs = _scales(wl)
+    cache, segs = _build(wl, ks, vs)
+    cache.apply_trace(wl.step, segs.tokens)
+    sids = [op[1] for op in wl.step]
+    tables, ctx_d, max_ctx = cache.tables(sids, -(-int(wl.ctx_lens.max()) // 16))
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    q = wl.chunk_q(q_lens)
+    starts = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    chunk_attention(cache.k_cache, cache.v_cache, q.cuda(), torch.from_numpy(starts).cuda(),
+                    tables, ctx_d, int(q_lens.max()), max_ctx, wl.scale, out=out,
+                    scales=cache.scales)
+    torch.cuda.synchronize()
+
+    def seq_kv(b):
+        k, v = wl.seq_kv(b, segs)
+        kq = OF.dequantize(OF.quantize(k.float().numpy(), ks[None, :, None]), ks[None, :, None])
+        vq = OF.dequantize(OF.quantize(v.float().numpy(), vs[None, :, None]), vs[None, :, None])
+        return kq, vq
+    ref = OA.chunk_batch(q, starts, seq_kv, wl.ctx_lens, wl.scale, seqs)
+    rows = np.concatenate([np.arange(starts[b], starts[b + 1]) for b in seqs])
+    check_close(out, ref, wl.dtype, rows=rows, label=label)
+
+
+def test_fp8_chunk_speculative_verify_shape():
+    """70B-shaped GQA-8 batch on FP8 pools, 6 new tokens per sequence: the narrow kernel,
+    three 16-column tiles per workgroup, non-temporal loads, sequences longest first."""
+    wl = make_workload(3)
+    say("FP8 pools, workload 3, 6 new tokens per sequence")
+    seqs = sorted(set([0, 1, int(np.argmax(wl.ctx_lens)), int(np.argmin(wl.ctx_lens))]
+                      + list(range(5, 128, 17))))
+    _chunk_fp8(wl, np.minimum(6, wl.ctx_lens), seqs, "fp8 verify, workload 3")
+
+
+@pytest.mark.parametrize("q_lens,H,Hkv,D,dt", [
+    ([300, 1024, 40, 1], 16, 2, 128, "bf16"),    # wide kernel (G=8): chunks, a whole prompt
+    ([40, 64, 7, 1], 16, 2, 64, "f16"),           # wide kernel at head dim 64
+    ([5, 3, 6, 2], 16, 2, 128, "f16"),            # narrow, three tiles, key partitions + merge
+    ([12, 10, 9, 11], 8, 2, 64, "bf16"),          # narrow, three tiles at head dim 64
+    ([1, 2, 1, 2], 4, 4, 128, "bf16"),            # narrow, one tile (MHA)
+])
+def test_fp8_chunks(q_lens, H, Hkv, D, dt):
+    from workloads import custom_workload
+    ctx = [700, 1500, 2100, 33]
+    wl = custom_workload(ctx, H, Hkv, D, dtype=dt, seed=H + D + q_lens[0])
+    say(f"FP8 pools, chunks {q_lens} over {ctx}, H={H} Hkv={Hkv} D={D} {dt}")
+    _chunk_fp8(wl, np.minimum(q_lens, ctx), range(len(ctx)), f"fp8 chunks H={H} D={D}")

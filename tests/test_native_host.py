@@ -83,9 +83,11 @@ def test_cache_flags_validation():
         c8 = _cache(flags=N.PA_CACHE_FP8, **kw)
         assert lib.pa_cache_write(C.byref(c8), FAKE, FAKE, FAKE, 4, None) == N.PA_ERR_INVALID_ARG
         assert b"scales" in lib.pa_last_error()
+    # pa_chunk_attention takes FP8 pools: this call passes the pool checks and stops at
+    # its missing workspace, before any launch
     c8 = _cache(flags=N.PA_CACHE_FP8, k_scales=FAKE, v_scales=FAKE)
     assert lib.pa_chunk_attention(C.byref(c8), FAKE, FAKE, 2, 12, 6, 4, FAKE, 200, FAKE, 3000, 0.1,
-                                  FAKE, None, 0, None) == N.PA_ERR_UNSUPPORTED
+                                  FAKE, None, 0, None) == N.PA_ERR_WORKSPACE
 
 
 @no_device
