@@ -484,7 +484,8 @@ pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t d
  *   workspace        device, >= pa_chunk_workspace_size(...) bytes, 16-byte aligned
  *                    (NULL when that size is 0).
  * One workgroup per (sequence, KV head, 16-48 (token, head) columns, key
- * partition), sequences taken longest first when there are at most 48 columns;
+ * partition), sequences taken longest first when there are at most 48 columns
+ * and the launch gives each workgroup slot at most 4 items;
  * when the column groups alone do not fill the device, keys are split
  * into partitions of 1024, 2048 or 4096 tokens (the longest that still gives
  * every workgroup slot two items).  A sequence whose context fits one partition

@@ -24,8 +24,9 @@
 // lane-local.  The 4 waves split a partition's blocks (every 4th) and combine in
 // LDS.  Every K/V tile a workgroup reads serves its 16-48 columns, which suits a
 // few new tokens per sequence (speculative verify) but makes long chunks L2-bound.
-// Its workgroups take the sequences longest first (a counting sort over classes
-// of context length), so the longest items do not start last.
+// When its launch gives each workgroup slot only a few items, its workgroups take
+// the sequences longest first (a counting sort over classes of context length),
+// so the longest items do not start last.
 //
 // chunk_wide_kernel: each wave owns 32 columns (two groups of 16) and all four
 // waves walk the same keys, two blocks (32 tokens) per stage, so a K/V tile
@@ -73,6 +74,7 @@ struct ChunkArgs {
   int32_t col_tiles;            // column groups per (sequence, KV head) in the grid
   int32_t parts;                // key partitions per column group in the grid (P)
   int32_t part_blocks;          // blocks per key partition when P > 1
+  int32_t ordered;              // narrow kernel: take the sequences longest first
   float scale_log2;             // scale * log2(e)
 };
 
@@ -173,13 +175,12 @@ __device__ int32_t seq_of_rank(const ChunkArgs& a, int32_t r, int32_t lane) {
 }
 // chunk_item with the groups taken in largest-first order of their sequences: group
 // rank g = (sequence rank) * Hkv + KV head, placed on XCD g % 8 as above.  The
-// order costs every workgroup two passes over the lengths, so batches of more than
-// kMaxOrderedSeqs sequences (many items per slot, which balance by themselves)
-// keep the plain order.
-constexpr int32_t kMaxOrderedSeqs = 1024;
+// order costs every workgroup two passes over the lengths, so the launch asks for
+// it (a.ordered) only when the slots get few items each; many items per slot
+// balance by themselves.
 __device__ __forceinline__ bool chunk_item_ordered(const ChunkArgs& a, int32_t lane,
                                                    ChunkItem* it) {
-  if (a.num_seqs > kMaxOrderedSeqs) return chunk_item(a, a.parts, it);
+  if (!a.ordered) return chunk_item(a, a.parts, it);
   const int32_t per_group = a.col_tiles * a.parts;
   const int32_t x = blockIdx.x & 7;
   const int32_t k = blockIdx.x >> 3;
@@ -921,7 +922,10 @@ struct ChunkPlan {
   int32_t merge_tiles;  // 16-column tiles of the merge launch
   int32_t parts;
   int32_t part_blocks;
+  bool ordered;         // narrow kernel, at most kOrderedItemsPerSlot items per slot
 };
+constexpr int64_t kOrderedItemsPerSlot = 4;
+constexpr int32_t kMaxOrderedSeqs = 1024;
 ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t max_q_len, int32_t max_ctx) {
   ChunkPlan p;
@@ -939,15 +943,17 @@ ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, 
   p.part_blocks = kMinPartTokens / kBlock;
   if (items >= (p.wide ? 1 : 8) * slots) {
     p.parts = 1;
-    return p;
+  } else {
+    for (int32_t pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2)
+      if (items * ((max_ctx + pt - 1) / pt) >= 2 * slots) {
+        p.part_blocks = pt / kBlock;
+        break;
+      }
+    const int32_t part_tokens = p.part_blocks * kBlock;
+    p.parts = (max_ctx + part_tokens - 1) / part_tokens;
   }
-  for (int32_t pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2)
-    if (items * ((max_ctx + pt - 1) / pt) >= 2 * slots) {
-      p.part_blocks = pt / kBlock;
-      break;
-    }
-  const int32_t part_tokens = p.part_blocks * kBlock;
-  p.parts = (max_ctx + part_tokens - 1) / part_tokens;
+  p.ordered = !p.wide && num_seqs <= kMaxOrderedSeqs &&
+              items * p.parts <= kOrderedItemsPerSlot * slots;
   return p;
 }
 
@@ -1082,6 +1088,7 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   a.col_tiles = plan.tiles;
   a.parts = P;
   a.part_blocks = plan.part_blocks;
+  a.ordered = plan.ordered ? 1 : 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one column group per (sequence, KV head) reads each tile once, unless blocks
