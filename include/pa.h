@@ -184,7 +184,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *   block_tables        device, int32[num_seqs][max_blocks_per_seq].
  *   context_lens        device, int32[num_seqs], each in [1, max_context_len].
  *   max_context_len     host bound on every context length, <= 16*max_blocks_per_seq.
- *   num_heads           a multiple of num_kv_heads, at most 16 per KV head.
+ *   num_heads           a multiple of num_kv_heads.  With more than 16 query heads
+ *                       per KV head (one matrix-core tile holds 16), the call runs
+ *                       the kernels of pa_chunk_attention with one query per
+ *                       sequence, their key-partition states in the workspace past
+ *                       its counters; pa_decode_fused then stores the new tokens in
+ *                       a launch of their own (slots stored as given), and
+ *                       pa_decode_attention does the whole computation, leaving
+ *                       nothing to pa_decode_merge.
  *   workspace           device, >= pa_decode_workspace_size(...) bytes, 16-byte
  *                       aligned, counters zero (may be NULL when that size is 0).
  * When every sequence has at most 8 partitions the merge runs inside the

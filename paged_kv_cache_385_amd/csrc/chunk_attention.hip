@@ -61,7 +61,7 @@ struct ChunkArgs {
   const uint16_t* q;            // [total][H][D]
   const uint16_t* k_cache;
   const uint16_t* v_cache;
-  const int32_t* q_starts;      // [B + 1]
+  const int32_t* q_starts;      // [B + 1], or NULL: sequence b's one query is row b
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* ctx_lens;      // [B]
   uint16_t* out;                // [total][H][D]
@@ -203,7 +203,9 @@ struct ChunkSeq {
 };
 template <int kTileCols = kCols>
 __device__ __forceinline__ bool chunk_seq(const ChunkArgs& a, const ChunkItem& it, ChunkSeq* s) {
-  const int32_t qs = a.q_starts[it.b], qe = a.q_starts[it.b + 1];
+  // no q_starts: one query per sequence, row b (decode with wide query groups)
+  const int32_t qs = a.q_starts ? a.q_starts[it.b] : it.b;
+  const int32_t qe = a.q_starts ? a.q_starts[it.b + 1] : it.b + 1;
   if (qs < 0 || qe < qs || qe > a.total) return false;
   s->qs = qs;
   s->n = qe - qs;
@@ -1005,30 +1007,15 @@ void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d
 
 }  // namespace
 
-extern "C" {
+namespace pa {
 
-size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                               int32_t head_dim, int32_t total_q, int32_t max_q_len,
-                               int32_t max_context_len) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
-      head_dim <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len <= 0)
-    return 0;
-  const int32_t P =
-      chunk_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_q_len, max_context_len).parts;
-  if (P <= 1) return 0;
-  const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
-  return round256(static_cast<size_t>(rows) * sizeof(float2)) +
-         static_cast<size_t>(rows) * head_dim * sizeof(float);
-}
-
-pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t* q_starts,
-                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                             int32_t num_heads, const int32_t* block_tables,
-                             int32_t max_blocks_per_seq, const int32_t* context_lens,
-                             int32_t max_context_len, float scale, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  const char* fn = "pa_chunk_attention";
-  pa::clear_error();
+// pa_chunk_attention's checks and launches; q_starts NULL means one query per
+// sequence, row b (the caller has checked that this is what it wants).
+pa_status chunk_run(const char* fn, const pa_cache* cache, const void* q, const int32_t* q_starts,
+                    int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = pa::check_cache(cache, fn);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || total_q < 0)
@@ -1043,7 +1030,7 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   if (max_blocks_per_seq < 1 || static_cast<int64_t>(max_blocks_per_seq) * kBlock < max_context_len)
     return pa::fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq %d cannot hold %d tokens", fn,
                     max_blocks_per_seq, max_context_len);
-  if (!q || !q_starts || !block_tables || !context_lens || !out || !pa::aligned16(q) ||
+  if (!q || !block_tables || !context_lens || !out || !pa::aligned16(q) ||
       !pa::aligned16(out))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer or q / out not 16-byte aligned", fn);
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
@@ -1100,6 +1087,47 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
   else
     launch_chunk<BF16>(a, plan, groups8, cache->head_dim, fp8, once, s);
   return pa::launch_status(fn);
+}
+
+pa_status chunk_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                       int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len, float scale,
+                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_run(fn, cache, q, nullptr, num_seqs, num_seqs, 1, num_heads, block_tables,
+                   max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                   workspace_bytes, stream);
+}
+
+}  // namespace pa
+
+extern "C" {
+
+size_t pa_chunk_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t total_q, int32_t max_q_len,
+                               int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      head_dim <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len <= 0)
+    return 0;
+  const int32_t P =
+      chunk_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_q_len, max_context_len).parts;
+  if (P <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(total_q) * num_heads * P;
+  return round256(static_cast<size_t>(rows) * sizeof(float2)) +
+         static_cast<size_t>(rows) * head_dim * sizeof(float);
+}
+
+pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t* q_starts,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  if (!q_starts && num_seqs > 0 && total_q > 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_chunk_attention: q_starts is NULL");
+  return pa::chunk_run("pa_chunk_attention", cache, q, q_starts, num_seqs, total_q, max_q_len,
+                       num_heads, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                       scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -44,4 +44,14 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
                      const int64_t* slot_mapping, bool merge, bool fuse_merge, void* ev_begin,
                      void* ev_end, void* stream);
 
+// Decode with more than 16 query heads per KV head: pa_chunk_attention's kernels
+// with one query per sequence (q and out [num_seqs][num_heads][head_dim]), the
+// key-partition states in `workspace` (pa_chunk_workspace_size bytes for
+// total_q = num_seqs, max_q_len = 1, which pa_decode_workspace_size covers past
+// its counters).  Checks and launches as pa_chunk_attention.
+pa_status chunk_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                       int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len, float scale,
+                       void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 }  // namespace pa

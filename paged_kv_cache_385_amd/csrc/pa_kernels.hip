@@ -902,6 +902,7 @@ struct DecodeSetup {
   int64_t grid;
   bool shared_blocks;   // read K/V through the caches
   bool fp8;             // the pools hold E4M3 codes
+  bool wide_group;      // more than 16 query heads per KV head: the chunk kernels
 };
 
 pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
@@ -915,7 +916,7 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
     return pa::fail(PA_ERR_INVALID_ARG, "%s: num_heads %d not a multiple of num_kv_heads %d", fn,
                     num_heads, cache->num_kv_heads);
   const int32_t G = num_heads / cache->num_kv_heads;
-  if (G > 16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", fn, G);
+  su->wide_group = G > 16;
   if (max_ctx < 1) return pa::fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d", fn, max_ctx);
   if (need_q) {
     if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * kBlock < max_ctx)
@@ -1082,10 +1083,31 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
       su.args.new_slots = slot_mapping;
     }
   }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (su.wide_group) {
+    // More than 16 query heads per KV head do not fit one matrix-core tile of the
+    // decode pass: the several-token kernels run with one query per sequence, their
+    // partition states past the workspace counters.  A 16-bit store of new tokens is
+    // then its own launch first (the slots are stored as given).
+    if (k_new && !su.fp8) {
+      st = pa_cache_write(cache, k_new, v_new, slot_mapping, num_seqs, stream);
+      if (st != PA_OK) return st;
+    }
+    const size_t cb = ws_counter_bytes(num_seqs, num_heads);
+    void* ws = workspace && workspace_bytes > cb ? static_cast<char*>(workspace) + cb : nullptr;
+    const size_t wsb = ws ? workspace_bytes - cb : 0;
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
+      return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
+    st = chunk_decode(fn, cache, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
+                      context_lens, max_context_len, scale, out, ws, wsb, stream);
+    if (st != PA_OK) return st;
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
+      return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
+    return PA_OK;
+  }
   const int32_t P = su.args.max_parts;
   if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())
     su.args.counters = static_cast<int32_t*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
     return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
   if (cache->dtype == PA_F16)
@@ -1254,7 +1276,8 @@ pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_h
   pa_status st = prepare_decode("pa_decode_merge", cache, nullptr, num_seqs, num_heads, nullptr, 0,
                                 context_lens, max_context_len, 1.f, out, workspace,
                                 workspace_bytes, false, &su);
-  if (st != PA_OK || num_seqs == 0 || su.args.max_parts <= 1) return st;
+  // wide query groups: pa_decode_attention has merged already
+  if (st != PA_OK || num_seqs == 0 || su.args.max_parts <= 1 || su.wide_group) return st;
   MergeArgs m;
   m.ctx_lens = context_lens;
   m.out = static_cast<uint16_t*>(out);
