@@ -1,0 +1,74 @@
+"""bench.py's HBM-counter summary on synthetic rocprofv3 counter files (no GPU).
+
+The summary scales each counter by what it read for a calibration copy of known size,
+takes the last --steps calls (a call may be an attention and a merge launch), and stamps
+the result with the kernel source; the bench line uses it only while stamp and run match.
+"""
+
+import csv
+import json
+import types
+
+import bench
+
+
+def _counter_csv(path, name, calib_value, launches, values):
+    """3 calibration copies, then the launches (kernel name, value) in dispatch order."""
+    rows = []
+    did = 1
+    for _ in range(3):
+        rows.append(dict(Dispatch_Id=did, Kernel_Name="__amd_rocclr_copyBuffer", Counter_Name=name,
+                         Counter_Value=calib_value))
+        did += 1
+    for k, v in zip(launches, values):
+        rows.append(dict(Dispatch_Id=did, Kernel_Name=k, Counter_Name=name, Counter_Value=v))
+        did += 1
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _args(tmp_path, chunk, fetch, write, steps=4, warmup=2):
+    return types.SimpleNamespace(chunk=chunk, workload=3, steps=steps, warmup=warmup,
+                                 copy_calibration=1, summarize_counters=[str(fetch), str(write)])
+
+
+def test_decode_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    out = tmp_path / "decode.json"
+    path, src, names = bench.TRAFFIC["decode"]
+    monkeypatch.setitem(bench.TRAFFIC, "decode", (str(out), src, names))
+    k = "void decode_attn_kernel<BF16, 128>(DecodeArgs)"
+    # a 1 MiB copy reads as 512 KiB of FETCH_SIZE (scale 2) and 1024 KiB of WRITE_SIZE
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", 512, [k] * 6, [9, 9, 100, 100, 110, 110])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", 1024, [k] * 6, [1, 1, 4, 4, 4, 4])
+    bench.summarize_counters(_args(tmp_path, None, tmp_path / "f.csv", tmp_path / "w.csv"))
+    t = json.loads(out.read_text())
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
+    assert t["launches"] == 4                                 # the warm-up launches are dropped
+    assert t["fetch_bytes_per_launch"] == int(105 * 1024 * 2)
+    assert t["write_bytes_per_launch"] == 4 * 1024
+    assert t["traffic_bytes_per_launch"] == 105 * 2048 + 4096
+    assert t["source_sha256"] == bench.source_sha256(src)
+    args = types.SimpleNamespace(chunk=None, workload=3)
+    assert bench.recorded_traffic(args, 4, 2) == t["traffic_bytes_per_launch"]
+    assert bench.recorded_traffic(args, 5, 2) is None         # another run shape
+    assert bench.recorded_traffic(types.SimpleNamespace(chunk=None, workload=2), 4, 2) is None
+
+
+def test_chunk_summary_sums_the_launches_of_a_call(tmp_path, monkeypatch):
+    out = tmp_path / "chunk_{mode}.json"
+    path, src, names = bench.TRAFFIC["chunk"]
+    monkeypatch.setitem(bench.TRAFFIC, "chunk", (str(out), src, names))
+    a, m = "chunk_attn_kernel<BF16, 128, 3, true, false>", "chunk_merge_kernel<BF16, 128>"
+    calls = [a, m] * 6                                        # 2 warm-up + 4 timed calls
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", 512, calls, [50, 5] * 6)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", 1024, calls, [3, 1] * 6)
+    bench.summarize_counters(_args(tmp_path, "verify", tmp_path / "f.csv", tmp_path / "w.csv"))
+    t = json.loads((tmp_path / "chunk_verify.json").read_text())
+    assert t["workload"] == "chunk-verify" and t["launches"] == 8
+    assert t["fetch_bytes_per_launch"] == 55 * 1024 * 2       # per call: attention + merge
+    assert t["write_bytes_per_launch"] == 4 * 1024
+    assert bench.recorded_traffic(types.SimpleNamespace(chunk="verify", workload=3), 4, 2) \
+        == t["traffic_bytes_per_launch"]
+    assert bench.recorded_traffic(types.SimpleNamespace(chunk="prefill", workload=3), 4, 2) is None
