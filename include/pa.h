@@ -543,7 +543,9 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  * makes copy_stream wait for the end of the step that last read staging_dev).
  * workspace: at least pa_decode_workspace_size(n, num_heads, head_dim,
  * 16 * max_blocks_per_seq) bytes.  attn_begin / attn_end: optional hipEvent_t
- * recorded around the attention pass (NULL to skip).  info (optional) receives
+ * that take the start and end of the attention kernel itself (attached to its
+ * dispatch; with more than 16 query heads per KV head, recorded before and
+ * after the attention launches), NULL to skip.  info (optional) receives
  * the number of copy-on-write pairs and the longest context of the step.
  * The decode reads through the caches (PA_CACHE_SHARED_BLOCKS) whenever the
  * block manager holds a block with more than one reference.

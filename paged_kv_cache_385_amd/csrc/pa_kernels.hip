@@ -24,6 +24,7 @@
 //           C = out^T; lane l accumulates head l%16, so the online-softmax rescale
 //           is lane-local.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -974,26 +975,32 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   return PA_OK;
 }
 
+// The attention launch.  Events given (hipEvent_t, may be NULL) are attached to the
+// dispatch itself: they take the kernel's own start and end times, without the queue
+// time around it that events recorded before and after the launch would include.
 template <class E, bool kStream, bool kFp8>
-void launch_attn_t(const DecodeSetup& su, int d, hipStream_t s) {
+void launch_attn_t(const DecodeSetup& su, int d, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (d == 64)
-    decode_attn_kernel<E, 64, kStream, kFp8><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+    hipExtLaunchKernelGGL(decode_attn_kernel<E, 64, kStream, kFp8>, dim3(su.grid), dim3(kThreads),
+                          0, s, e0, e1, 0, su.args);
   else
-    decode_attn_kernel<E, 128, kStream, kFp8><<<dim3(su.grid), dim3(kThreads), 0, s>>>(su.args);
+    hipExtLaunchKernelGGL(decode_attn_kernel<E, 128, kStream, kFp8>, dim3(su.grid), dim3(kThreads),
+                          0, s, e0, e1, 0, su.args);
 }
 
 template <class E>
-void launch_attn(const DecodeSetup& su, int d, hipStream_t s) {
+void launch_attn(const DecodeSetup& su, int d, hipStream_t s, hipEvent_t e0 = nullptr,
+                 hipEvent_t e1 = nullptr) {
   if (su.fp8) {
     if (su.shared_blocks)
-      launch_attn_t<E, false, true>(su, d, s);
+      launch_attn_t<E, false, true>(su, d, s, e0, e1);
     else
-      launch_attn_t<E, true, true>(su, d, s);
+      launch_attn_t<E, true, true>(su, d, s, e0, e1);
   } else {
     if (su.shared_blocks)
-      launch_attn_t<E, false, false>(su, d, s);
+      launch_attn_t<E, false, false>(su, d, s, e0, e1);
     else
-      launch_attn_t<E, true, false>(su, d, s);
+      launch_attn_t<E, true, false>(su, d, s, e0, e1);
   }
 }
 
@@ -1108,16 +1115,14 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
   const int32_t P = su.args.max_parts;
   if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())
     su.args.counters = static_cast<int32_t*>(workspace);
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
-    return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
+  // the events, if any, take the attention kernel's own start and end
+  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_begin), e1 = static_cast<hipEvent_t>(ev_end);
   if (cache->dtype == PA_F16)
-    launch_attn<F16>(su, cache->head_dim, s);
+    launch_attn<F16>(su, cache->head_dim, s, e0, e1);
   else
-    launch_attn<BF16>(su, cache->head_dim, s);
+    launch_attn<BF16>(su, cache->head_dim, s, e0, e1);
   st = launch_status(fn);
   if (st != PA_OK) return st;
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
-    return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
   if (!merge || P <= 1 || su.args.counters) return PA_OK;
   MergeArgs m;
   m.ctx_lens = context_lens;

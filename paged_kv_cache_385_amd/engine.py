@@ -300,7 +300,7 @@ class DecodeBatch:
 
         k_new, v_new: [B, Hkv, D] of the step's new tokens; q: [B, H, D]; all
         contiguous device tensors of the cache dtype.  ``attn_events``, if given,
-        are recorded around the attention pass.
+        take the start and end of the attention kernel (attached to its dispatch).
         """
         for t, shape in ((k_new, self._kv_shape), (v_new, self._kv_shape), (q, self._q_shape)):
             if (t.dtype != self.cache.dtype or t.device != self._device
