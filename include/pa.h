@@ -208,6 +208,27 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_decode_partitioned -- pa_decode with the context partition length fixed by
+ * the caller.  Defined by: a long context is split into pieces that separate
+ * workgroups attend over, and the pieces' results are combined by log-sum-exp
+ * ("PagedAttention 实战", section "2026 年的新变化": sequence split).
+ * pa_decode picks the partition length per launch from the batch shape and the
+ * device's compute-unit count, and the float32 rounding of the merge depends
+ * on it; a fixed length gives results that are bit-identical on any device and
+ * reproduces a stated split (e.g. 512-token partitions).
+ *   partition_tokens   512, 1024, 2048 or 4096 (0: chosen per launch, as pa_decode).
+ * Every other argument, the workspace rule (pa_decode_workspace_size covers every
+ * length) and the merge placement are as pa_decode.  More than 16 query heads per
+ * KV head with a non-zero partition_tokens: PA_ERR_UNSUPPORTED.  Any other length:
+ * PA_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+pa_status pa_decode_partitioned(const pa_cache* cache, const void* q, int32_t num_seqs,
+                                int32_t num_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float scale, int32_t partition_tokens,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pa_decode_fused -- the step's cache write and its decode in one attention pass.
  * Same result as pa_cache_write(cache, k_new, v_new, slot_mapping, num_seqs)
  * followed by pa_decode(...), when token i (k_new[i], v_new[i], [Hkv][D]) is

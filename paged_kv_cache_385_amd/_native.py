@@ -74,6 +74,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32]),
     "pa_decode": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32, C.c_float, _P,
                             _P, C.c_size_t, _P]),
+    "pa_decode_partitioned": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,
+                                        C.c_float, _I32, _P, _P, C.c_size_t, _P]),
     "pa_decode_attention": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,
                                       C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_decode_merge": (C.c_int, [C.POINTER(PaCache), _I32, _I32, _P, _I32, _P, _P, C.c_size_t,

@@ -138,7 +138,7 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
                         reinterpret_cast<const int32_t*>(db + l.tables), max_blocks_per_seq,
                         reinterpret_cast<const int32_t*>(db + l.ctx), max_ctx, scale, out, workspace,
                         workspace_bytes, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots),
-                        true, true, attn_begin, attn_end, stream);
+                        true, true, 0, attn_begin, attn_end, stream);
 }
 
 }  // extern "C"

@@ -37,12 +37,14 @@ pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, i
 // the attention pass between the optional events ev_begin / ev_end (hipEvent_t),
 // then, if merge, the log-sum-exp merge (inside the attention pass when
 // fuse_merge allows and the partitions are few, else a second launch).
+// part_tokens fixes the partition length (512 .. 4096, a power of two); 0 lets
+// the launch choose it from the batch shape and the device.
 pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
                      int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                      void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
-                     const int64_t* slot_mapping, bool merge, bool fuse_merge, void* ev_begin,
-                     void* ev_end, void* stream);
+                     const int64_t* slot_mapping, bool merge, bool fuse_merge,
+                     int32_t part_tokens, void* ev_begin, void* ev_end, void* stream);
 
 // Decode with more than 16 query heads per KV head: pa_chunk_attention's kernels
 // with one query per sequence (q and out [num_seqs][num_heads][head_dim]), the

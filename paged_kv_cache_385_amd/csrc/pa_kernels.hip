@@ -906,10 +906,17 @@ struct DecodeSetup {
   bool wide_group;      // more than 16 query heads per KV head: the chunk kernels
 };
 
+// A partition length the caller may fix: 0 (chosen per launch) or 512 .. 4096 tokens,
+// a power of two.
+bool valid_part_tokens(int32_t pt) {
+  return pt == 0 || (pt >= kPartTokens && pt <= kMaxPartTokens && (pt & (pt - 1)) == 0);
+}
+
 pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
                          int32_t num_heads, const int32_t* block_tables, int32_t max_blocks,
                          const int32_t* ctx_lens, int32_t max_ctx, float scale, void* out,
-                         void* workspace, size_t workspace_bytes, bool need_q, DecodeSetup* su) {
+                         void* workspace, size_t workspace_bytes, bool need_q, DecodeSetup* su,
+                         int32_t part_tokens = 0) {
   pa_status st = check_cache(cache, fn);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
@@ -931,7 +938,10 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
     return pa::fail(PA_ERR_INVALID_ARG, "%s: context_lens / out NULL or out misaligned", fn);
   if (parts_for(max_ctx, kPartTokens) > kMaxParts)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d too long", fn, max_ctx);
-  const int32_t PT = part_tokens_for(num_seqs, cache->num_kv_heads, max_ctx);
+  if (!valid_part_tokens(part_tokens))
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d (0, or a power of two in 512 .. 4096)",
+                    fn, part_tokens);
+  const int32_t PT = part_tokens ? part_tokens : part_tokens_for(num_seqs, cache->num_kv_heads, max_ctx);
   const int32_t P = parts_for(max_ctx, PT);
   // The workspace is sized for 512-token partitions; a launch with longer ones uses a prefix.
   const size_t need = P > 1 ? pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx) : 0;
@@ -1004,12 +1014,14 @@ void launch_attn(const DecodeSetup& su, int d, hipStream_t s, hipEvent_t e0 = nu
   }
 }
 
+// The separate merge launch; a stop event given (hipEvent_t, may be NULL) takes the
+// merge kernel's own end time.
 template <class E>
-void launch_merge(const MergeArgs& m, int64_t grid, int d, hipStream_t s) {
+void launch_merge(const MergeArgs& m, int64_t grid, int d, hipStream_t s, hipEvent_t e1 = nullptr) {
   if (d == 64)
-    decode_merge_kernel<E, 64><<<dim3(grid), dim3(256), 0, s>>>(m);
+    hipExtLaunchKernelGGL(decode_merge_kernel<E, 64>, dim3(grid), dim3(256), 0, s, nullptr, e1, 0, m);
   else
-    decode_merge_kernel<E, 128><<<dim3(grid), dim3(256), 0, s>>>(m);
+    hipExtLaunchKernelGGL(decode_merge_kernel<E, 128>, dim3(grid), dim3(256), 0, s, nullptr, e1, 0, m);
 }
 
 template <class E>
@@ -1063,14 +1075,17 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
                      int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                      void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
-                     const int64_t* slot_mapping, bool merge, bool fuse_merge, void* ev_begin,
-                     void* ev_end, void* stream) {
+                     const int64_t* slot_mapping, bool merge, bool fuse_merge,
+                     int32_t part_tokens, void* ev_begin, void* ev_end, void* stream) {
   pa::clear_error();
   DecodeSetup su;
   pa_status st = prepare_decode(fn, cache, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
                                 context_lens, max_context_len, scale, out, workspace,
-                                workspace_bytes, true, &su);
+                                workspace_bytes, true, &su, part_tokens);
   if (st != PA_OK || num_seqs == 0) return st;
+  if (part_tokens && su.wide_group)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: a fixed partition length needs at most 16 query heads "
+                    "per KV head", fn);
   if (k_new) {
     if (!v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
@@ -1115,15 +1130,16 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
   const int32_t P = su.args.max_parts;
   if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())
     su.args.counters = static_cast<int32_t*>(workspace);
-  // the events, if any, take the attention kernel's own start and end
+  // The events, if any, take the attention kernel's own start and the end of the
+  // last kernel of the pass: the attention kernel, or the separate merge after it.
+  const bool separate_merge = merge && P > 1 && !su.args.counters;
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_begin), e1 = static_cast<hipEvent_t>(ev_end);
   if (cache->dtype == PA_F16)
-    launch_attn<F16>(su, cache->head_dim, s, e0, e1);
+    launch_attn<F16>(su, cache->head_dim, s, e0, separate_merge ? nullptr : e1);
   else
-    launch_attn<BF16>(su, cache->head_dim, s, e0, e1);
+    launch_attn<BF16>(su, cache->head_dim, s, e0, separate_merge ? nullptr : e1);
   st = launch_status(fn);
-  if (st != PA_OK) return st;
-  if (!merge || P <= 1 || su.args.counters) return PA_OK;
+  if (st != PA_OK || !separate_merge) return st;
   MergeArgs m;
   m.ctx_lens = context_lens;
   m.out = static_cast<uint16_t*>(out);
@@ -1136,9 +1152,9 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
   m.part_tokens = su.args.part_blocks * kBlock;
   const int64_t grid = (static_cast<int64_t>(num_seqs) * num_heads + 3) / 4;
   if (cache->dtype == PA_F16)
-    launch_merge<F16>(m, grid, cache->head_dim, s);
+    launch_merge<F16>(m, grid, cache->head_dim, s, e1);
   else
-    launch_merge<BF16>(m, grid, cache->head_dim, s);
+    launch_merge<BF16>(m, grid, cache->head_dim, s, e1);
   return launch_status(fn);
 }
 
@@ -1269,8 +1285,8 @@ pa_status pa_decode_attention(const pa_cache* cache, const void* q, int32_t num_
                               size_t workspace_bytes, void* stream) {
   return pa::decode_run("pa_decode_attention", cache, q, num_seqs, num_heads, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                        workspace_bytes, nullptr, nullptr, nullptr, false, false, nullptr, nullptr,
-                        stream);
+                        workspace_bytes, nullptr, nullptr, nullptr, false, false, 0, nullptr,
+                        nullptr, stream);
 }
 
 pa_status pa_decode_merge(const pa_cache* cache, int32_t num_seqs, int32_t num_heads,
@@ -1308,8 +1324,19 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
                     void* workspace, size_t workspace_bytes, void* stream) {
   return pa::decode_run("pa_decode", cache, q, num_seqs, num_heads, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                        workspace_bytes, nullptr, nullptr, nullptr, true, true, nullptr, nullptr,
-                        stream);
+                        workspace_bytes, nullptr, nullptr, nullptr, true, true, 0, nullptr,
+                        nullptr, stream);
+}
+
+pa_status pa_decode_partitioned(const pa_cache* cache, const void* q, int32_t num_seqs,
+                                int32_t num_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float scale, int32_t partition_tokens,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa::decode_run("pa_decode_partitioned", cache, q, num_seqs, num_heads, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
+                        workspace_bytes, nullptr, nullptr, nullptr, true, true, partition_tokens,
+                        nullptr, nullptr, stream);
 }
 
 pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* v_new,
@@ -1320,8 +1347,8 @@ pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* 
   if (!k_new) return pa::fail(PA_ERR_INVALID_ARG, "pa_decode_fused: k_new is NULL");
   return pa::decode_run("pa_decode_fused", cache, q, num_seqs, num_heads, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                        workspace_bytes, k_new, v_new, slot_mapping, true, true, nullptr, nullptr,
-                        stream);
+                        workspace_bytes, k_new, v_new, slot_mapping, true, true, 0, nullptr,
+                        nullptr, stream);
 }
 
 }  // extern "C"

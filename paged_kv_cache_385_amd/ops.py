@@ -209,6 +209,21 @@ def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int
     return out
 
 
+def decode_partitioned(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
+                       scale: float, partition_tokens: int, out=None, workspace=None, stream=None,
+                       scales=None) -> torch.Tensor:
+    """pa_decode_partitioned: pa_decode with a fixed partition length (512 .. 4096 tokens,
+    or 0 for the per-launch choice); returns out [B, H, D]."""
+    desc, B, H, out, ws, wsb = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
+                                            workspace, False, scales)
+    N.check(N.lib().pa_decode_partitioned(C.byref(desc), q.data_ptr(), B, H,
+                                          block_tables.data_ptr(), block_tables.shape[1],
+                                          context_lens.data_ptr(), max_context_len, scale,
+                                          int(partition_tokens), out.data_ptr(), ws, wsb,
+                                          _stream_ptr(stream, q.device)), "pa_decode_partitioned")
+    return out
+
+
 def decode_fused(k_cache, v_cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
                  max_context_len: int, scale: float, out=None, workspace=None,
                  stream=None, scales=None) -> torch.Tensor:

@@ -123,6 +123,22 @@ def test_call_validation():
 
 
 @no_device
+def test_partitioned_decode_validation():
+    lib = N.lib()
+    c = _cache()
+    need = lib.pa_decode_workspace_size(2, 4, 128, 1000)
+    part = lambda pt, H=4, ws=FAKE, wsb=need: lib.pa_decode_partitioned(  # noqa: E731
+        C.byref(c), FAKE, 2, H, FAKE, 64, FAKE, 1000, 0.1, pt, FAKE, ws, wsb, None)
+    for bad in (256, 768, 8192, -512, 1):
+        assert part(bad) == N.PA_ERR_INVALID_ARG, bad
+        assert b"partition_tokens" in lib.pa_last_error()
+    assert part(512, ws=None, wsb=0) == N.PA_ERR_WORKSPACE   # 1000 tokens in two partitions
+    # 17 query heads per KV head run the several-token kernels, which choose their own split
+    need34 = lib.pa_decode_workspace_size(2, 34, 128, 1000)
+    assert part(1024, H=34, wsb=need34) == N.PA_ERR_UNSUPPORTED
+
+
+@no_device
 def test_chunk_call_validation():
     lib = N.lib()
     c = _cache()                                        # 2 KV heads, head_dim 128

@@ -158,6 +158,42 @@ def test_exhaustion_is_atomic():
     assert _snapshot(bm) == snap
 
 
+def test_prefill_append_counts_the_copy_on_write_block():
+    """append_tokens is all or nothing, and its block count includes the private copy of
+    a shared, partly filled last block.  Worked by hand on a 6-block pool (free order
+    0, 1, ..., so blocks are taken in ascending order):
+      seq 0 holds 20 tokens in blocks [0, 1] (block 1 holds 4); seq 1 is its fork, so
+      both blocks have two references and blocks 2..5 are free.
+      61 more tokens for seq 1 reach 81 tokens = 6 blocks: the copy of block 1 plus 4
+      new blocks = 5 > 4 free -> refused, nothing changes.  (A count that leaves out
+      the copy would see 4 <= 4, start, and fail on token 81 with the pool changed.)
+      60 tokens reach 80 = 5 blocks: copy + 3 new = 4 -> accepted.  Block 1 is copied
+      to 2 (pair (1, 2)), positions 20..31 land in block 2, then 32..47 in 3, 48..63
+      in 4 and 64..79 in 5.
+      seq 0 is now block 1's only holder and fills it in place (12 tokens, no block);
+      its 33rd token needs a block the empty pool does not have -> refused."""
+    bm = BM.RefBlockManager(6, 16)
+    bm.add_seq(0)
+    assert bm.append_tokens(0, 20) == (list(range(0, 20)), [])
+    bm.fork(0, 1)
+    snap = _snapshot(bm)
+    with pytest.raises(BM.OutOfBlocks):
+        bm.append_tokens(1, 61)
+    assert _snapshot(bm) == snap
+    slots, cows = bm.append_tokens(1, 60)
+    assert cows == [(1, 2)]
+    assert slots == (list(range(2 * 16 + 4, 3 * 16)) + list(range(3 * 16, 6 * 16)))
+    assert bm.block_table(1) == [0, 2, 3, 4, 5]
+    assert bm.block_table(0) == [0, 1]
+    assert [bm.refcount(b) for b in range(6)] == [2, 1, 1, 1, 1, 1]
+    assert bm.free_list() == []
+    assert bm.append_tokens(0, 12) == (list(range(16 + 4, 32)), [])
+    snap = _snapshot(bm)
+    with pytest.raises(BM.OutOfBlocks):
+        bm.append_tokens(0, 1)
+    assert _snapshot(bm) == snap
+
+
 def test_free_returns_blocks_first_logical_on_top():
     bm = BM.RefBlockManager(8, 16, [3, 1, 4, 0, 5, 2, 6, 7])
     bm.add_seq(0)
