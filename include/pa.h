@@ -208,6 +208,31 @@ pa_status pa_decode(const pa_cache* cache, const void* q, int32_t num_seqs, int3
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Its scratch (the merge
+ * counters and the partition states pa_decode keeps in the workspace) is a
+ * device array of PA_NOALLOC_SCRATCH_BYTES inside the library: each GPU the call
+ * runs on holds one until the process ends, and the first call on a device looks
+ * up its address there (the current device; `stream` must belong to it).
+ *   - A call whose pa_decode_workspace_size(num_seqs, num_heads, head_dim,
+ *     max_context_len) exceeds PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE
+ *     and enqueues nothing.
+ *   - Each call first zeroes the counters with a small kernel (no memset node),
+ *     then runs pa_decode's kernels on the scratch: the same bits as pa_decode.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents: calls that may overlap on one GPU (other streams, other host
+ *     threads) race and must be serialised by the caller.
+ * Arguments and errors otherwise as pa_decode.
+ * ------------------------------------------------------------------------- */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(const pa_cache* cache, const void* q, int32_t num_seqs,
+                            int32_t num_heads, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float scale, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pa_decode_partitioned -- pa_decode with the context partition length fixed by
  * the caller.  Defined by: a long context is split into pieces that separate
  * workgroups attend over, and the pieces' results are combined by log-sum-exp

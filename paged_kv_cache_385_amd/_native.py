@@ -26,6 +26,7 @@ PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PaCache(C.Structure):
@@ -74,6 +75,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32]),
     "pa_decode": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32, C.c_float, _P,
                             _P, C.c_size_t, _P]),
+    "pa_decode_noalloc": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,
+                                    C.c_float, _P, _P]),
     "pa_decode_partitioned": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,
                                         C.c_float, _I32, _P, _P, C.c_size_t, _P]),
     "pa_decode_attention": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _P, _I32,

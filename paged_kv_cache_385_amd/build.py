@@ -63,9 +63,12 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     c_o = os.path.join(BUILD, "chunk_attention.o")
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "chunk_attention.hip"), "-o",
           c_o], verbose)
+    n_o = os.path.join(BUILD, "decode_noalloc.o")
+    _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "decode_noalloc.hip"), "-o",
+          n_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, "-o", tmp],
-         verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, n_o, "-o",
+          tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -209,6 +209,19 @@ def decode(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int
     return out
 
 
+def decode_noalloc(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
+                   scale: float, out=None, stream=None, scales=None) -> torch.Tensor:
+    """pa_decode_noalloc: pa_decode on the library's own scratch (no workspace); returns
+    out [B, H, D].  Calls that may overlap on one device race on that scratch."""
+    desc, B, H, out, _, _ = _decode_args(k_cache, v_cache, q, block_tables, context_lens, out,
+                                         None, False, scales)
+    N.check(N.lib().pa_decode_noalloc(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
+                                      block_tables.shape[1], context_lens.data_ptr(),
+                                      max_context_len, scale, out.data_ptr(),
+                                      _stream_ptr(stream, q.device)), "pa_decode_noalloc")
+    return out
+
+
 def decode_partitioned(k_cache, v_cache, q, block_tables, context_lens, max_context_len: int,
                        scale: float, partition_tokens: int, out=None, workspace=None, stream=None,
                        scales=None) -> torch.Tensor:
