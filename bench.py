@@ -34,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 EVENT_EVERY = 5                # timed steps whose attention pass carries a timing event pair
+FLUSH_BYTES = 1 << 30          # written before a flushed step: > 8 x 4 MB L2 + 256 MB Infinity Cache
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, AMD published (no sparsity)
 METRIC = "paged-attn decode KV GB/s read (% of HBM peak); sequence-steps/s"
@@ -41,8 +42,8 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc")
 # per measured leg: the counter summary file, the kernel source it is stamped with and
 # the kernel names that make up one call
 TRAFFIC = {
-    "decode": (os.path.join(ROOT, "profiles", "decode_attn_traffic.json"),
-               os.path.join(CSRC, "pa_kernels.hip"), ("decode_attn_kernel",)),
+    "decode": (os.path.join(ROOT, "profiles", "decode_attn_traffic_{mode}.json"),
+               os.path.join(CSRC, "pa_kernels.hip"), ("decode_attn_kernel", "decode_merge_kernel")),
     "chunk": (os.path.join(ROOT, "profiles", "chunk_attn_traffic_{mode}.json"),
               os.path.join(CSRC, "chunk_attention.hip"),
               ("chunk_attn_kernel", "chunk_wide_kernel", "chunk_merge_kernel")),
@@ -85,6 +86,14 @@ def parse():
                     help="measure pa_chunk_attention instead of the decode step: 'verify' = the "
                          "70B-shaped batch with 6 new tokens per sequence (HBM-bound), 'prefill' = "
                          "the last 1024-token chunk of four 4096-token prompts (matrix-core bound)")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="after the timed steps, this many more steps each preceded by a "
+                         f"{FLUSH_BYTES >> 20} MiB write that evicts L2 and the Infinity Cache "
+                         "(outside the attention events): the flushed roofline fraction")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read probes (the measured read ceiling)")
+    ap.add_argument("--no-other-ops", action="store_true",
+                    help="skip timing pa_copy_blocks and a bulk pa_cache_write")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -101,11 +110,14 @@ def source_sha256(path: str) -> str:
 
 def traffic_leg(args):
     """(summary file, stamped source, kernel names, workload key) of the measured leg."""
+    fp8 = getattr(args, "kv_dtype", "native") == "fp8"
     if args.chunk:
         path, src, names = TRAFFIC["chunk"]
-        return path.format(mode=args.chunk), src, names, f"chunk-{args.chunk}"
+        mode = args.chunk + ("_fp8" if fp8 else "")
+        return path.format(mode=mode), src, names, f"chunk-{mode}"
     path, src, names = TRAFFIC["decode"]
-    return path, src, names, args.workload
+    mode = f"w{args.workload}" + ("_fp8" if fp8 else "")
+    return path.format(mode=mode), src, names, mode
 
 
 def summarize_counters(args):
@@ -146,19 +158,32 @@ def summarize_counters(args):
     print(json.dumps(out))
 
 
-def recorded_traffic(args, steps: int, warmup: int):
-    """Traffic per call from the leg's counter file, if it was taken on this kernel source
-    and run."""
+def recorded_traffic(args):
+    """The leg's counter summary (traffic per call and the steps and warm-up of the run it
+    was taken on), if it was taken on this kernel source and workload; else None."""
     path, src, _, key = traffic_leg(args)
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if (t.get("source_sha256") != source_sha256(src) or t.get("workload") != key
-            or t.get("steps") != steps or t.get("warmup") != warmup):
+    if t.get("source_sha256") != source_sha256(src) or t.get("workload") != key:
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t
+
+
+def traffic_fields(rec, algorithmic_bytes):
+    """roofline.traffic and its context: the counter run's HBM bytes per call, that run's
+    algorithmic bytes per call (``algorithmic_bytes(steps, warmup)``) and their ratio."""
+    if rec is None:
+        return {"traffic": None}
+    t = int(rec["traffic_bytes_per_launch"])
+    alg = algorithmic_bytes(int(rec["steps"]), int(rec["warmup"]))
+    return {"traffic": t, "traffic_run": {"steps": rec["steps"], "warmup": rec["warmup"],
+                                          "algorithmic_bytes": int(alg),
+                                          "fetch_bytes": rec["fetch_bytes_per_launch"],
+                                          "write_bytes": rec["write_bytes_per_launch"]},
+            "traffic_ratio": round(t / alg, 4)}
 
 
 def calibration_copy(args, dev):
@@ -190,27 +215,171 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The oracle, as it stands, on the first sequences of the workload until the budget is spent."""
+def host_info() -> dict:
+    """The host the CPU baseline runs on: logical CPUs, those this process may use, model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "usable_cpus": usable, "model": model,
+            "blas_threads": blas_threads()}
+
+
+def _timed_oracle(wl, budget_s: float):
+    """The oracle on the workload's sequences in order until the budget is spent; returns
+    (seconds, CPU seconds of the process, K/V bytes, sequences)."""
     from oracle import attention as OA
-    threads = blas_threads()
     q = wl.q()
-    t_total, kv_bytes, seqs = 0.0, 0, 0
+    t_total, cpu_total, kv_bytes, seqs = 0.0, 0.0, 0, 0
     per_tok = 2 * wl.num_kv_heads * wl.head_dim * 2
     b = 0
     while t_total < budget_s:
         k, v = wl.seq_kv(b % wl.num_seqs)        # generation is not timed
+        c0 = time.process_time()
         t0 = time.perf_counter()
         OA.decode_attention(q[b % wl.num_seqs], k, v, wl.scale)
         t_total += time.perf_counter() - t0
+        cpu_total += time.process_time() - c0
         kv_bytes += int(wl.ctx_lens[b % wl.num_seqs]) * per_tok
         seqs += 1
         b += 1
-    return {"value": kv_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "seq_steps_per_s": seqs / t_total,
-            "sample": f"{seqs} sequence decodes cycling over the workload's {wl.num_seqs} sequences, "
-                      f"{kv_bytes / 1e6:.1f} MB of K/V, float64 numpy, {t_total:.1f} s"}
+    return t_total, cpu_total, kv_bytes, seqs
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle, as it stands, on the workload's sequences: once with the BLAS pool at
+    its default size, once limited to one thread, half the budget each.  ``cores`` is
+    the threads the oracle actually kept busy (process CPU time / wall time)."""
+    info = host_info()
+    t, c, kvb, n = _timed_oracle(wl, budget_s / 2)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1, c1, kvb1, n1 = _timed_oracle(wl, budget_s / 2)
+        one = {"value": kvb1 / t1 / 1e9, "seq_steps_per_s": n1 / t1,
+               "cores": round(c1 / t1, 2), "sequences": n1}
+    except Exception as e:                       # threadpoolctl missing: report the one run
+        log(f"one-thread oracle run skipped: {e}")
+    return {"value": kvb / t / 1e9, "unit": "GB/s", "cores": round(c / t, 2),
+            "kind": "oracle", "seq_steps_per_s": n / t,
+            "threads_allowed": info["blas_threads"], "host": info, "one_thread": one,
+            "sample": f"{n} sequence decodes cycling over the workload's {wl.num_seqs} sequences "
+                      f"({kvb / 1e6:.1f} MB of K/V) in {t:.1f} s with the BLAS pool at "
+                      f"{info['blas_threads']} threads, then the same at 1 thread; float64 numpy"}
+
+
+def _time_launches(fn, reps: int, stream) -> float:
+    """Average microseconds per call of ``reps`` back-to-back calls between one event pair."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()                                       # untimed first call
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def read_ceiling(cache, sids, max_blocks, wl, dev, achieved_gbs, reps: int = 10):
+    """Measured read ceilings (pa_probe_read_*): a contiguous 2 GiB read, and a gather of
+    exactly the (block, KV head) tiles the decode pass reads, K and V, in a shuffled order
+    (the decode pass reads them in its own order).  Each at 2, 4 and 8 workgroups per
+    compute unit; the best is reported."""
+    import ctypes as C
+    import torch
+    from paged_kv_cache_385_amd import _native
+    lib = _native.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = C.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    contiguous = {}
+    for wg in (2, 4, 8):
+        us = _time_launches(lambda: _native.check(lib.pa_probe_read_contiguous(
+            buf.data_ptr(), buf.numel(), wg, sink.data_ptr(), sp), "pa_probe_read_contiguous"),
+            reps, stream)
+        contiguous[wg] = buf.numel() / (us * 1e-6) / 1e9
+    del buf
+    tab, ctx = cache.bm.pack(np.asarray(sids, dtype=np.int64), max_blocks)
+    Hkv = wl.num_kv_heads
+    tiles = np.concatenate([(tab[b, :-(-int(ctx[b]) // 16)].astype(np.int64)[:, None] * Hkv
+                             + np.arange(Hkv)[None, :]).ravel() for b in range(len(ctx))])
+    tiles = np.random.default_rng(385).permutation(tiles).astype(np.int32)
+    tiles_d = torch.from_numpy(tiles).to(dev)
+    pool_bytes = cache.k_cache.numel() * cache.k_cache.element_size()
+    tile_bytes = 2 * len(tiles) * 4096
+    gather = {}
+    for wg in (2, 4, 8):
+        us = _time_launches(lambda: _native.check(lib.pa_probe_read_tiles(
+            cache.k_cache.data_ptr(), cache.v_cache.data_ptr(), pool_bytes, tiles_d.data_ptr(),
+            tiles.ctypes.data, len(tiles), wg, sink.data_ptr(), sp), "pa_probe_read_tiles"),
+            reps, stream)
+        gather[wg] = tile_bytes / (us * 1e-6) / 1e9
+    bc, bg = max(contiguous, key=contiguous.get), max(gather, key=gather.get)
+    log(f"read ceiling: contiguous {contiguous[bc]:.0f} GB/s ({bc} workgroups/CU), tile gather "
+        f"{gather[bg]:.0f} GB/s ({bg} workgroups/CU) over {tile_bytes / 1e6:.1f} MB")
+    return {"unit": "GB/s", "contiguous": round(contiguous[bc], 1),
+            "tile_gather": round(gather[bg], 1),
+            "frac_of_tile_gather": round(achieved_gbs / gather[bg], 4),
+            "contiguous_bytes": 2 << 30, "tile_gather_bytes": tile_bytes,
+            "workgroups_per_cu": {"contiguous": bc, "tile_gather": bg},
+            "kernels": "probe_contiguous_kernel, probe_tiles_kernel (pa_probe.h)"}
+
+
+def other_ops(dev, reps: int = 20):
+    """pa_copy_blocks and a bulk pa_cache_write, in GB/s of bytes read + written.
+    copy-on-write: the 112 pairs of the shared-prefix workload (16 prompts x 7 copies of
+    the partly filled last prefix block; 32 KV heads, head_dim 128, float16: 128 KiB of K
+    and 128 KiB of V per block) in one call.  Bulk write: 131072 tokens of the 70B-shaped
+    layer (8 KV heads, head_dim 128, bfloat16) into 8192 blocks, 16 consecutive slots per
+    block, the blocks in random order (a prefill's store)."""
+    import torch
+    import paged_kv_cache_385_amd as pa
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(385)
+    out = {}
+    nb, hkv, d = 2048, 32, 128
+    k, v = pa.alloc_pool(nb, hkv, d, torch.float16, dev, fill_bits=0x3C00)
+    perm = rng.permutation(nb)
+    pairs_h = np.ascontiguousarray(np.stack([perm[:112], perm[112:224]], 1).astype(np.int32))
+    pairs = torch.from_numpy(pairs_h).to(dev)
+    us = _time_launches(lambda: pa.copy_blocks(k, v, pairs, pairs_host=pairs_h), reps, stream)
+    moved = 2 * 112 * 2 * hkv * 16 * d * 2
+    out["copy_blocks"] = {"pairs": 112, "us": round(us, 2), "bytes": moved,
+                          "gbs": round(moved / (us * 1e-6) / 1e9, 1),
+                          "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "kernel": "block_copy_kernel"}
+    del k, v, pairs
+    nb, hkv, T = 8192, 8, 131072
+    k, v = pa.alloc_pool(nb, hkv, d, torch.bfloat16, dev, fill_bits=0)
+    blocks = rng.permutation(nb)[:T // 16]
+    slots = torch.from_numpy((blocks[:, None] * 16 + np.arange(16)[None, :]).ravel().astype(np.int64)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(385)
+    kn = torch.randn((T, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vn = torch.randn((T, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    us = _time_launches(lambda: pa.cache_write(k, v, kn, vn, slots), reps, stream)
+    moved = 2 * T * 2 * hkv * d * 2 + 8 * T
+    out["cache_write_bulk"] = {"tokens": T, "us": round(us, 2), "bytes": moved,
+                               "gbs": round(moved / (us * 1e-6) / 1e9, 1),
+                               "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "kernel": "cache_write_kernel"}
+    log(f"other ops: copy_blocks 112 pairs {out['copy_blocks']['us']:.1f} us "
+        f"({out['copy_blocks']['gbs']:.0f} GB/s); cache_write {T} tokens "
+        f"{out['cache_write_bulk']['us']:.1f} us ({out['cache_write_bulk']['gbs']:.0f} GB/s)")
+    return out
 
 
 def chunk_workload(mode):
@@ -312,8 +481,8 @@ def run_chunk(args):
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFS, 4)}
     kname = "chunk_wide_kernel" if mq * (H // Hkv) >= 128 else "chunk_attn_kernel"
-    roof.update({"traffic": None if fp8 else recorded_traffic(args, K, W),
-                 "kernel": f"{kname}<{wl.dtype_name.upper()},{D}" + (",FP8>" if fp8 else ">")
+    roof.update(traffic_fields(recorded_traffic(args), lambda s_, w_: kv_bytes + io_bytes))
+    roof.update({"kernel": f"{kname}<{wl.dtype_name.upper()},{D}" + (",FP8>" if fp8 else ">")
                  + (" + chunk_merge_kernel" if need else ""),
                  "avg_launch_us": round(us, 2), "bytes_per_launch": kv_bytes + io_bytes,
                  "flops_per_launch": flops})
@@ -330,21 +499,24 @@ def run_chunk(args):
         log("CPU oracle baseline ...")
         qc = wl.chunk_q(q_lens)
         st = np.concatenate([[0], np.cumsum(q_lens)])
-        t_total, done_b, done_f = 0.0, 0, 0
+        t_total, c_total, done_b, done_f = 0.0, 0.0, 0, 0
         b = 0
         while t_total < args.cpu_seconds and b < 4 * B:
             bb = b % B
             k, v = wl.seq_kv(bb)
             n = int(q_lens[bb])
             rows = slice(int(st[bb]), int(st[bb]) + n)
+            c1 = time.process_time()
             t1 = time.perf_counter()
             OA.chunk_attention(qc[rows], k, v, wl.scale)
             t_total += time.perf_counter() - t1
+            c_total += time.process_time() - c1
             done_b += int(wl.ctx_lens[bb]) * per_tok
             done_f += chunk_flops([wl.ctx_lens[bb]], [n], H, D)
             b += 1
         cpu = done_b / t_total / 1e9 if unit == "GB/s" else done_f / t_total / 1e12
-        result["cpu_baseline"] = {"value": cpu, "unit": unit, "cores": blas_threads(), "kind": "oracle",
+        result["cpu_baseline"] = {"value": cpu, "unit": unit, "cores": round(c_total / t_total, 2),
+                                  "kind": "oracle", "host": host_info(),
                                   "sample": f"{b} sequences' chunks, float64 numpy, {t_total:.1f} s"}
     print(json.dumps(result), flush=True)
 
@@ -516,12 +688,11 @@ def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
     its attention computes each admitted request's new tokens (float64 numpy)."""
     from oracle import attention as OA
     from oracle.prefix_cache import RefPrefixCache
-    threads = blas_threads()
     B = len(prompts)
     nb = B * (-(-max(len(p) for p in prompts) // 16) + 1)
     ref = RefPrefixCache(nb)
     rng = np.random.default_rng(7)
-    t_total, done = 0.0, 0
+    t_total, c_total, done = 0.0, 0.0, 0
     # warm the cache with the first request (not timed), as the timed steps find it warm
     c = ref.add_seq_cached(-1, prompts[0])
     ref.append_tokens(-1, len(prompts[0]) - c)
@@ -532,6 +703,7 @@ def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
             break
         k = rng.standard_normal((len(p), Hkv, D)).astype(np.float32)
         v = rng.standard_normal((len(p), Hkv, D)).astype(np.float32)
+        c0 = time.process_time()
         t0 = time.perf_counter()
         c = ref.add_seq_cached(i, p)
         ref.append_tokens(i, len(p) - c)
@@ -539,8 +711,10 @@ def prefix_cpu_baseline(args, prompts, H, Hkv, D, scale):
         q = rng.standard_normal((len(p) - c, H, D)).astype(np.float32)
         OA.chunk_attention(q, k, v, scale)
         t_total += time.perf_counter() - t0
+        c_total += time.process_time() - c0
         done += 1
-    return {"value": done / t_total, "unit": "requests/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / t_total, "unit": "requests/s", "cores": round(c_total / t_total, 2),
+            "kind": "oracle", "host": host_info(),
             "sample": f"{done} of the step's {B} requests: oracle prefix-cache admission and "
                       f"float64 attention of their new tokens, {t_total:.1f} s"}
 
@@ -667,7 +841,8 @@ def main():
     _native.lib()
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
-    wl = make_workload(args.workload, grow=K + W)
+    F = args.flush_steps
+    wl = make_workload(args.workload, grow=K + W + F)
     B, H, Hkv, D = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim
     log(f"workload {wl.cfg_id} ({wl.name}): B={B} H={H} Hkv={Hkv} D={D} {wl.dtype_name}, "
         f"ctx mean {wl.ctx_lens.mean():.0f} max {wl.ctx_lens.max()}, pool {wl.num_blocks} blocks")
@@ -696,11 +871,11 @@ def main():
     segs.clear()
     sids = [op[1] for op in wl.step]
     bsz = args.block_size
-    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W) // bsz) * (bsz // 16)   # in 16-token tiles
+    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W + F) // bsz) * (bsz // 16)   # in 16-token tiles
     batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, staging=args.staging)
     q = wl.q().to(dev)
     steps_kv = []
-    for i in range(K + W):
+    for i in range(K + W + F):
         k, v = new_token_kv(wl.seed, i, B, Hkv, D, wl.dtype)
         steps_kv.append((k.to(dev), v.to(dev)))
     torch.cuda.synchronize()
@@ -726,8 +901,9 @@ def main():
     # the timed region.
     sampled = [j for j in range(K) if j % EVENT_EVERY == 0]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sampled]
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(F)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for e in [start, stop] + [x for pair in ev for x in pair]:
+    for e in [start, stop] + [x for pair in ev + fev for x in pair]:
         e.record(batch.stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -741,25 +917,67 @@ def main():
     gpu_ms = start.elapsed_time(stop)
     attn_ms = [a.elapsed_time(b) for a, b in ev]
 
+    # Flushed variant (after the timed region): before each of F more steps, a write of
+    # FLUSH_BYTES evicts the pools from L2 and the Infinity Cache, outside the events.
+    flushed_ms = []
+    if F:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        for j in range(F):
+            flush.fill_(j & 0xFF)
+            batch.step(*steps_kv[W + K + j], q, attn_events=fev[j])
+        torch.cuda.synchronize()
+        flushed_ms = [a.elapsed_time(b) for a, b in fev]
+        del flush
+
     kv_read = sum(int((base_ctx + W + j).sum()) * per_tok for j in range(K))
     value = kv_read / wall / 1e9
     attn_avg_ms = float(np.mean(attn_ms))
-    attn_bytes = float(np.mean([step_bytes(W + j) for j in sampled]))
     # HBM minimum: every distinct cached token once.  The block manager counts, per used
     # block, the most tokens any sharer keeps in it; all live sequences are the batch's,
     # and each step adds one private token per sequence.
     occupied = int(cache.bm.stats()["occupied_slots"])
+    last = W + K + F - 1                       # the step the block manager's count is taken at
 
     def unique_bytes(i):
         ctx = base_ctx + i
-        tokens = occupied - B * (W + K - 1 - i)
+        tokens = occupied - B * (last - i)
         return tokens * per_tok + 2 * B * H * D * 2 + int((-(-ctx // 16)).sum()) * 4 + 4 * B
 
-    attn_unique = float(np.mean([unique_bytes(W + j) for j in sampled]))
-    shared = attn_unique < attn_bytes
-    achieved = (attn_unique if shared else attn_bytes) / (attn_avg_ms * 1e-3) / 1e9
+    shared = unique_bytes(W) < step_bytes(W)
+
+    def launch_bytes(i):                       # the roofline's bytes of the attention pass
+        return unique_bytes(i) if shared else step_bytes(i)
+
+    def mean_bytes(steps, warmup, every=1):    # per launch over a run's timed steps
+        return float(np.mean([launch_bytes(warmup + j) for j in range(0, steps, every)]))
+
+    attn_bytes = float(np.mean([step_bytes(W + j) for j in sampled]))
+    roof_bytes = mean_bytes(K, W, EVENT_EVERY)
+    achieved = roof_bytes / (attn_avg_ms * 1e-3) / 1e9
+    med, p10, p90 = (float(x) * 1e3 for x in np.percentile(attn_ms, [50, 10, 90]))
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms, attention pass "
-        f"{attn_avg_ms * 1e3:.1f} us avg (min {min(attn_ms) * 1e3:.1f}, max {max(attn_ms) * 1e3:.1f})")
+        f"{attn_avg_ms * 1e3:.1f} us avg (median {med:.1f}, p10 {p10:.1f}, p90 {p90:.1f})")
+    kname = f"decode_attn_kernel<{wl.dtype_name.upper()},{D}" + (",FP8>" if fp8 else ">")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update(traffic_fields(recorded_traffic(args) if bsz == 16 else None,
+                               lambda s_, w_: mean_bytes(s_, w_)))
+    roof.update({"kernel": kname, "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+                 "median_us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                 "samples": len(attn_ms), "bytes_per_launch": int(roof_bytes)})
+    if flushed_ms:
+        f_bytes = float(np.mean([launch_bytes(W + K + j) for j in range(F)]))
+        f_avg = float(np.mean(flushed_ms))
+        fm, f10, f90 = (float(x) * 1e3 for x in np.percentile(flushed_ms, [50, 10, 90]))
+        roof["flushed_frac"] = round(f_bytes / (f_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        roof["flushed"] = {"avg_us": round(f_avg * 1e3, 2), "median_us": round(fm, 2),
+                           "p10_us": round(f10, 2), "p90_us": round(f90, 2), "samples": F,
+                           "bytes_per_launch": int(f_bytes),
+                           "flush": f"{FLUSH_BYTES >> 20} MiB written before each launch"}
+        log(f"flushed: {F} steps, attention pass {f_avg * 1e3:.1f} us avg (median {fm:.1f}, "
+            f"p10 {f10:.1f}, p90 {f90:.1f}), frac {roof['flushed_frac']}")
+    if not fp8 and D == 128 and bsz == 16 and not args.no_ceiling:
+        roof["ceiling"] = read_ceiling(cache, sids, max_blocks, wl, dev, achieved)
 
     result = {
         "metric": METRIC,
@@ -782,13 +1000,7 @@ def main():
         "pool_waste": round(cache.bm.stats()["waste"], 4),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(B * K / wall, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 or bsz != 16 else recorded_traffic(args, K, W),
-                     "kernel": f"decode_attn_kernel<{wl.dtype_name.upper()},{D}"
-                               + (",FP8>" if fp8 else ">"),
-                     "avg_launch_us": round(attn_avg_ms * 1e3, 2),
-                     "bytes_per_launch": int(attn_unique if shared else attn_bytes)},
+        "roofline": roof,
     }
     if shared:
         # aliased blocks: the roofline counts each shared block once (what HBM must
@@ -796,6 +1008,10 @@ def main():
         result["roofline"]["accounting"] = "unique cached tokens (shared blocks once)"
         result["roofline"]["bytes_per_launch_logical"] = int(attn_bytes)
         result["roofline"]["achieved_logical"] = round(attn_bytes / (attn_avg_ms * 1e-3) / 1e9, 1)
+    del cache, batch, steps_kv
+    torch.cuda.empty_cache()
+    if not args.no_other_ops:
+        result["other_ops"] = other_ops(dev)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

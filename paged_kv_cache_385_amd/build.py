@@ -66,9 +66,12 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     n_o = os.path.join(BUILD, "decode_noalloc.o")
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "decode_noalloc.hip"), "-o",
           n_o], verbose)
+    p_o = os.path.join(BUILD, "hbm_probe.o")
+    _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "hbm_probe.hip"), "-o", p_o],
+         verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, n_o, "-o",
-          tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, n_o, p_o,
+          "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

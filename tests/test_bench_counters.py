@@ -2,7 +2,8 @@
 
 The summary scales each counter by what it read for a calibration copy of known size,
 takes the last --steps calls (a call may be an attention and a merge launch), and stamps
-the result with the kernel source; the bench line uses it only while stamp and run match.
+the result with the kernel source; the bench line uses it only while the stamp and the workload
+match, and reports it with the counter run's own algorithmic bytes.
 """
 
 import csv
@@ -31,11 +32,16 @@ def _counter_csv(path, name, calib_value, launches, values):
 
 def _args(tmp_path, chunk, fetch, write, steps=4, warmup=2):
     return types.SimpleNamespace(chunk=chunk, workload=3, steps=steps, warmup=warmup,
-                                 copy_calibration=1, summarize_counters=[str(fetch), str(write)])
+                                 kv_dtype="native", copy_calibration=1,
+                                 summarize_counters=[str(fetch), str(write)])
+
+
+def _leg(chunk=None, workload=3, kv_dtype="native"):
+    return types.SimpleNamespace(chunk=chunk, workload=workload, kv_dtype=kv_dtype)
 
 
 def test_decode_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
-    out = tmp_path / "decode.json"
+    out = tmp_path / "decode_{mode}.json"
     path, src, names = bench.TRAFFIC["decode"]
     monkeypatch.setitem(bench.TRAFFIC, "decode", (str(out), src, names))
     k = "void decode_attn_kernel<BF16, 128>(DecodeArgs)"
@@ -43,17 +49,29 @@ def test_decode_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", 512, [k] * 6, [9, 9, 100, 100, 110, 110])
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", 1024, [k] * 6, [1, 1, 4, 4, 4, 4])
     bench.summarize_counters(_args(tmp_path, None, tmp_path / "f.csv", tmp_path / "w.csv"))
-    t = json.loads(out.read_text())
+    t = json.loads((tmp_path / "decode_w3.json").read_text())
+    assert t["workload"] == "w3"
     assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
     assert t["launches"] == 4                                 # the warm-up launches are dropped
     assert t["fetch_bytes_per_launch"] == int(105 * 1024 * 2)
     assert t["write_bytes_per_launch"] == 4 * 1024
     assert t["traffic_bytes_per_launch"] == 105 * 2048 + 4096
     assert t["source_sha256"] == bench.source_sha256(src)
-    args = types.SimpleNamespace(chunk=None, workload=3)
-    assert bench.recorded_traffic(args, 4, 2) == t["traffic_bytes_per_launch"]
-    assert bench.recorded_traffic(args, 5, 2) is None         # another run shape
-    assert bench.recorded_traffic(types.SimpleNamespace(chunk=None, workload=2), 4, 2) is None
+    rec = bench.recorded_traffic(_leg())
+    assert rec["traffic_bytes_per_launch"] == t["traffic_bytes_per_launch"]
+    assert bench.recorded_traffic(_leg(workload=2)) is None            # another workload
+    assert bench.recorded_traffic(_leg(kv_dtype="fp8")) is None        # another pool type
+    # the bench line: the counter run's bytes, and their ratio to that run's algorithmic bytes
+    seen = []
+
+    def alg(steps, warmup):
+        seen.append((steps, warmup))
+        return 105 * 1024
+    f = bench.traffic_fields(rec, alg)
+    assert seen == [(4, 2)]
+    assert f["traffic"] == t["traffic_bytes_per_launch"]
+    assert f["traffic_ratio"] == round((105 * 2048 + 4096) / (105 * 1024), 4)
+    assert bench.traffic_fields(None, alg) == {"traffic": None}
 
 
 def test_chunk_summary_sums_the_launches_of_a_call(tmp_path, monkeypatch):
@@ -69,6 +87,6 @@ def test_chunk_summary_sums_the_launches_of_a_call(tmp_path, monkeypatch):
     assert t["workload"] == "chunk-verify" and t["launches"] == 8
     assert t["fetch_bytes_per_launch"] == 55 * 1024 * 2       # per call: attention + merge
     assert t["write_bytes_per_launch"] == 4 * 1024
-    assert bench.recorded_traffic(types.SimpleNamespace(chunk="verify", workload=3), 4, 2) \
+    assert bench.recorded_traffic(_leg("verify"))["traffic_bytes_per_launch"] \
         == t["traffic_bytes_per_launch"]
-    assert bench.recorded_traffic(types.SimpleNamespace(chunk="prefill", workload=3), 4, 2) is None
+    assert bench.recorded_traffic(_leg("prefill")) is None
