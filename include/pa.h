@@ -323,8 +323,9 @@ const char* pa_last_error(void);
  * slots keep their numbering (32 b + i is tile 2 b + i / 16, position i % 16);
  * pa_bm_pack and pa_bm_step write tables in tiles (max_blocks counts tiles);
  * copy-on-write pairs from the append calls are in manager blocks, a pair (s, d)
- * meaning tile copies (2 s, 2 d) and (2 s + 1, 2 d + 1) (pa_decode_step expands
- * them itself).  Prefix caching and swapping need 16-token blocks.
+ * meaning tile copies (2 s, 2 d) and (2 s + 1, 2 d + 1) (pa_bm_tile_pairs expands
+ * them; pa_decode_step does so itself).  Prefix caching and swapping need 16-token
+ * blocks.
  * ======================================================================== */
 typedef struct pa_bm pa_bm;
 
@@ -376,6 +377,14 @@ pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
 pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slots,
                      int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow, int32_t* tables,
                      int32_t max_blocks, int32_t* ctx_lens, int32_t* max_ctx);
+/* Copy-on-write pairs of manager blocks (n pairs, host int32[n][2]) as the pairs of
+ * pool tiles that pa_copy_blocks takes: the same pairs with 16-token blocks; with
+ * 32-token blocks each pair (s, d) becomes (2 s, 2 d), (2 s + 1, 2 d + 1), in order.
+ * tile_pairs (host int32[cap][2]) may be `pairs` itself (expanded in place);
+ * *n_tiles receives the number of tile pairs.  PA_ERR_INVALID_ARG when cap is too
+ * small (nothing written). */
+pa_status pa_bm_tile_pairs(const pa_bm* bm, const int32_t* pairs, int32_t n, int32_t* tile_pairs,
+                           int32_t cap, int32_t* n_tiles);
 
 /* ---------------------------------------------------------------------------
  * Automatic prefix caching (host only).  A request whose leading tokens equal an

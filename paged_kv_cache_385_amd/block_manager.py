@@ -133,6 +133,16 @@ class BlockManager:
                 "pa_bm_free_list")
         return out[:n.value].tolist()
 
+    def tile_pairs(self, pairs) -> np.ndarray:
+        """Copy-on-write pairs of manager blocks as pairs of pool tiles (pa_bm_tile_pairs)."""
+        p = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        cap = 2 * max(1, p.shape[0])
+        out = np.empty((cap, 2), dtype=np.int32)
+        n = C.c_int32()
+        N.check(self._lib.pa_bm_tile_pairs(self._h, _ptr(p), p.shape[0], _ptr(out), cap,
+                                           C.byref(n)), "pa_bm_tile_pairs")
+        return out[:n.value]
+
     def stats(self) -> dict:
         st = N.PaBmStats()
         N.check(self._lib.pa_bm_stats_get(self._h, C.byref(st)), "pa_bm_stats_get")

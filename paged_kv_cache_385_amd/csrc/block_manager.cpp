@@ -500,7 +500,7 @@ pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32
   const Seq* s = bm->find(seq_id);
   if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_block_table: no sequence %lld", (long long)seq_id);
   const int32_t m = static_cast<int32_t>(s->table.size());
-  std::memcpy(out, s->table.data(), sizeof(int32_t) * std::min(m, cap));
+  std::copy_n(s->table.begin(), std::min(m, cap), out);   // (memcpy of nothing from NULL is UB)
   *n = m;
   return PA_OK;
 }
@@ -525,7 +525,7 @@ pa_status pa_bm_pack(const pa_bm* bm, int32_t n, const int64_t* seq_ids, int32_t
     int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
     const int32_t m = static_cast<int32_t>(s->table.size());
     if (f == 1) {
-      std::memcpy(row, s->table.data(), sizeof(int32_t) * m);
+      std::copy_n(s->table.begin(), m, row);
     } else {
       for (int32_t j = 0; j < m; ++j)
         for (int32_t t = 0; t < f; ++t) row[j * f + t] = s->table[j] * f + t;
@@ -561,6 +561,26 @@ pa_status pa_bm_step(pa_bm* bm, int32_t n, const int64_t* seq_ids, int64_t* slot
   int32_t m = 0;
   for (int32_t i = 0; i < n; ++i) m = std::max(m, ctx_lens[i]);
   *max_ctx = m;
+  return PA_OK;
+}
+
+pa_status pa_bm_tile_pairs(const pa_bm* bm, const int32_t* pairs, int32_t n, int32_t* tile_pairs,
+                           int32_t cap, int32_t* n_tiles) {
+  if (!bm || n < 0 || (n > 0 && (!pairs || !tile_pairs)) || !n_tiles)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_tile_pairs: bad arguments");
+  const int32_t f = bm->block_size / PA_BLOCK_SIZE;        // tiles per manager block
+  if (static_cast<int64_t>(n) * f > cap)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_tile_pairs: %d pairs need %lld tile pairs, cap %d", n,
+                    static_cast<long long>(n) * f, cap);
+  // last pair first, so expanding in place never overwrites a pair not yet read
+  for (int32_t i = n - 1; i >= 0; --i) {
+    const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    for (int32_t j = f - 1; j >= 0; --j) {
+      tile_pairs[2 * (f * i + j)] = f * src + j;
+      tile_pairs[2 * (f * i + j) + 1] = f * dst + j;
+    }
+  }
+  *n_tiles = n * f;
   return PA_OK;
 }
 
@@ -987,7 +1007,7 @@ pa_status pa_bm_host_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_
     return pa::fail(PA_ERR_NOT_FOUND, "pa_bm_host_table: no swapped-out sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& t = it->second.table;
   const int32_t m = static_cast<int32_t>(t.size());
-  std::memcpy(out, t.data(), sizeof(int32_t) * std::min(m, cap));
+  std::copy_n(t.begin(), std::min(m, cap), out);
   *n = m;
   return PA_OK;
 }

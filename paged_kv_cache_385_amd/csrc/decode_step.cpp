@@ -92,18 +92,10 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   st = pa_bm_step(bm, num_seqs, seq_ids, slots_h, pairs_h, num_seqs, &n_cow, tables_h,
                   max_blocks_per_seq, ctx_h, &max_ctx);
   if (st != PA_OK) return st;
-  const int32_t f = pa::bm_tiles_per_block(bm);
-  if (f == 2) {
-    // each copied 32-token block is two tile copies: expand in place, last pair first
-    for (int32_t i = n_cow - 1; i >= 0; --i) {
-      const int32_t src = pairs_h[2 * i], dst = pairs_h[2 * i + 1];
-      pairs_h[4 * i] = 2 * src;
-      pairs_h[4 * i + 1] = 2 * dst;
-      pairs_h[4 * i + 2] = 2 * src + 1;
-      pairs_h[4 * i + 3] = 2 * dst + 1;
-    }
-    n_cow *= 2;
-  }
+  // pairs of manager blocks -> pairs of pool tiles (two per 32-token block), in place;
+  // the staging area holds two tile pairs per sequence
+  st = pa_bm_tile_pairs(bm, pairs_h, n_cow, pairs_h, 2 * num_seqs, &n_cow);
+  if (st != PA_OK) return st;
   if (info) {
     info->num_cow = n_cow;
     info->max_context_len = max_ctx;

@@ -50,6 +50,11 @@ constexpr int kMaxParts = 1024;                             // longest context /
 #define PA_SIZE_CLASSES 4
 #endif
 constexpr int kClasses = PA_SIZE_CLASSES;                   // size classes of last partitions
+// pa_cache_write calls with at least this many tokens take the whole-block kernel
+#ifndef PA_BULK_WRITE_TOKENS
+#define PA_BULK_WRITE_TOKENS 64
+#endif
+constexpr int kBulkTokens = PA_BULK_WRITE_TOKENS;
 static_assert(kClasses >= 1 && kClasses <= 64, "one lane per size class");
 
 // ---- cache write -----------------------------------------------------------------
@@ -78,6 +83,67 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   uint16_t* vdst = v_cache + tile + (static_cast<int64_t>(off >> 2) * D + 8 * c) * 4 + (off & 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i) vdst[4 * i] = vv[i];
+}
+
+// Bulk form: one workgroup of 2*D threads per (16 consecutive tokens of the input,
+// KV head).  When those 16 tokens fill one whole block in order (slots 16j ..
+// 16j + 15, what a prefill or an admission stores), the workgroup writes the
+// block's K and V tiles of that head front to back, 16 bytes per thread each:
+//   thread i, K: dims 8(i/16) .. +7 of token i%16, one 16-byte load;
+//   thread i, V: dims 2m, 2m+1 of tokens 4(i/(D/2)) .. +3, m = i % (D/2): four
+//   4-byte loads, one per token, each a contiguous run across the wave.
+// Any other group (a partial block, slots out of order or out of range, the
+// input's ragged end) stores its tokens one element group at a time, as
+// cache_write_kernel does.
+template <int D>
+__global__ __launch_bounds__(2 * D) void cache_write_bulk_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, int32_t num_tokens, int32_t hkv, int64_t num_slots) {
+  constexpr int kThreadsB = 2 * D;
+  constexpr int kChunks = D / 8;
+  const int32_t i = threadIdx.x;
+  const int32_t h = blockIdx.y;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBlock;
+  const int64_t s0 = t0 + kBlock <= num_tokens ? slots[t0] : -1;
+  bool whole = s0 >= 0 && (s0 & (kBlock - 1)) == 0 && s0 + kBlock <= num_slots;
+  if (whole) {
+#pragma unroll
+    for (int j = 1; j < kBlock; ++j) whole = whole && slots[t0 + j] == s0 + j;
+  }
+  const int64_t row = static_cast<int64_t>(hkv) * D;            // elements per input token
+  if (whole) {
+    const int64_t tile = ((s0 >> 4) * hkv + h) * (kBlock * D);
+    const int32_t kt = i & 15, kc = i >> 4;
+    store16(k_cache + tile + 8 * i, load16(k + (t0 + kt) * row + h * D + 8 * kc));
+    const int32_t quad = i / (D / 2), m = i % (D / 2);
+    const uint16_t* vs = v + (t0 + 4 * quad) * row + h * D + 2 * m;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint32_t*>(vs + j * row);
+    // [dim 2m][token 4quad .. +3], then [dim 2m + 1][...]
+    const u32x4 out = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16),
+                       (w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+    store16(v_cache + tile + 8 * i, out);
+    return;
+  }
+  // element groups (token, 8-dim chunk) of this head: 16 x D/8 <= 2D threads
+  static_assert(kBlock * kChunks <= kThreadsB, "one element group per thread");
+  if (i >= kBlock * kChunks) return;
+  const int64_t t = t0 + i / kChunks;
+  const int32_t c = i % kChunks;
+  if (t >= num_tokens) return;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int32_t off = static_cast<int32_t>(slot & 15);
+  const int64_t src = t * row + h * D + 8 * c;
+  const int64_t tile = (blk * hkv + h) * (kBlock * D);
+  store16(k_cache + tile + (static_cast<int64_t>(c) * kBlock + off) * 8, load16(k + src));
+  const u16x8 vv = __builtin_bit_cast(u16x8, load16(v + src));
+  uint16_t* vdst = v_cache + tile + (static_cast<int64_t>(off >> 2) * D + 8 * c) * 4 + (off & 3);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vdst[4 * e] = vv[e];
 }
 
 // FP8 pools: the same thread map; the 8 dims of a thread are 8 consecutive bytes
@@ -1186,6 +1252,18 @@ pa_status pa_cache_write(const pa_cache* cache, const void* k, const void* v,
   }
   auto kc = static_cast<uint16_t*>(cache->k_cache);
   auto vc = static_cast<uint16_t*>(cache->v_cache);
+  if (num_tokens >= kBulkTokens && cache->num_kv_heads <= 65535) {
+    // many tokens (a prefill, an admission): whole blocks are written tile by tile
+    const dim3 g(static_cast<uint32_t>((num_tokens + kBlock - 1) / kBlock),
+                 static_cast<uint32_t>(cache->num_kv_heads));
+    if (D == 64)
+      cache_write_bulk_kernel<64><<<g, dim3(128), 0, s>>>(kp, vp, slot_mapping, kc, vc, num_tokens,
+                                                          cache->num_kv_heads, num_slots);
+    else
+      cache_write_bulk_kernel<128><<<g, dim3(256), 0, s>>>(kp, vp, slot_mapping, kc, vc, num_tokens,
+                                                           cache->num_kv_heads, num_slots);
+    return launch_status("pa_cache_write");
+  }
   if (D == 64)
     cache_write_kernel<64><<<dim3(grid), dim3(256), 0, s>>>(kp, vp, slot_mapping, kc, vc, num_tokens,
                                                            cache->num_kv_heads, num_slots);

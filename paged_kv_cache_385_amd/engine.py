@@ -96,8 +96,7 @@ class PagedKVCache:
         pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
         if len(pairs) == 0:
             return
-        if self.tiles_per_block == 2:                    # block b = tiles 2 b, 2 b + 1
-            pairs = np.ascontiguousarray(np.stack([2 * pairs, 2 * pairs + 1], 1).reshape(-1, 2))
+        pairs = self.bm.tile_pairs(pairs)                # block b = tiles 2 b, 2 b + 1
         ops.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(pairs).to(self.device),
                         pairs_host=pairs, scales=self.scales)
 

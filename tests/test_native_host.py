@@ -356,6 +356,23 @@ def test_pack_tables_of_32_token_blocks():
         nat.pack([1], 3)                    # 2 blocks are 4 tiles
 
 
+def test_tile_pairs_of_32_token_blocks():
+    """pa_bm_tile_pairs: block pairs as the pool's tile pairs (worked by hand), in place."""
+    lib = N.lib()
+    n16, n32 = BlockManager(8, 16), BlockManager(8, 32)
+    pairs = np.array([[3, 0], [5, 7]], dtype=np.int32)
+    assert n16.tile_pairs(pairs).tolist() == [[3, 0], [5, 7]]
+    assert n32.tile_pairs(pairs).tolist() == [[6, 0], [7, 1], [10, 14], [11, 15]]
+    assert n32.tile_pairs(np.zeros((0, 2), np.int32)).shape == (0, 2)
+    buf = np.zeros((4, 2), dtype=np.int32)
+    buf[:2] = pairs
+    n = C.c_int32()
+    assert lib.pa_bm_tile_pairs(n32._h, buf.ctypes.data, 2, buf.ctypes.data, 4, C.byref(n)) == N.PA_OK
+    assert n.value == 4 and buf.tolist() == [[6, 0], [7, 1], [10, 14], [11, 15]]
+    assert lib.pa_bm_tile_pairs(n32._h, pairs.ctypes.data, 2, buf.ctypes.data, 3,
+                                C.byref(n)) == N.PA_ERR_INVALID_ARG
+
+
 # ---- the step entry points ---------------------------------------------------------------
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("seed", range(4))
