@@ -86,15 +86,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 }
 
 // Bulk form: one workgroup of 2*D threads per (16 consecutive tokens of the input,
-// KV head).  When those 16 tokens fill one whole block in order (slots 16j ..
-// 16j + 15, what a prefill or an admission stores), the workgroup writes the
-// block's K and V tiles of that head front to back, 16 bytes per thread each:
-//   thread i, K: dims 8(i/16) .. +7 of token i%16, one 16-byte load;
+// KV head).  A whole block is a run of 16 consecutive input tokens whose slots are
+// 16j .. 16j + 15 in order (what a prefill or an admission stores, wherever the
+// run starts in the input); at most one such run starts within any 16 tokens.  The
+// workgroup writes the run that starts among its tokens, if any, as the block's K
+// and V tiles of that head front to back, 16 bytes per thread each:
+//   thread i, K: dims 8(i/16) .. +7 of token i%16 of the run, one 16-byte load;
 //   thread i, V: dims 2m, 2m+1 of tokens 4(i/(D/2)) .. +3, m = i % (D/2): four
 //   4-byte loads, one per token, each a contiguous run across the wave.
-// Any other group (a partial block, slots out of order or out of range, the
-// input's ragged end) stores its tokens one element group at a time, as
-// cache_write_kernel does.
+// Its tokens outside any whole block (partial blocks, slots out of order, skipped
+// or out-of-range slots) are stored one element group at a time, as
+// cache_write_kernel does; its tokens inside a run that started in the previous
+// group are left to that group's workgroup.
 template <int D>
 __global__ __launch_bounds__(2 * D) void cache_write_bulk_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -102,18 +105,40 @@ __global__ __launch_bounds__(2 * D) void cache_write_bulk_kernel(
     uint16_t* __restrict__ v_cache, int32_t num_tokens, int32_t hkv, int64_t num_slots) {
   constexpr int kThreadsB = 2 * D;
   constexpr int kChunks = D / 8;
+  constexpr int kWin = 3 * kBlock - 1;           // tokens g0 - 15 .. g0 + 31
+  static_assert(kThreadsB >= 64 && kBlock * kChunks <= kThreadsB, "one element group per thread");
+  __shared__ int64_t s_slot[kWin];
+  __shared__ int32_t s_prev, s_start;
   const int32_t i = threadIdx.x;
   const int32_t h = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBlock;
-  const int64_t s0 = t0 + kBlock <= num_tokens ? slots[t0] : -1;
-  bool whole = s0 >= 0 && (s0 & (kBlock - 1)) == 0 && s0 + kBlock <= num_slots;
-  if (whole) {
-#pragma unroll
-    for (int j = 1; j < kBlock; ++j) whole = whole && slots[t0 + j] == s0 + j;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kBlock;
+  for (int32_t j = i; j < kWin; j += kThreadsB) {
+    const int64_t t = g0 - (kBlock - 1) + j;
+    s_slot[j] = t >= 0 && t < num_tokens ? slots[t] : -1;
   }
+  __syncthreads();
+  if (i < 64) {
+    // lane j < 31: does a whole block start at token g0 - 15 + j?
+    bool start = false;
+    if (i < 2 * kBlock - 1) {
+      const int64_t s0 = s_slot[i];
+      start = s0 >= 0 && (s0 & (kBlock - 1)) == 0 && s0 + kBlock <= num_slots;
+      for (int j = 1; j < kBlock && start; ++j) start = s_slot[i + j] == s0 + j;
+    }
+    const uint64_t m = __ballot(start);
+    if (i == 0) {
+      const uint64_t prev = m & ((1ull << (kBlock - 1)) - 1);   // starts before g0
+      const uint64_t cur = m >> (kBlock - 1);                   // starts at g0 .. g0 + 15
+      s_prev = prev ? __ffsll(static_cast<unsigned long long>(prev)) : 0;   // tokens covered
+      s_start = cur ? __ffsll(static_cast<unsigned long long>(cur)) - 1 : -1;
+    }
+  }
+  __syncthreads();
+  const int32_t covered_prev = s_prev, start = s_start;
   const int64_t row = static_cast<int64_t>(hkv) * D;            // elements per input token
-  if (whole) {
-    const int64_t tile = ((s0 >> 4) * hkv + h) * (kBlock * D);
+  if (start >= 0) {
+    const int64_t t0 = g0 + start;
+    const int64_t tile = ((s_slot[kBlock - 1 + start] >> 4) * hkv + h) * (kBlock * D);
     const int32_t kt = i & 15, kc = i >> 4;
     store16(k_cache + tile + 8 * i, load16(k + (t0 + kt) * row + h * D + 8 * kc));
     const int32_t quad = i / (D / 2), m = i % (D / 2);
@@ -125,15 +150,15 @@ __global__ __launch_bounds__(2 * D) void cache_write_bulk_kernel(
     const u32x4 out = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16),
                        (w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
     store16(v_cache + tile + 8 * i, out);
-    return;
   }
-  // element groups (token, 8-dim chunk) of this head: 16 x D/8 <= 2D threads
-  static_assert(kBlock * kChunks <= kThreadsB, "one element group per thread");
+  // the group's other tokens, one (token, 8-dim chunk) per thread
   if (i >= kBlock * kChunks) return;
-  const int64_t t = t0 + i / kChunks;
+  const int32_t r = i / kChunks;                 // token g0 + r
   const int32_t c = i % kChunks;
+  if (r < covered_prev || (start >= 0 && r >= start)) return;
+  const int64_t t = g0 + r;
   if (t >= num_tokens) return;
-  const int64_t slot = slots[t];
+  const int64_t slot = s_slot[kBlock - 1 + r];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot >> 4;
   const int32_t off = static_cast<int32_t>(slot & 15);

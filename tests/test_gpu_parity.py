@@ -342,15 +342,21 @@ def test_no_write_lands_outside_the_pools(cfg):
 def _mixed_slots(rng, nb):
     """A slot mapping that mixes every case the bulk store distinguishes: whole blocks in
     order aligned with the 16-token groups, a whole block in shuffled order, a partial
-    block, skipped (negative) and out-of-range slots, then whole blocks that straddle
-    the groups, and a ragged end."""
+    block, skipped (negative) and out-of-range slots, whole blocks that straddle the
+    groups, prompts of ragged length back to back (their whole blocks start anywhere in
+    a group), and a ragged end."""
     blocks = rng.permutation(nb)
     segs = [np.arange(16) + 16 * int(b) for b in blocks[:3]]                 # aligned, whole
     segs.append(rng.permutation(16) + 16 * int(blocks[3]))                   # whole, shuffled
     segs.append(np.arange(3, 13) + 16 * int(blocks[4]))                      # partial
     segs.append(np.array([-1, -7, 16 * nb, 16 * nb + 5, -1]))                # skipped / out of range
     segs += [np.arange(16) + 16 * int(b) for b in blocks[5:8]]               # whole, straddling
-    segs.append(np.arange(9) + 16 * int(blocks[8]))                          # ragged end
+    pos = 8
+    for n in (37, 50, 21):          # prompts of ragged length in their own blocks, back to back
+        bl = blocks[pos:pos + (n + 15) // 16]
+        pos += len(bl)
+        segs.append((bl[:, None] * 16 + np.arange(16)).ravel()[:n])
+    segs.append(np.arange(9) + 16 * int(blocks[pos]))                        # ragged end
     return np.concatenate(segs).astype(np.int64)
 
 
