@@ -261,6 +261,8 @@ struct DecodeArgs {
   int32_t max_blocks, max_ctx, num_blocks, max_parts;
   int32_t part_blocks;  // blocks per partition (32 .. 256)
   int32_t part_shift;   // log2(part_blocks)
+  int32_t head_groups;  // work items per (sequence, partition): num_kv_heads >> heads_shift
+  int32_t heads_shift;  // log2 of the KV heads one item covers (0, 1 or 2)
   float scale_log2;     // scale * log2(e)
 };
 
@@ -331,10 +333,11 @@ __device__ __forceinline__ void load_ctx_group(const DecodeArgs& a, int32_t c0, 
   }
 }
 
-// Work item of this workgroup.  Every partition of every sequence and KV head is
-// one item; the list holds the full partitions first, ordered (KV head, sequence,
-// partition), then the last, shorter partitions from the largest size class to
-// the smallest, ordered (KV head, sequence) within a class -- big items start
+// Work item of this workgroup.  Every partition of every sequence and group of
+// 2^heads_shift KV heads is one item (*okvh returns the group); the list holds the
+// full partitions first, ordered (KV head group, sequence, partition), then the
+// last, shorter partitions from the largest size class to the smallest, ordered
+// (KV head group, sequence) within a class -- big items start
 // first so the short ones fill the tail.  Workgroup ids are mapped to list
 // positions so that each of the 8 XCDs (which take workgroup ids round-robin)
 // gets 8 consecutive positions out of every 64.  Returns false for a workgroup
@@ -343,7 +346,7 @@ __device__ __forceinline__ void load_ctx_group(const DecodeArgs& a, int32_t c0, 
 // item's context length comes back in *octx.
 __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_t* okvh,
                           int32_t* op, int32_t* octx) {
-  const int32_t B = a.num_seqs, pbs = a.part_shift, hkv = a.num_kv_heads;
+  const int32_t B = a.num_seqs, pbs = a.part_shift, hkv = a.head_groups;
   constexpr int32_t kGroup = 64 * kPlanChunks;
   int32_t cv0[kPlanChunks];            // the first group, kept for the second pass
   load_ctx_group(a, 0, lane, cv0);
@@ -462,25 +465,36 @@ void decode_attn_kernel(DecodeArgs a) {
   const int32_t tid = threadIdx.x;
   const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t lane = tid & 63;
-  int32_t b, kvh, p, ctx;
-  if (!plan_item(a, lane, &b, &kvh, &p, &ctx)) return;
+  int32_t b, kg, p, ctx;
+  if (!plan_item(a, lane, &b, &kg, &p, &ctx)) return;
   b = __builtin_amdgcn_readfirstlane(b);
-  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  kg = __builtin_amdgcn_readfirstlane(kg);
   p = __builtin_amdgcn_readfirstlane(p);
   ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int32_t G = a.group;
   const int32_t PB = a.part_blocks;
+  // The item covers KV heads kg * hpi .. + hpi - 1; each has wph = 4 / hpi waves, and
+  // this wave works on head kvh with the other waves of that head.
+  const int32_t hsh = a.heads_shift;
+  const int32_t hpi = 1 << hsh;           // KV heads of the item
+  const int32_t wsh = 2 - hsh;            // log2(waves per head)
+  const int32_t wph = 1 << wsh;
+  const int32_t hl = w >> wsh;            // this wave's head within the item
+  const int32_t wi = w & (wph - 1);       // this wave among its head's waves
+  const int32_t kvh = kg * hpi + hl;
 
-  if (b >= a.num_seqs || kvh >= a.num_kv_heads) return;   // cannot happen; keeps every read in bounds
+  if (b >= a.num_seqs || kg >= a.head_groups) return;   // cannot happen; keeps every read in bounds
   const bool bad_ctx = ctx < 1 || ctx > a.max_ctx;
   const int32_t nparts = bad_ctx ? 1 : (ctx + PB * kBlock - 1) / (PB * kBlock);
   if (p < 0 || p >= nparts) return;
   const int32_t n = lane & 15;       // query head within the group (MFMA column)
   const int32_t g4 = lane >> 4;      // token quad within a block (MFMA row group)
-  const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G) * D;
+  const int32_t rows = hpi * G;      // output rows of the item: heads kg * hpi * G .. + rows - 1
+  const int64_t item_row0 = (static_cast<int64_t>(b) * a.num_heads + kg * rows) * D;
+  const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G) * D;   // this wave's
 
   if (bad_ctx) {
-    for (int32_t i = tid; i < G * D; i += kThreads) a.out[q_row0 + i] = E::kNaN;
+    for (int32_t i = tid; i < rows * D; i += kThreads) a.out[item_row0 + i] = E::kNaN;
     return;
   }
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -493,11 +507,11 @@ void decode_attn_kernel(DecodeArgs a) {
                      : u32x4{0, 0, 0, 0};
   }
 
-  // This wave's blocks are first, first + 4, ... below jend (at most PB / 4 of them).
+  // This wave's blocks are first, first + wph, ... below jend (at most PB / wph of them).
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
   const int32_t jend = min(nblk, (p + 1) * PB);
-  const int32_t first = p * PB + w;
-  const int32_t nw = first < jend ? (jend - first + kWaves - 1) / kWaves : 0;
+  const int32_t first = p * PB + wi;
+  const int32_t nw = first < jend ? (jend - first + wph - 1) >> wsh : 0;
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t head_off = static_cast<int64_t>(kvh) * tile_elems;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
@@ -509,7 +523,7 @@ void decode_attn_kernel(DecodeArgs a) {
   // All of the wave's block ids in one load: lane i holds the id of its i-th block,
   // so no table read sits between two tile loads.
   int32_t ids = 0;
-  if (lane < nw) ids = bt[first + kWaves * lane];
+  if (lane < nw) ids = bt[first + wph * lane];
   const bool id_bad = lane < nw && (ids < 0 || ids >= a.num_blocks);
   if (id_bad) ids = 0;
 
@@ -531,8 +545,8 @@ void decode_attn_kernel(DecodeArgs a) {
   if (!kFp8 && a.new_slots != nullptr && p == nparts - 1) {
     const int64_t slot = a.new_slots[b];
     const int32_t jl = nblk - 1 - p * PB;       // last block, within the partition
-    if (slot >= 0 && (jl & (kWaves - 1)) == w) {
-      st_i = jl / kWaves;
+    if (slot >= 0 && (jl & (wph - 1)) == wi) {
+      st_i = jl >> wsh;
       st_off = (ctx - 1) % kBlock;
       const int32_t phys = __builtin_amdgcn_readlane(ids, st_i);
       const bool phys_bad = __builtin_amdgcn_readlane(id_bad ? 1 : 0, st_i) != 0;
@@ -641,7 +655,7 @@ void decode_attn_kernel(DecodeArgs a) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = E::mfma_qk(K[kk], qf[kk], s);
-    const int32_t valid = i < nw ? ctx - (first + kWaves * i) * kBlock : 0;   // tokens in context
+    const int32_t valid = i < nw ? ctx - (first + wph * i) * kBlock : 0;   // tokens in context
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -716,13 +730,9 @@ void decode_attn_kernel(DecodeArgs a) {
   if (tid == 0) s_bad = 0;
   __syncthreads();
   if (bad_blk) s_bad = 1;
-  float mw[kWaves];
+  // the waves of this wave's head
   float M = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < kWaves; ++u) {
-    mw[u] = s_m[u][n];
-    M = fmaxf(M, mw[u]);
-  }
+  for (int u = hl * wph; u < (hl + 1) * wph; ++u) M = fmaxf(M, s_m[u][n]);
   const float wscale = fast_exp2(m_run - M);   // 0 for a wave that saw no block
   if (n < G) {
     float* row = &s_acc[w][n * kLdsStride];
@@ -738,22 +748,24 @@ void decode_attn_kernel(DecodeArgs a) {
   __syncthreads();
   const bool poisoned = s_bad != 0;
 
-  // each thread finishes 4 consecutive dims of one head
-  for (int32_t i4 = tid; i4 < G * (D / 4); i4 += kThreads) {
-    const int32_t hh = i4 / (D / 4);
-    const int32_t d = (i4 - hh * (D / 4)) * 4;
+  // each thread finishes 4 consecutive dims of one query head of the item: row hr is
+  // column hh of the item's head h2, whose waves are h2 * wph .. + wph - 1
+  for (int32_t i4 = tid; i4 < rows * (D / 4); i4 += kThreads) {
+    const int32_t hr = i4 / (D / 4);
+    const int32_t d = (i4 - hr * (D / 4)) * 4;
+    const int32_t h2 = hr / G;
+    const int32_t hh = hr - h2 * G;
+    const int32_t u0 = h2 * wph;
     float Mh = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kWaves; ++u) Mh = fmaxf(Mh, s_m[u][hh]);
+    for (int u = u0; u < u0 + wph; ++u) Mh = fmaxf(Mh, s_m[u][hh]);
     float L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < kWaves; ++u) {
+    for (int u = u0; u < u0 + wph; ++u) {
       L += s_l[u][hh] * fast_exp2(s_m[u][hh] - Mh);
       o += *reinterpret_cast<const f32x4*>(&s_acc[u][hh * kLdsStride + d]);
     }
-    if (kFp8) o *= a.v_scales[kvh];        // V codes stand for code * v_scale
-    const int64_t row = q_row0 + static_cast<int64_t>(hh) * D;
+    if (kFp8) o *= a.v_scales[kg * hpi + h2];   // V codes stand for code * v_scale
+    const int64_t row = item_row0 + static_cast<int64_t>(hr) * D;
     if (nparts == 1) {
       u16x4 ov;
       if (poisoned) {
@@ -765,7 +777,7 @@ void decode_attn_kernel(DecodeArgs a) {
       }
       *reinterpret_cast<u16x4*>(a.out + row + d) = ov;
     } else {
-      const int64_t st = (static_cast<int64_t>(b) * a.num_heads + kvh * G + hh) * a.max_parts + p;
+      const int64_t st = (static_cast<int64_t>(b) * a.num_heads + kg * rows + hr) * a.max_parts + p;
       if (poisoned) o = f32x4{NAN, NAN, NAN, NAN};
       const float2 ml = poisoned ? float2{0.f, NAN} : float2{Mh, L};
       if (a.counters) {
@@ -784,21 +796,21 @@ void decode_attn_kernel(DecodeArgs a) {
   }
   if (nparts == 1 || a.counters == nullptr) return;
 
-  // Fused merge: the last of the sequence's partitions (for this KV head) to
+  // Fused merge: the last of the sequence's partitions (for these KV heads) to
   // finish combines all of them.  Its partial stores are complete (waited for)
   // before the count is raised, and the merging workgroup reads the states with
   // device-coherent loads after it has seen the count reach nparts - 1.
   __shared__ int32_t s_ticket;
   wait_stores();
   __syncthreads();
-  int32_t* counter = a.counters + static_cast<int64_t>(b) * a.num_kv_heads + kvh;
+  int32_t* counter = a.counters + static_cast<int64_t>(b) * a.head_groups + kg;
   if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_ticket != nparts - 1) return;
-  for (int32_t i4 = tid; i4 < G * (D / 4); i4 += kThreads) {
-    const int32_t hh = i4 / (D / 4);
-    const int32_t d = (i4 - hh * (D / 4)) * 4;
-    const int64_t st0 = (static_cast<int64_t>(b) * a.num_heads + kvh * G + hh) * a.max_parts;
+  for (int32_t i4 = tid; i4 < rows * (D / 4); i4 += kThreads) {
+    const int32_t hr = i4 / (D / 4);
+    const int32_t d = (i4 - hr * (D / 4)) * 4;
+    const int64_t st0 = (static_cast<int64_t>(b) * a.num_heads + kg * rows + hr) * a.max_parts;
     float M = -INFINITY;
     for (int32_t u = 0; u < nparts; ++u) M = fmaxf(M, load_coherent(&a.ws_ml[st0 + u].x));
     float L = 0.f;
@@ -814,7 +826,7 @@ void decode_attn_kernel(DecodeArgs a) {
     u16x4 ov;
 #pragma unroll
     for (int r = 0; r < 4; ++r) ov[r] = E::from_float(o[r] * inv);
-    *reinterpret_cast<u16x4*>(a.out + q_row0 + static_cast<int64_t>(hh) * D + d) = ov;
+    *reinterpret_cast<u16x4*>(a.out + item_row0 + static_cast<int64_t>(hr) * D + d) = ov;
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -971,6 +983,26 @@ int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx)
   return kPartTokens;
 }
 
+// log2 of the KV heads one decode item covers: 1 (two heads, two waves each) when
+// each KV head serves one query head, the pools are 16-bit and B * Hkv / 2 *
+// (partitions at 4096 tokens) items still give every workgroup slot (three per
+// compute unit) 4/3 of one; else 0.  Measured on the 7B-shaped layer: 217.5 against
+// 223 us; four heads per item, and two on FP8 pools, were slower.  The kernel takes
+// shifts up to 2.  PA_HEADS_PER_ITEM=1 in the environment keeps one KV head per item
+// (read once).
+int32_t heads_shift_for(int32_t num_seqs, int32_t num_kv_heads, int32_t group, bool fp8,
+                        int32_t max_ctx) {
+  static const bool off = [] {
+    const char* e = std::getenv("PA_HEADS_PER_ITEM");
+    return e && e[0] == '1';
+  }();
+  if (off || group != 1 || fp8 || num_kv_heads % 2) return 0;
+  const int64_t slots = 3 * static_cast<int64_t>(device_cus());
+  const int64_t items = static_cast<int64_t>(num_seqs) * (num_kv_heads >> 1) *
+                        parts_for(max_ctx, kMaxPartTokens);
+  return 3 * items >= 4 * slots ? 1 : 0;
+}
+
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t ws_ml_bytes(int64_t rows) { return round256(static_cast<size_t>(rows) * sizeof(float2)); }
 // Workspace: counters int32[B][H] (zero between calls) | (max, sum) float2[rows] | acc float[rows][D]
@@ -1032,13 +1064,19 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   if (!valid_part_tokens(part_tokens))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d (0, or a power of two in 512 .. 4096)",
                     fn, part_tokens);
-  const int32_t PT = part_tokens ? part_tokens : part_tokens_for(num_seqs, cache->num_kv_heads, max_ctx);
+  // One query head per KV head (MHA): an item covers 2 KV heads of a sequence while
+  // that still leaves every workgroup slot about 4/3 of an item, so fewer items pay
+  // the start-up of one.
+  const int32_t hsh = heads_shift_for(num_seqs, cache->num_kv_heads, G,
+                                      (cache->flags & PA_CACHE_FP8) != 0, max_ctx);
+  const int32_t groups = cache->num_kv_heads >> hsh;
+  const int32_t PT = part_tokens ? part_tokens : part_tokens_for(num_seqs, groups, max_ctx);
   const int32_t P = parts_for(max_ctx, PT);
   // The workspace is sized for 512-token partitions; a launch with longer ones uses a prefix.
   const size_t need = P > 1 ? pa_decode_workspace_size(num_seqs, num_heads, cache->head_dim, max_ctx) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return pa::fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
-  const int64_t grid = static_cast<int64_t>(P) * cache->num_kv_heads * num_seqs;
+  const int64_t grid = static_cast<int64_t>(P) * groups * num_seqs;
   if (grid > INT32_MAX) return pa::fail(PA_ERR_UNSUPPORTED, "%s: grid too large", fn);
   DecodeArgs& a = su->args;
   a.q = static_cast<const uint16_t*>(q);
@@ -1067,6 +1105,8 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.max_parts = P;
   a.part_blocks = PT / kBlock;
   a.part_shift = __builtin_ctz(static_cast<unsigned>(PT / kBlock));
+  a.head_groups = groups;
+  a.heads_shift = hsh;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.k_scales = cache->k_scales;
   a.v_scales = cache->v_scales;
