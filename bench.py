@@ -43,9 +43,10 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_385_amd", "csrc")
 # the kernel names that make up one call
 TRAFFIC = {
     "decode": (os.path.join(ROOT, "profiles", "decode_attn_traffic_{mode}.json"),
-               os.path.join(CSRC, "pa_kernels.hip"), ("decode_attn_kernel", "decode_merge_kernel")),
+               (os.path.join(CSRC, "pa_kernels.hip"), os.path.join(CSRC, "decode_grouped.hip")),
+               ("decode_attn_kernel", "decode_merge_kernel", "decode_group_kernel")),
     "chunk": (os.path.join(ROOT, "profiles", "chunk_attn_traffic_{mode}.json"),
-              os.path.join(CSRC, "chunk_attention.hip"),
+              (os.path.join(CSRC, "chunk_attention.hip"),),
               ("chunk_attn_kernel", "chunk_wide_kernel", "chunk_merge_kernel")),
 }
 CONTEXT_TEXT = {
@@ -102,10 +103,14 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha256(path: str) -> str:
+def source_sha256(paths) -> str:
+    """sha256 of the leg's kernel sources, concatenated in order."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_leg(args):
@@ -140,8 +145,12 @@ def summarize_counters(args):
         calib = copies[-3:]                       # the three calibration copies come last
         kib = float(np.mean([float(r["Counter_Value"]) for r in calib]))
         scale = out["copy_bytes"] / (kib * 1024.0)
-        per_call = len(attn) // (args.steps + args.warmup)
-        timed = attn[-args.steps * per_call:]
+        calls = args.steps + args.warmup + (0 if args.chunk else args.flush_steps)
+        per_call = len(attn) // calls
+        if per_call < 1 or len(attn) != per_call * calls:
+            raise SystemExit(f"{path}: {len(attn)} launches of {names} for {calls} calls: "
+                             "run with the --steps, --warmup and --flush-steps of the counter runs")
+        timed = attn[args.warmup * per_call:(args.warmup + args.steps) * per_call]
         mean_kib = float(np.sum([float(r["Counter_Value"]) for r in timed])) / args.steps
         out[f"{name}_counter"] = timed[0]["Counter_Name"]
         out[f"{name}_copy_kib"] = kib
@@ -957,7 +966,9 @@ def main():
     med, p10, p90 = (float(x) * 1e3 for x in np.percentile(attn_ms, [50, 10, 90]))
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms, attention pass "
         f"{attn_avg_ms * 1e3:.1f} us avg (median {med:.1f}, p10 {p10:.1f}, p90 {p90:.1f})")
-    kname = f"decode_attn_kernel<{wl.dtype_name.upper()},{D}" + (",FP8>" if fp8 else ">")
+    # the step decodes a batch of forked families as groups (one read of each shared block)
+    kname = (f"decode_group_kernel<{wl.dtype_name.upper()},{D}" if batch.last_grouped
+             else f"decode_attn_kernel<{wl.dtype_name.upper()},{D}") + (",FP8>" if fp8 else ">")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof.update(traffic_fields(recorded_traffic(args) if bsz == 16 else None,

@@ -254,6 +254,63 @@ pa_status pa_decode_partitioned(const pa_cache* cache, const void* q, int32_t nu
                                 void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Grouped decode -- pa_decode for a batch in which groups of sequences share the
+ * leading blocks of their block tables: samples or beams forked from one prompt
+ * point those logical blocks at the same physical blocks ("理解 vLLM
+ * PagedAttention", section 六; "vLLM 核心概念", section "内存共享").  Same result as
+ * pa_decode (the same formula, every sequence over its whole context; a different
+ * float32 summation order, so not the same bits), but each shared block is read
+ * once per group: one work item scores it against the query heads of every member
+ * (at most 16 query heads per KV head in a group, i.e. 16 / G members).
+ *
+ * pa_group_plan (host only) finds the groups and the work items:
+ *   tables           host int32[num_seqs][max_blocks_per_seq], the batch's tables.
+ *   context_lens     host int32[num_seqs], each in [1, max_context_len].
+ *   min_items        items (over all KV heads) to aim for when choosing the
+ *                    partition length (e.g. 4 x the device's compute units).
+ *   plan             host int32 buffer of plan_bytes >= pa_group_plan_bytes(...).
+ *   *plan_ints       receives the plan's length in int32s, or 0 when grouping would
+ *                    save less than a tenth of the block reads (use pa_decode then)
+ *                    or cannot be expressed (query groups wider than 16, lists
+ *                    too long for the workspace).
+ * Groups: sequences whose first block is the same physical block, in sequence order,
+ * cut into chunks of 16 / G; each group shares its members' longest common table
+ * prefix.  A group's block list is its shared blocks, then every member's own
+ * blocks; it is cut into partitions of 32..256 blocks (the longest that still gives
+ * min_items items and fits the workspace's states).  Plan layout (int32): header
+ * [groups, item pairs, partition blocks, max partitions, num_seqs, 0, 0, 0]; per
+ * group [first member, members, shared blocks, list blocks, partitions, longest
+ * context, 0, 0]; per member [sequence, offset of its own blocks in the list after
+ * the shared ones, blocks, context length]; per item pair (group << 12 | partition),
+ * largest first.  Errors: PA_ERR_INVALID_ARG (nothing written).
+ *
+ * pa_decode_grouped runs the plan: one workgroup per (item pair, KV head).
+ *   plan / plan_host  the plan in device memory (a copy of plan_host) and on the host.
+ *   block_tables      device copy of the tables the plan was made from; the context
+ *                     lengths are the plan's.
+ *   workspace         >= pa_decode_workspace_size(num_seqs, num_heads, head_dim,
+ *                     max_context_len) bytes, counters zero (may be NULL when every
+ *                     group has one partition); the partitions of a (group, KV
+ *                     head) are merged by the last of them to finish.
+ * plan_host is checked whole before the launch (every member a sequence of this
+ * batch with a context in [1, max_context_len] and the matching block count, every
+ * group's list length, partitions and items consistent): a plan that fails is
+ * PA_ERR_INVALID_ARG.  The device copy must equal it.  A block id outside
+ * [0, num_blocks) poisons its group's rows with NaN.  No cache write is fused
+ * (call pa_cache_write first).  Other arguments and errors as pa_decode.
+ * ------------------------------------------------------------------------- */
+size_t pa_group_plan_bytes(int32_t num_seqs, int32_t max_context_len);
+pa_status pa_group_plan(const int32_t* tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t max_context_len, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t min_items, int32_t* plan, size_t plan_bytes,
+                        int32_t* plan_ints);
+pa_status pa_decode_grouped(const pa_cache* cache, const void* q, int32_t num_seqs,
+                            int32_t num_heads, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            const int32_t* plan, const int32_t* plan_host, float scale, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pa_decode_fused -- the step's cache write and its decode in one attention pass.
  * Same result as pa_cache_write(cache, k_new, v_new, slot_mapping, num_seqs)
  * followed by pa_decode(...), when token i (k_new[i], v_new[i], [Hkv][D]) is
@@ -588,10 +645,15 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  *      returns);
  *   3. enqueues pa_copy_blocks (if any pair), then pa_decode_fused: the store
  *      of k_new/v_new ([num_seqs][num_kv_heads][head_dim], token i belongs to
- *      seq_ids[i]) and the decode, all on `stream`.
+ *      seq_ids[i]) and the decode, all on `stream`.  When the block manager
+ *      holds shared blocks and pa_group_plan finds groups worth decoding
+ *      together (its plan is made on the host from the packed tables and staged
+ *      with them), the step enqueues pa_cache_write of the new tokens and then
+ *      pa_decode_grouped instead of pa_decode_fused.
  * Staging layout (each part 256-byte aligned, both buffers 256-byte aligned and
  * at least pa_decode_step_staging_bytes() long): int64 slots[n] | int32 ctx[n] |
- * int32 tables[n][max_blocks_per_seq] | int32 pairs[2 n][2] (tile pairs).  staging_host must
+ * int32 tables[n][max_blocks_per_seq] | int32 pairs[2 n][2] (tile pairs) | int32
+ * plan[pa_group_plan_bytes(n, 16 * max_blocks_per_seq) / 4].  staging_host must
  * not be rewritten while an earlier copy from it may still be pending, nor
  * staging_dev while kernels of an earlier step may still read it (the caller
  * alternates two buffers of each and waits on events; with copy_stream, it
@@ -601,7 +663,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  * that take the start and end of the attention kernel itself (attached to its
  * dispatch; with more than 16 query heads per KV head, recorded before and
  * after the attention launches), NULL to skip.  info (optional) receives
- * the number of copy-on-write pairs and the longest context of the step.
+ * the number of copy-on-write pairs, the longest context of the step and
+ * whether it decoded as groups.
  * The decode reads through the caches (PA_CACHE_SHARED_BLOCKS) whenever the
  * block manager holds a block with more than one reference.
  * Every argument is checked before the block manager changes; after that only
@@ -610,6 +673,7 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
 typedef struct pa_step_info {
   int32_t num_cow;
   int32_t max_context_len;
+  int32_t grouped;          /* 1: pa_decode_grouped ran, 0: pa_decode_fused */
 } pa_step_info;
 
 size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);

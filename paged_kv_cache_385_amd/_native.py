@@ -53,7 +53,7 @@ class PaBmPrefixStats(C.Structure):
 
 
 class PaStepInfo(C.Structure):
-    _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32)]
+    _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32), ("grouped", C.c_int32)]
 
 
 class PaError(RuntimeError):
@@ -87,6 +87,10 @@ SIGNATURES = {
                                       C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_decode_merge": (C.c_int, [C.POINTER(PaCache), _I32, _I32, _P, _I32, _P, _P, C.c_size_t,
                                   _P]),
+    "pa_group_plan_bytes": (C.c_size_t, [_I32, _I32]),
+    "pa_group_plan": (C.c_int, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _P, C.c_size_t, _PI32]),
+    "pa_decode_grouped": (C.c_int, [C.POINTER(PaCache), _P, _I32, _I32, _P, _I32, _I32, _P, _P,
+                                    C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_decode_fused": (C.c_int, [C.POINTER(PaCache), _P, _P, _P, _P, _I32, _I32, _P, _I32, _P,
                                   _I32, C.c_float, _P, _P, C.c_size_t, _P]),
     "pa_status_string": (C.c_char_p, [C.c_int]),

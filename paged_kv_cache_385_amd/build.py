@@ -66,12 +66,18 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     n_o = os.path.join(BUILD, "decode_noalloc.o")
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "decode_noalloc.hip"), "-o",
           n_o], verbose)
+    gp_o = os.path.join(BUILD, "group_plan.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", *inc, "-c",
+          os.path.join(CSRC, "group_plan.cpp"), "-o", gp_o], verbose)
+    g_o = os.path.join(BUILD, "decode_grouped.o")
+    _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "decode_grouped.hip"), "-o",
+          g_o], verbose)
     p_o = os.path.join(BUILD, "hbm_probe.o")
     _run([hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, "hbm_probe.hip"), "-o", p_o],
          verbose)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, n_o, p_o,
-          "-o", tmp], verbose)
+          gp_o, g_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -3,9 +3,10 @@ UndefinedBehaviorSanitizer, for the host test suites (no device code, no GPU).
 
     python -m paged_kv_cache_385_amd.build_host_san
 
-Builds ``_build/san/libpa_host_san.so`` from ``csrc/block_manager.cpp`` with g++.
-The library exports the block manager's C ABI (``pa_bm_*``, ``pa_status_string``,
-``pa_last_error``) and nothing that launches a kernel.  Python loads it in place
+Builds ``_build/san/libpa_host_san.so`` from ``csrc/block_manager.cpp`` and
+``csrc/group_plan.cpp`` with g++.  The library exports the block manager's C ABI
+(``pa_bm_*``, ``pa_status_string``, ``pa_last_error``) and the grouped-decode
+planner (``pa_group_plan*``), and nothing that launches a kernel.  Python loads it in place
 of ``libpa.so`` when ``PA_LIB_PATH`` names it and ``PA_LIB_HOST_ONLY=1``; the
 sanitizer runtime must come first in the process (``LD_PRELOAD`` of ``libasan.so``,
 see ``sanitizer_env``).
@@ -28,7 +29,8 @@ FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     cmd = ["g++", *FLAGS, "-I", os.path.join(ROOT, "include"),
-           os.path.join(PKG, "csrc", "block_manager.cpp"), "-o", LIB + ".tmp"]
+           os.path.join(PKG, "csrc", "block_manager.cpp"), os.path.join(PKG, "csrc", "group_plan.cpp"),
+           "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

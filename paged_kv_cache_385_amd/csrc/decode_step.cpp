@@ -13,11 +13,15 @@
 //   3. pa_copy_blocks for the pairs (two 16-token tiles per copied block of a
 //      32-token manager), then pa_decode_fused (the new tokens'
 //      store and the decode in one attention pass, then the merge) -- all on
-//      the caller's stream.
+//      the caller's stream.  When the manager holds shared blocks and grouping
+//      the batch by shared prefix saves enough block reads (pa_group_plan, run on
+//      the packed tables, its plan staged and uploaded with them), the new
+//      tokens are stored by pa_cache_write and pa_decode_grouped attends.
 
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 #include "pa_internal.h"
 
@@ -28,7 +32,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct StagingLayout {
-  size_t slots, ctx, tables, pairs, total;
+  size_t slots, ctx, tables, pairs, plan, plan_bytes, total;
 };
 
 StagingLayout layout(int32_t n, int32_t max_blocks) {
@@ -38,8 +42,20 @@ StagingLayout layout(int32_t n, int32_t max_blocks) {
   l.tables = l.ctx + align_up(sizeof(int32_t) * static_cast<size_t>(n));
   l.pairs = l.tables + align_up(sizeof(int32_t) * static_cast<size_t>(n) * max_blocks);
   // up to two tile copies per sequence (a 32-token block is two 16-token tiles)
-  l.total = l.pairs + align_up(sizeof(int32_t) * 4 * static_cast<size_t>(n));
+  l.plan = l.pairs + align_up(sizeof(int32_t) * 4 * static_cast<size_t>(n));
+  // a grouped-decode plan for the longest context the tables can hold
+  l.plan_bytes = align_up(pa_group_plan_bytes(n, max_blocks * PA_BLOCK_SIZE));
+  l.total = l.plan + l.plan_bytes;
   return l;
+}
+
+// PA_GROUPED_DECODE=0 in the environment: steps never take the grouped decode (read once).
+bool grouped_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_GROUPED_DECODE");
+    return !(e && e[0] == '0');
+  }();
+  return on;
 }
 
 }  // namespace
@@ -96,9 +112,20 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   // the staging area holds two tile pairs per sequence
   st = pa_bm_tile_pairs(bm, pairs_h, n_cow, pairs_h, 2 * num_seqs, &n_cow);
   if (st != PA_OK) return st;
+  // Blocks shared by several sequences of the manager: the batch may decode as groups
+  // that read each shared block once (pa_decode_grouped), when the plan says it saves
+  // enough.  A plan that cannot be made leaves the ordinary decode.
+  auto* plan_h = reinterpret_cast<int32_t*>(hb + l.plan);
+  int32_t plan_ints = 0;
+  if (grouped_enabled() && pa::bm_shared_blocks(bm) > 0 &&
+      pa_group_plan(tables_h, num_seqs, max_blocks_per_seq, ctx_h, max_ctx, num_heads,
+                    cache->num_kv_heads, 4 * pa::device_cus(), plan_h, l.plan_bytes,
+                    &plan_ints) != PA_OK)
+    plan_ints = 0;
   if (info) {
     info->num_cow = n_cow;
     info->max_context_len = max_ctx;
+    info->grouped = plan_ints > 0 ? 1 : 0;
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -109,7 +136,9 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
       return pa::fail(PA_ERR_HIP, "pa_decode_step: staging_host is not pinned, mapped host memory");
     db = static_cast<char*>(dp);
   } else {
-    const size_t upload = n_cow ? l.pairs + sizeof(int32_t) * 2 * n_cow : l.pairs;
+    const size_t upload = plan_ints ? l.plan + sizeof(int32_t) * plan_ints
+                          : n_cow    ? l.pairs + sizeof(int32_t) * 2 * n_cow
+                                     : l.pairs;
     hipStream_t cs = copy_stream ? static_cast<hipStream_t>(copy_stream) : s;
     if (hipMemcpyAsync(db, hb, upload, hipMemcpyHostToDevice, cs) != hipSuccess)
       return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
@@ -126,6 +155,16 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   // blocks shared by several sequences are read through the caches
   pa_cache c = *cache;
   if (pa::bm_shared_blocks(bm) > 0) c.flags |= PA_CACHE_SHARED_BLOCKS;
+  if (plan_ints) {
+    // grouped: the new tokens are stored by their own launch, then the groups attend
+    st = pa_cache_write(cache, k_new, v_new, reinterpret_cast<const int64_t*>(db + l.slots), num_seqs,
+                        stream);
+    if (st != PA_OK) return st;
+    return pa::decode_grouped_run("pa_decode_step", &c, q, num_seqs, num_heads,
+                                  reinterpret_cast<const int32_t*>(db + l.tables), max_blocks_per_seq,
+                                  max_ctx, reinterpret_cast<const int32_t*>(db + l.plan), plan_h, scale,
+                                  out, workspace, workspace_bytes, attn_begin, attn_end, stream);
+  }
   return pa::decode_run("pa_decode_step", &c, q, num_seqs, num_heads,
                         reinterpret_cast<const int32_t*>(db + l.tables), max_blocks_per_seq,
                         reinterpret_cast<const int32_t*>(db + l.ctx), max_ctx, scale, out, workspace,

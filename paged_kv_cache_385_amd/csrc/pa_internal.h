@@ -46,6 +46,15 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
                      const int64_t* slot_mapping, bool merge, bool fuse_merge,
                      int32_t part_tokens, void* ev_begin, void* ev_end, void* stream);
 
+// pa_decode_grouped with the optional events (hipEvent_t) attached to the kernel's
+// dispatch: its own start and end.
+pa_status decode_grouped_run(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
+                             int32_t num_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, int32_t max_context_len,
+                             const int32_t* plan, const int32_t* plan_host, float scale, void* out,
+                             void* workspace, size_t workspace_bytes, void* ev_begin, void* ev_end,
+                             void* stream);
+
 // Decode with more than 16 query heads per KV head: pa_chunk_attention's kernels
 // with one query per sequence (q and out [num_seqs][num_heads][head_dim]), the
 // key-partition states in `workspace` (pa_chunk_workspace_size bytes for

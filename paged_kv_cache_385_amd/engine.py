@@ -257,6 +257,7 @@ class DecodeBatch:
         self._q_shape = (B, num_heads, cache.head_dim)
         self._i = 0
         self.last_max_ctx = 0
+        self.last_grouped = False
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
 
     def _staged_dev(self) -> torch.Tensor:
@@ -342,4 +343,5 @@ class DecodeBatch:
         else:
             self.last_pairs = np.zeros((0, 2), dtype=np.int32)
         self.last_max_ctx = self._info.max_context_len
+        self.last_grouped = bool(self._info.grouped)
         return self.out

@@ -237,6 +237,47 @@ def decode_partitioned(k_cache, v_cache, q, block_tables, context_lens, max_cont
     return out
 
 
+def group_plan(tables: np.ndarray, context_lens: np.ndarray, max_context_len: int, num_heads: int,
+               num_kv_heads: int, min_items: int = 1024) -> np.ndarray:
+    """pa_group_plan on host arrays: the grouped-decode plan (int32), empty when grouping
+    the batch by shared prefix would not pay."""
+    tab = np.ascontiguousarray(tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, mb = tab.shape
+    nbytes = int(N.lib().pa_group_plan_bytes(B, max_context_len))
+    plan = np.zeros(max(nbytes // 4, 1), dtype=np.int32)
+    n = C.c_int32()
+    N.check(N.lib().pa_group_plan(tab.ctypes.data, B, mb, ctx.ctypes.data, max_context_len,
+                                  num_heads, num_kv_heads, min_items, plan.ctypes.data, nbytes,
+                                  C.byref(n)), "pa_group_plan")
+    return plan[:n.value].copy()
+
+
+def decode_grouped(k_cache, v_cache, q, block_tables, max_context_len: int, scale: float,
+                   plan: np.ndarray, out=None, workspace=None, stream=None, scales=None,
+                   shared_blocks: bool = True) -> torch.Tensor:
+    """pa_decode_grouped with a plan from ``group_plan`` (uploaded here); returns out."""
+    dt = _compute_dtype(k_cache, q)
+    desc = cache_desc(k_cache, v_cache, shared_blocks, scales=scales, dtype=dt)
+    B, H, D = q.shape
+    _need(q, dt, k_cache.device, "q")
+    _need(block_tables, torch.int32, k_cache.device, "block_tables")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, dt, k_cache.device, "out", (B, H, D))
+    plan_h = np.ascontiguousarray(plan, dtype=np.int32)
+    plan_d = torch.from_numpy(plan_h).to(k_cache.device)
+    ws, wsb = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                   workspace.numel() * workspace.element_size())
+    N.check(N.lib().pa_decode_grouped(C.byref(desc), q.data_ptr(), B, H, block_tables.data_ptr(),
+                                      block_tables.shape[1], max_context_len, plan_d.data_ptr(),
+                                      plan_h.ctypes.data, scale, out.data_ptr(), ws, wsb,
+                                      _stream_ptr(stream, q.device)), "pa_decode_grouped")
+    return out
+
+
 def decode_fused(k_cache, v_cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
                  max_context_len: int, scale: float, out=None, workspace=None,
                  stream=None, scales=None) -> torch.Tensor:

@@ -1,7 +1,8 @@
 """bench.py's HBM-counter summary on synthetic rocprofv3 counter files (no GPU).
 
 The summary scales each counter by what it read for a calibration copy of known size,
-takes the last --steps calls (a call may be an attention and a merge launch), and stamps
+takes the timed calls (after the warm-up calls, before the flushed ones; a call may be an
+attention and a merge launch), and stamps
 the result with the kernel source; the bench line uses it only while the stamp and the workload
 match, and reports it with the counter run's own algorithmic bytes.
 """
@@ -30,9 +31,9 @@ def _counter_csv(path, name, calib_value, launches, values):
         w.writerows(rows)
 
 
-def _args(tmp_path, chunk, fetch, write, steps=4, warmup=2):
+def _args(tmp_path, chunk, fetch, write, steps=4, warmup=2, flush_steps=0):
     return types.SimpleNamespace(chunk=chunk, workload=3, steps=steps, warmup=warmup,
-                                 kv_dtype="native", copy_calibration=1,
+                                 flush_steps=flush_steps, kv_dtype="native", copy_calibration=1,
                                  summarize_counters=[str(fetch), str(write)])
 
 
@@ -90,3 +91,20 @@ def test_chunk_summary_sums_the_launches_of_a_call(tmp_path, monkeypatch):
     assert bench.recorded_traffic(_leg("verify"))["traffic_bytes_per_launch"] \
         == t["traffic_bytes_per_launch"]
     assert bench.recorded_traffic(_leg("prefill")) is None
+
+
+def test_decode_summary_drops_the_flushed_steps(tmp_path, monkeypatch):
+    import pytest
+    out = tmp_path / "decode_{mode}.json"
+    path, src, names = bench.TRAFFIC["decode"]
+    monkeypatch.setitem(bench.TRAFFIC, "decode", (str(out), src, names))
+    k = "void decode_group_kernel<F16, 128, true, false>(GroupArgs)"
+    # 2 warm-up, 4 timed and 3 flushed steps: only the timed ones count
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", 1024, [k] * 9, [1, 1, 10, 10, 10, 10, 99, 99, 99])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", 1024, [k] * 9, [2] * 9)
+    bench.summarize_counters(_args(tmp_path, None, tmp_path / "f.csv", tmp_path / "w.csv",
+                                   flush_steps=3))
+    t = json.loads((tmp_path / "decode_w3.json").read_text())
+    assert t["launches"] == 4 and t["fetch_bytes_per_launch"] == 10 * 1024
+    with pytest.raises(SystemExit):            # the counter runs had other --flush-steps
+        bench.summarize_counters(_args(tmp_path, None, tmp_path / "f.csv", tmp_path / "w.csv"))

@@ -172,14 +172,16 @@ def _independent(cfg_id: int, name: str, dtype: str, ctx: np.ndarray, H: int, Hk
 
 def _shared_prefix(seed: int, rng: np.random.Generator, prompts: int = 16, samples: int = 8,
                    prefix: int = 1024, suffix_max: int = 512, extra_max: int = 15, H: int = 32,
-                   D: int = 128, dtype: str = "f16", grow: int = 0) -> Workload:
+                   D: int = 128, dtype: str = "f16", grow: int = 0,
+                   Hkv: int | None = None) -> Workload:
     """Parallel sampling over a shared prompt prefix.
 
     Prompt p's prefix holds ``prefix + r_p`` tokens, r_p ~ U{1..extra_max}, so
     its last block is partially filled and shared by all ``samples`` children.
     Each sample then appends a private suffix of U{0..suffix_max} tokens and
     finally the step's new token.  ``extra_max = 0`` gives the literal
-    block-aligned prefix (r_p = 0).
+    block-aligned prefix (r_p = 0).  ``Hkv`` KV heads (default ``H``: one query
+    head per KV head).
     """
     B = prompts * samples
     extras = (rng.integers(1, extra_max, size=prompts, endpoint=True) if extra_max > 0
@@ -214,7 +216,8 @@ def _shared_prefix(seed: int, rng: np.random.Generator, prompts: int = 16, sampl
             setup.append(("append", b, seg, 0, int(suffix[b])))
         step.append(("append", b, seg, int(suffix[b]), 1))
     wl = Workload(cfg_id=4, name="shared-prefix parallel sampling", dtype_name=dtype, num_seqs=B,
-                  num_heads=H, num_kv_heads=H, head_dim=D, scale=1.0 / math.sqrt(D), seed=seed,
+                  num_heads=H, num_kv_heads=H if Hkv is None else Hkv, head_dim=D,
+                  scale=1.0 / math.sqrt(D), seed=seed,
                   num_blocks=num_blocks, free_order=free_order, ctx_lens=ctx, setup=setup,
                   step=step, seg_lengths=seg_lengths, seq_slices=seq_slices)
     wl.notes.update(prompts=prompts, samples=samples, prefix_len=prefix_len.tolist(),
