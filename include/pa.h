@@ -267,7 +267,8 @@ pa_status pa_decode_partitioned(const pa_cache* cache, const void* q, int32_t nu
  *   tables           host int32[num_seqs][max_blocks_per_seq], the batch's tables.
  *   context_lens     host int32[num_seqs], each in [1, max_context_len].
  *   min_items        items (over all KV heads) to aim for when choosing the
- *                    partition length (e.g. 4 x the device's compute units).
+ *                    partition length (the decode step asks for 2 per compute
+ *                    unit: longer items pay their start-up fewer times).
  *   plan             host int32 buffer of plan_bytes >= pa_group_plan_bytes(...).
  *   *plan_ints       receives the plan's length in int32s, or 0 when grouping would
  *                    save less than a tenth of the block reads (use pa_decode then)

@@ -360,15 +360,10 @@ void launch_t(const GroupArgs& g, int64_t grid, int d, hipStream_t s, hipEvent_t
 }
 
 template <class E>
-void launch(const GroupArgs& g, int64_t grid, int d, bool fp8, bool stream_loads, hipStream_t s,
-            hipEvent_t e0, hipEvent_t e1) {
-  if (fp8) {
-    if (stream_loads) launch_t<E, true, true>(g, grid, d, s, e0, e1);
-    else launch_t<E, false, true>(g, grid, d, s, e0, e1);
-  } else {
-    if (stream_loads) launch_t<E, true, false>(g, grid, d, s, e0, e1);
-    else launch_t<E, false, false>(g, grid, d, s, e0, e1);
-  }
+void launch(const GroupArgs& g, int64_t grid, int d, bool fp8, hipStream_t s, hipEvent_t e0,
+            hipEvent_t e1) {
+  if (fp8) launch_t<E, true, true>(g, grid, d, s, e0, e1);
+  else launch_t<E, true, false>(g, grid, d, s, e0, e1);
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -463,16 +458,16 @@ pa_status decode_grouped_run(const char* fn, const pa_cache* cache, const void* 
   g.items_off = g.members_off + kMemberInts * num_seqs;
   g.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const bool fp8 = (cache->flags & PA_CACHE_FP8) != 0;
-  // shared blocks are read by one item only, but other blocks may still be aliased
-  // (sharers outside the group): loads through the caches unless told otherwise
-  const bool stream_loads = (cache->flags & PA_CACHE_SHARED_BLOCKS) == 0;
+  // Within a group every block is read by one item only; a prefix that several groups
+  // share (a family wider than one tile) is read by items that seldom run on one XCD
+  // at once.  The loads stream (non-temporal): measured faster for every plan tried.
   const int64_t grid = static_cast<int64_t>(pairs) * cache->num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_begin), e1 = static_cast<hipEvent_t>(ev_end);
   if (cache->dtype == PA_F16)
-    launch<F16>(g, grid, cache->head_dim, fp8, stream_loads, s, e0, e1);
+    launch<F16>(g, grid, cache->head_dim, fp8, s, e0, e1);
   else
-    launch<BF16>(g, grid, cache->head_dim, fp8, stream_loads, s, e0, e1);
+    launch<BF16>(g, grid, cache->head_dim, fp8, s, e0, e1);
   return launch_status(fn);
 }
 

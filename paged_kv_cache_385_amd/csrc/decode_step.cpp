@@ -119,7 +119,7 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
   int32_t plan_ints = 0;
   if (grouped_enabled() && pa::bm_shared_blocks(bm) > 0 &&
       pa_group_plan(tables_h, num_seqs, max_blocks_per_seq, ctx_h, max_ctx, num_heads,
-                    cache->num_kv_heads, 4 * pa::device_cus(), plan_h, l.plan_bytes,
+                    cache->num_kv_heads, 2 * pa::device_cus(), plan_h, l.plan_bytes,
                     &plan_ints) != PA_OK)
     plan_ints = 0;
   if (info) {
