@@ -287,6 +287,18 @@ void chunk_attn_kernel(ChunkArgs a) {
   int32_t ids0 = 0;
   if (lane < min(64, nw)) ids0 = bt[first + kWaves * lane];
 
+  // FP8 pools: the K scale folds into the score scale, the V scale into the output.
+  // The running max is taken on raw scores and then scaled, which needs a scale
+  // > 0: the sign of a negative one is moved into q (its sign bits flipped).
+  const float scale_signed = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
+  const uint32_t q_flip = scale_signed < 0.f ? 0x80008000u : 0u;
+  // A zero scale would turn a masked score (-inf) into NaN: 1e-30 leaves every
+  // exponent rounding to the same value and a masked one at -inf.
+  const float score_scale = fmaxf(fabsf(scale_signed), 1e-30f);
+  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
+  // keys up to the workgroup's first column's position are seen by every column
+  const int32_t pmin = ctx - sq.n + col0 / G;
+
   // This lane's column in tile t: token ti of the chunk, head gh of the group,
   // position pos[t].  Padding columns load zero q and mask nothing.
   int32_t pos[NT];
@@ -305,9 +317,9 @@ void chunk_attn_kernel(ChunkArgs a) {
         // wave w stores the fragments (t, kk) with (t * KK + kk) % 4 == w
         if ((t * KK + kk) % kWaves == w)
           s_q[(t * KK + kk) * 64 + lane] =
-              col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+              col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) ^ q_flip : u32x4{0, 0, 0, 0};
       } else {
-        qf[t][kk] = col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+        qf[t][kk] = col_ok ? load16(a.q + q_row + 32 * kk + 8 * g4) ^ q_flip : u32x4{0, 0, 0, 0};
       }
     }
   }
@@ -315,17 +327,18 @@ void chunk_attn_kernel(ChunkArgs a) {
 
   const int64_t head_off_b = static_cast<int64_t>(kvh) * kTileBytes;
   const int64_t blk_stride_b = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
-  // FP8 pools: the K scale folds into the score scale, the V scale into the output
-  const float score_scale = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
-  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
 
+  // Running max, unnormalised output and column sums of P per tile; the sums come
+  // from the matrix cores (P^T times a tile of ones: every row of lsum holds the
+  // column's sum), which keeps a conversion and an add per score off the vector ALU.
   bool bad_blk = false;
-  float m_run[NT], l_run[NT];
-  f32x4 acc[NT][MT];
+  float m_run[NT];
+  f32x4 acc[NT][MT], lsum[NT];
+  const u16x4 ones = __builtin_bit_cast(u16x4, uint2{E::kOne2, E::kOne2});
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -402,35 +415,41 @@ void chunk_attn_kernel(ChunkArgs a) {
         V[j2] = __builtin_bit_cast(u32x4, vv);
       }
     }
+    // the causal mask matters only for a block reaching past the first column's
+    // position (and for the padding steps past the wave's last block)
+    const bool diag = i >= cnt || t0 + kBlock - 1 > pmin;
+    const float c = score_scale;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int32_t seen = i < cnt ? pos[t] - t0 : -1;        // this column sees tokens 0 .. seen
+      // raw scores; the running max m_run is kept in scaled log2 units
       float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = s[t][r] * score_scale;
-        if (4 * g4 + r > seen) sv[r] = -INFINITY;
+      for (int r = 0; r < 4; ++r) sv[r] = s[t][r];
+      if (diag) {
+        const int32_t seen = i < cnt ? pos[t] - t0 : -1;      // this column sees tokens 0 .. seen
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g4 + r > seen) sv[r] = -INFINITY;
       }
-      float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bmax = col_max4(bmax);
+      const float bmax = col_max4_raw(max3_raw(max3_raw(sv[0], sv[1], sv[2]), sv[3], sv[3]));
       // The reference max moves only when a score passes it by more than kLazyMax
-      // (log2 units), so P <= 2^kLazyMax and most blocks skip the rescale.
-      const float m_new = bmax > m_run[t] + kLazyMax ? bmax : m_run[t];
+      // (log2 units; c >= 0, so the max commutes with the scale), so P <= 2^kLazyMax
+      // and most blocks skip the rescale.
+      const float m_new = bmax * c > m_run[t] + kLazyMax ? bmax * c : m_run[t];
       // a column may have seen nothing yet: exponentiate against a finite stand-in
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[t] - m_use);
       m_run[t] = m_new;
-      u16x4 pb;
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = E::from_float(fast_exp2(sv[r] - m_use));
-        psum += E::to_float(pb[r]);
-      }
-      l_run[t] = l_run[t] * alpha + psum;
+      // P in 16 bits, two scores per word
+      const u16x4 pb = __builtin_bit_cast(
+          u16x4, uint2{E::pack2(fast_exp2(__builtin_fmaf(sv[0], c, -m_use)),
+                                fast_exp2(__builtin_fmaf(sv[1], c, -m_use))),
+                       E::pack2(fast_exp2(__builtin_fmaf(sv[2], c, -m_use)),
+                                fast_exp2(__builtin_fmaf(sv[3], c, -m_use)))});
       if (__ballot(alpha != 1.f) != 0) {              // the reference moved somewhere
 #pragma unroll
         for (int j = 0; j < MT; ++j) acc[t][j] *= alpha;
+        lsum[t] *= alpha;
       }
 #pragma unroll
       for (int j2 = 0; j2 < KK; ++j2) {
@@ -440,6 +459,7 @@ void chunk_attn_kernel(ChunkArgs a) {
         acc[t][2 * j2] = E::mfma_pv(lo, pb, acc[t][2 * j2]);
         acc[t][2 * j2 + 1] = E::mfma_pv(hi, pb, acc[t][2 * j2 + 1]);
       }
+      lsum[t] = E::mfma_pv(ones, pb, lsum[t]);
     }
   };
 
@@ -468,11 +488,9 @@ void chunk_attn_kernel(ChunkArgs a) {
   // ---- combine the four waves in LDS, one 16-column tile at a time ----
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    l_run[t] += __shfl_xor(l_run[t], 16);
-    l_run[t] += __shfl_xor(l_run[t], 32);
     if (g4 == 0) {
       s_m[t][w][n] = m_run[t];
-      s_l[t][w][n] = l_run[t];
+      s_l[t][w][n] = lsum[t][0];
     }
   }
   if (tid == 0) s_bad = 0;
@@ -537,12 +555,14 @@ void chunk_attn_kernel(ChunkArgs a) {
   }
 }
 
-constexpr int kWideCols = 128;                // columns per workgroup of the wide kernel
-constexpr int kWaveCols = kWideCols / kWaves; // 32 per wave: two groups of 16
+constexpr int kWideGroups = 2;                  // groups of 16 columns per wave
+constexpr int kWaveCols = 16 * kWideGroups;
+constexpr int kWideCols = kWaves * kWaveCols;   // columns per workgroup of the wide kernel
 
 template <class E, int D, bool kFp8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWideGroups > 2 ? 1 : 2)))
 void chunk_wide_kernel(ChunkArgs a) {
+  constexpr int NG = kWideGroups;
   constexpr int KK = D / 32;                 // 32-dim steps of q.K^T
   constexpr int MT = D / 16;                 // 16-dim tiles of the output
   constexpr int kTileElems = kBlock * D;     // one block's K (or V) tile
@@ -593,13 +613,22 @@ void chunk_wide_kernel(ChunkArgs a) {
 
   // position of the tile's first column: keys up to it are seen by every column
   const int32_t pmin = ctx - sq.n + (tile * kWideCols) / G;
-  // the lane's two columns (one per group of 16)
-  int32_t pos[2];
-  bool col_ok[2];
-  int64_t hrow[2];
-  u32x4 qf[2][KK];
+  // FP8 pools: the K scale folds into the score scale, the V scale into the output.
+  // The running max is taken on raw scores and then scaled, which needs a scale
+  // > 0: the sign of a negative one is moved into q (its sign bits flipped).
+  const float scale_signed = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
+  const uint32_t q_flip = scale_signed < 0.f ? 0x80008000u : 0u;
+  // A zero scale would turn a masked score (-inf) into NaN: 1e-30 leaves every
+  // exponent rounding to the same value and a masked one at -inf.
+  const float score_scale = fmaxf(fabsf(scale_signed), 1e-30f);
+  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
+  // the lane's columns (one per group of 16)
+  int32_t pos[NG];
+  bool col_ok[NG];
+  int64_t hrow[NG];
+  u32x4 qf[NG][KK];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     const int32_t col = tile * kWideCols + w * kWaveCols + gi * 16 + n;
     col_ok[gi] = col < sq.cols;
     const int32_t ti = col_ok[gi] ? col / G : 0;
@@ -608,7 +637,7 @@ void chunk_wide_kernel(ChunkArgs a) {
     hrow[gi] = static_cast<int64_t>(sq.qs + ti) * H + kvh * G + gh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[gi][kk] = col_ok[gi] ? load16(a.q + hrow[gi] * D + 32 * kk + 8 * g4) : u32x4{0, 0, 0, 0};
+      qf[gi][kk] = col_ok[gi] ? load16(a.q + hrow[gi] * D + 32 * kk + 8 * g4) ^ q_flip : u32x4{0, 0, 0, 0};
   }
 
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -617,9 +646,6 @@ void chunk_wide_kernel(ChunkArgs a) {
   const int32_t nstage = (jend - jbeg + 1) / 2;
   const int64_t head_off_b = static_cast<int64_t>(kvh) * kTileBytes;
   const int64_t blk_stride_b = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
-  // FP8 pools: the K scale folds into the score scale, the V scale into the output
-  const float score_scale = kFp8 ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
-  const float out_scale = kFp8 ? a.v_scales[kvh] : 1.f;
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
 
@@ -735,19 +761,26 @@ void chunk_wide_kernel(ChunkArgs a) {
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][MT];
+  // Running max per column, the unnormalised output, and the column sums of P: those
+  // come from the matrix cores too, as P^T times a tile of ones (every row of lsum
+  // holds the column's sum), which moves a conversion and an add per score off the
+  // vector ALU, the unit this kernel waits on.
+  float m_run[NG];
+  f32x4 acc[NG][MT], lsum[NG];
+  const u32x4 ones = {E::kOne2, E::kOne2, E::kOne2, E::kOne2};
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
+  for (int gi = 0; gi < NG; ++gi) {
+    m_run[gi] = -INFINITY;
+    lsum[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[gi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](int32_t st, int buf) {
-    f32x4 sc[2][2];   // [group][block]
+    f32x4 sc[NG][2];   // [group][block]
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) sc[gi][0] = sc[gi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // all K operands first, then four independent accumulation chains per 32-dim step
+    for (int gi = 0; gi < NG; ++gi) sc[gi][0] = sc[gi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // all K operands first, then independent accumulation chains per 32-dim step
     u32x4 kf[2][KK];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -758,10 +791,9 @@ void chunk_wide_kernel(ChunkArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        sc[0][blk] = E::mfma_qk(kf[blk][kk], qf[0][kk], sc[0][blk]);
-        sc[1][blk] = E::mfma_qk(kf[blk][kk], qf[1][kk], sc[1][blk]);
-      }
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) sc[gi][blk] = E::mfma_qk(kf[blk][kk], qf[gi][kk], sc[gi][blk]);
     // V operands, read while the softmax runs
     u32x4 vf[MT];
 #pragma unroll
@@ -771,9 +803,9 @@ void chunk_wide_kernel(ChunkArgs a) {
     // a stage wholly at or before the tile's first position needs no causal mask
     const bool diag = t0 + 2 * kBlock - 1 > pmin;
     const float c = score_scale;
-    u32x4 pf[2];
+    u32x4 pf[NG];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+    for (int gi = 0; gi < NG; ++gi) {
       // raw scores; the running max m_run is kept in scaled log2 units
       float sv[8];
 #pragma unroll
@@ -785,10 +817,10 @@ void chunk_wide_kernel(ChunkArgs a) {
           if (key > pos[gi]) sv[e] = -INFINITY;
         }
       }
-      float bmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      bmax = col_max4(bmax);
-      // The reference max moves only when a score exceeds it by more than 2^8 (c > 0:
+      float bmax = max3_raw(max3_raw(sv[0], sv[1], sv[2]), max3_raw(sv[3], sv[4], sv[5]),
+                            max3_raw(sv[6], sv[7], sv[7]));
+      bmax = col_max4_raw(bmax);
+      // The reference max moves only when a score exceeds it by more than 2^8 (c >= 0:
       // the max commutes with the scale).  Exponents stay <= 8, so P <= 256, which the
       // 16-bit P and the float32 sums hold at full relative precision, and most stages
       // skip the rescale of the accumulators.  The normalisation and the partition
@@ -798,25 +830,25 @@ void chunk_wide_kernel(ChunkArgs a) {
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[gi] - m_use);
       m_run[gi] = m_new;
-      u16x8 pb;
-      float psum = 0.f;
+      // P in 16 bits, two scores per operand word
+      u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = E::from_float(fast_exp2(__builtin_fmaf(sv[e], c, -m_use)));
-        psum += E::to_float(pb[e]);
-      }
-      l_run[gi] = l_run[gi] * alpha + psum;
+      for (int w2 = 0; w2 < 4; ++w2)
+        pw[w2] = E::pack2(fast_exp2(__builtin_fmaf(sv[2 * w2], c, -m_use)),
+                          fast_exp2(__builtin_fmaf(sv[2 * w2 + 1], c, -m_use)));
       if (__ballot(alpha != 1.f) != 0) {              // the running max moved somewhere
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[gi][t] *= alpha;
+        lsum[gi] *= alpha;
       }
-      pf[gi] = __builtin_bit_cast(u32x4, pb);
+      pf[gi] = pw;
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      acc[0][t] = E::mfma_qk(vf[t], pf[0], acc[0][t]);
-      acc[1][t] = E::mfma_qk(vf[t], pf[1], acc[1][t]);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) acc[gi][t] = E::mfma_qk(vf[t], pf[gi], acc[gi][t]);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) lsum[gi] = E::mfma_qk(ones, pf[gi], lsum[gi]);
   };
 
   // free: the set that receives stage st + 2; held: the set holding stage st + 1
@@ -839,10 +871,10 @@ void chunk_wide_kernel(ChunkArgs a) {
     if (st + 1 < nstage) step(st + 1, kB, vB, kA, vA);
   }
 
-  // ---- outputs: lane l holds dims 16 t + 4 g4 .. + 3 of its two columns ----
+  // ---- outputs: lane l holds dims 16 t + 4 g4 .. + 3 of its columns ----
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float L = col_sum4(l_run[gi]);
+  for (int gi = 0; gi < NG; ++gi) {
+    const float L = lsum[gi][0];
     if (!col_ok[gi]) continue;
     if (direct) {
       const float inv = out_scale / L;
@@ -940,7 +972,7 @@ ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, 
   const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * p.tiles;
   // workgroups per compute unit: the wide kernel and the multi-tile narrow one at
   // head dim 128 run two, the others three or more
-  const int64_t per_cu = (p.wide || p.nt * head_dim > 192) ? 2 : 3;
+  const int64_t per_cu = p.wide ? (kWideGroups > 2 ? 1 : 2) : p.nt * head_dim > 192 ? 2 : 3;
   const int64_t slots = per_cu * static_cast<int64_t>(pa::device_cus());
   p.part_blocks = kMinPartTokens / kBlock;
   if (items >= (p.wide ? 1 : 8) * slots) {

@@ -19,6 +19,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = PA_BLOCK_SIZE;                       // tokens per block
 
@@ -48,6 +51,11 @@ struct F16 {
   __device__ static float to_float(uint16_t x) {
     return static_cast<float>(__builtin_bit_cast(_Float16, x));
   }
+  // two values rounded to nearest even, a in the low half: one operand word
+  __device__ static uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
+  static constexpr uint32_t kOne2 = 0x3C003C00u;     // two 1.0
 };
 
 struct BF16 {
@@ -74,6 +82,10 @@ struct BF16 {
   __device__ static float to_float(uint16_t x) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
   }
+  __device__ static uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  }
+  static constexpr uint32_t kOne2 = 0x3F803F80u;
 };
 
 // Eight E4M3 codes (two words, in memory order) as eight 16-bit elements: one
@@ -124,6 +136,24 @@ __device__ __forceinline__ float col_max4(float x) {
   a = b = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
   swap32(a, b);
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+// max of three floats as one v_max3_f32, without the canonicalising moves the
+// compiler puts before fmaxf on values it cannot prove canonical (matrix-core
+// results).  A NaN operand yields the larger of the others (IEEE mode).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// col_max4 with the same raw maxima
+__device__ __forceinline__ float col_max4_raw(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  const float m = max3_raw(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b),
+                           __builtin_bit_cast(float, b));
+  a = b = __builtin_bit_cast(uint32_t, m);
+  swap32(a, b);
+  return max3_raw(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float col_sum4(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;

@@ -286,3 +286,28 @@ def test_many_sequences_in_largest_first_order(B, H, q_max):
     assert not torch.isnan(out).any()
     ref = _oracle(wl, segs, q, starts, range(len(ctx)))
     check_close(out, ref, wl.dtype, label=f"{B} sequences, H={H}")
+
+
+@pytest.mark.parametrize("scale_mult", [-1.0, 0.0])
+def test_negative_and_zero_scales(scale_mult):
+    """The kernels take each block's maximum on raw scores and then scale it, which
+    holds for a scale >= 0; a negative scale is moved into the sign of q.  A negative
+    and a zero scale through the narrow kernel (few columns, key partitions merged)
+    and the wide kernel (>= 128 columns), against the oracle at the same scale."""
+    from paged_kv_cache_385_amd import chunk_attention
+    ctx = [700, 1500, 40, 300]
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=77)
+    scale = float(wl.scale * scale_mult)
+    say(f"scale {scale}: narrow and wide launches")
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    dev = cache.device
+    for q_lens in ([6, 5, 3, 6], [6, 200, 3, 20]):
+        q = wl.chunk_q(q_lens)
+        starts = _starts(q_lens)
+        out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+        chunk_attention(cache.k_cache, cache.v_cache, q.to(dev), torch.from_numpy(starts).to(dev),
+                        tables, ctx_d, int(max(q_lens)), wl.max_context_len, scale, out=out)
+        torch.cuda.synchronize()
+        ref = OA.chunk_batch(q, starts, lambda b: wl.seq_kv(b, segs), wl.ctx_lens, scale,
+                             range(len(ctx)))
+        check_close(out, ref, wl.dtype, label=f"scale {scale}, chunks {q_lens}")
