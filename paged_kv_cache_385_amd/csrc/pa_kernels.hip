@@ -449,7 +449,9 @@ __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_
   return false;     // not reached
 }
 
-// Three waves per SIMD: 136 registers, no spills, and 3 x 34 KB of LDS per CU.
+// Three waves per SIMD: 162-163 registers at head dim 128 on 16-bit pools, 130-132 on
+// FP8 pools (no spills), and 3 x 34 KB of LDS per CU.  Held to 128 registers (four
+// waves), the FP8 form spills and its steps took 84 against 81 us.
 template <class E, int D, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_attn_kernel(DecodeArgs a) {
@@ -535,14 +537,16 @@ void decode_attn_kernel(DecodeArgs a) {
   // into the cache from the same registers and addresses.  No other workgroup
   // reads that position.  A slot that is not the sequence's last position is not
   // written and poisons the sequence's output; a negative slot stores nothing.
-  // The fragments wait in the wave's (not yet used) LDS combine area.
+  // The fragments wait in the wave's (not yet used) LDS combine area.  FP8 pools:
+  // the fragments are quantised (the codes of the cache write) before they wait,
+  // and the codes are put into the loaded code tiles.
   bool st_on = false, slot_bad = false;
   int32_t st_i = -1, st_off = 0;
   u32x4* st_k = reinterpret_cast<u32x4*>(&s_acc[w][0]) + lane * KK;          // [64][KK]
   uint32_t* st_v = reinterpret_cast<uint32_t*>(&s_acc[w][0]) + 64 * 4 * KK + lane * KK;
   u32x4 kpatch[KK];
   uint32_t vpatch[KK];
-  if (!kFp8 && a.new_slots != nullptr && p == nparts - 1) {
+  if (a.new_slots != nullptr && p == nparts - 1) {
     const int64_t slot = a.new_slots[b];
     const int32_t jl = nblk - 1 - p * PB;       // last block, within the partition
     if (slot >= 0 && (jl & (wph - 1)) == wi) {
@@ -554,25 +558,66 @@ void decode_attn_kernel(DecodeArgs a) {
       slot_bad = !st_on;
       const int64_t src = (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * D;
       if (st_on && n == st_off) {
+        if constexpr (kFp8) {
+          // the lane's K codes: dims 64pp + 8g4 .. +7, then 64pp + 32 + 8g4 .. +7
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kpatch[kk] = load16(a.k_new + src + 32 * kk + 8 * g4);
+          for (int pp = 0; pp < LW; ++pp) {
+            kpatch[2 * pp] = load16(a.k_new + src + 64 * pp + 8 * g4);
+            kpatch[2 * pp + 1] = load16(a.k_new + src + 64 * pp + 32 + 8 * g4);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) kpatch[kk] = load16(a.k_new + src + 32 * kk + 8 * g4);
+        }
       }
       if (st_on && g4 == (st_off >> 2)) {
+        if constexpr (kFp8) {
+          // the lane's V codes: dims (64qq + 2n, +1), then (64qq + 32 + 2n, +1)
 #pragma unroll
-        for (int j2 = 0; j2 < KK; ++j2)
-          vpatch[j2] = *reinterpret_cast<const uint32_t*>(a.v_new + src + 32 * j2 + 2 * n);
+          for (int qq = 0; qq < LW; ++qq) {
+            vpatch[2 * qq] = *reinterpret_cast<const uint32_t*>(a.v_new + src + 64 * qq + 2 * n);
+            vpatch[2 * qq + 1] = *reinterpret_cast<const uint32_t*>(a.v_new + src + 64 * qq + 32 + 2 * n);
+          }
+        } else {
+#pragma unroll
+          for (int j2 = 0; j2 < KK; ++j2)
+            vpatch[j2] = *reinterpret_cast<const uint32_t*>(a.v_new + src + 32 * j2 + 2 * n);
+        }
       }
     }
   }
   const bool bad_blk = __ballot(id_bad) != 0 || slot_bad;
+  // FP8: the codes of two 16-bit values (a word) and of two words, low byte first
+  auto code2 = [](uint32_t x, float sc) {
+    return fp8_code(E::to_float(static_cast<uint16_t>(x & 0xffff)), sc) |
+           fp8_code(E::to_float(static_cast<uint16_t>(x >> 16)), sc) << 8;
+  };
+  auto code4 = [&](uint32_t x, uint32_t y, float sc) { return code2(x, sc) | code2(y, sc) << 16; };
   auto stash_patch = [&]() {   // after the first tile loads are issued
     if (st_on && n == st_off) {
+      if constexpr (kFp8) {
+        const float ks = a.k_scales[kvh];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) st_k[kk] = kpatch[kk];
+        for (int pp = 0; pp < LW; ++pp)
+          st_k[pp] = u32x4{code4(kpatch[2 * pp][0], kpatch[2 * pp][1], ks),
+                           code4(kpatch[2 * pp][2], kpatch[2 * pp][3], ks),
+                           code4(kpatch[2 * pp + 1][0], kpatch[2 * pp + 1][1], ks),
+                           code4(kpatch[2 * pp + 1][2], kpatch[2 * pp + 1][3], ks)};
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) st_k[kk] = kpatch[kk];
+      }
     }
     if (st_on && g4 == (st_off >> 2)) {
+      if constexpr (kFp8) {
+        // codes of dims (2n, 2n + 1) of both halves: the (half, parity) order of a word
+        const float vs = a.v_scales[kvh];
 #pragma unroll
-      for (int j2 = 0; j2 < KK; ++j2) st_v[j2] = vpatch[j2];
+        for (int qq = 0; qq < LW; ++qq) st_v[qq] = code4(vpatch[2 * qq], vpatch[2 * qq + 1], vs);
+      } else {
+#pragma unroll
+        for (int j2 = 0; j2 < KK; ++j2) st_v[j2] = vpatch[j2];
+      }
     }
   };
 
@@ -612,6 +657,34 @@ void decode_attn_kernel(DecodeArgs a) {
   // Block i of the wave; i >= nw is a padding step whose positions are all masked,
   // which leaves m_run, l_run and acc unchanged (m_run is finite by then).
   auto compute_block = [&](int buf, int32_t i) {
+    if (kFp8 && st_on && i == st_i) {
+      const int32_t phys = __builtin_amdgcn_readlane(ids, i);
+      char* kt8 = reinterpret_cast<char*>(a.k_dst) + phys * blk_stride_b + head_off_b;
+      char* vt8 = reinterpret_cast<char*>(a.v_dst) + phys * blk_stride_b + head_off_b;
+      if (n == st_off) {          // K codes of token st_off: 16 dims per lane per step
+#pragma unroll
+        for (int pp = 0; pp < LW; ++pp) {
+          kb[buf][pp] = st_k[pp];
+          *reinterpret_cast<u32x4*>(kt8 + ((pp * 16 + n) * 4 + g4) * 16) = kb[buf][pp];
+        }
+      }
+      if (g4 == (st_off >> 2)) {  // V: byte st_off % 4 of each (half, parity) word
+        const int32_t e = st_off & 3;
+#pragma unroll
+        for (int qq = 0; qq < LW; ++qq) {
+          const uint32_t c = st_v[qq];
+          u32x4 wv = vb[buf][qq];
+          char* vd = vt8 + ((g4 * (D / 64) + qq) * 16 + n) * 16 + e;
+#pragma unroll
+          for (int hp = 0; hp < 4; ++hp) {
+            const uint32_t code = (c >> (8 * hp)) & 0xffu;
+            wv[hp] = (wv[hp] & ~(0xffu << (8 * e))) | (code << (8 * e));
+            vd[4 * hp] = static_cast<char>(code);
+          }
+          vb[buf][qq] = wv;
+        }
+      }
+    }
     if (!kFp8 && st_on && i == st_i) {
       const int32_t phys = __builtin_amdgcn_readlane(ids, i);
       uint16_t* kt = a.k_dst + phys * blk_stride + head_off;
@@ -1221,8 +1294,8 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
     if (!v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new) ||
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
       return pa::fail(PA_ERR_INVALID_ARG, "%s: k_new / v_new / slot_mapping NULL or misaligned", fn);
-    if (su.fp8) {
-      // FP8 pools: the quantising store is its own launch, before the attention pass
+    if (su.fp8 && su.wide_group) {
+      // the several-token kernels do not store: the quantising store is its own launch
       const int64_t grid = (static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
                             (cache->head_dim / 8) + 255) / 256;
       launch_write8(cache, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),

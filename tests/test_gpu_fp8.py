@@ -173,3 +173,43 @@ def test_fp8_chunks(q_lens, H, Hkv, D, dt):
     wl = custom_workload(ctx, H, Hkv, D, dtype=dt, seed=H + D + q_lens[0])
     say(f"FP8 pools, chunks {q_lens} over {ctx}, H={H} Hkv={Hkv} D={D} {dt}")
     _chunk_fp8(wl, np.minimum(q_lens, ctx), range(len(ctx)), f"fp8 chunks H={H} D={D}")
+
+
+def test_fp8_fused_store_contract():
+    """The step's quantising store runs inside the attention pass on FP8 pools too:
+    the new tokens' codes are the oracle's, and a slot that is not the sequence's last
+    position is not stored and poisons only that sequence (a negative slot stores
+    nothing)."""
+    from paged_kv_cache_385_amd import alloc_workspace, decode_fused
+    from tests.test_gpu_parity import _step_inputs
+    from workloads import custom_workload
+    wl = custom_workload([20, 37, 600, 9], 8, 2, 128, dtype="bf16", seed=12)
+    ks, vs = _scales(wl)
+    say("FP8 fused store: codes, mismatched and negative slots")
+    cache, segs = _build(wl, ks, vs)
+    tab, ctx, slots, k_new, v_new = _step_inputs(wl, segs)
+    q = wl.q().cuda()
+    mx = int(wl.ctx_lens.max())
+    ws = alloc_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, mx)
+    kb = OL.k8_to_logical(cache.k_cache.cpu().numpy())
+    vb = OL.v8_to_logical(cache.v_cache.cpu().numpy())
+    bad = slots.clone()
+    bad[1] = slots[1] - 1          # an earlier position of sequence 1: rejected, not stored
+    bad[3] = -1                    # not stored
+    out = decode_fused(cache.k_cache, cache.v_cache, k_new, v_new, bad, q, tab, ctx, mx, wl.scale,
+                       workspace=ws, scales=cache.scales)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    assert not torch.isnan(out[[0, 2]].float()).any()
+    check_close(out, _oracle_out(wl, segs, ks, vs, [0, 2]), wl.dtype, rows=[0, 2],
+                label="FP8 fused, valid rows")
+    kd = OL.k8_to_logical(cache.k_cache.cpu().numpy())
+    vd = OL.v8_to_logical(cache.v_cache.cpu().numpy())
+    for pool_d, pool_b in ((kd, kb), (vd, vb)):
+        diff = np.argwhere((pool_d != pool_b).any(axis=(1, 3)))
+        assert {int(b) * 16 + int(t) for b, t in diff} == {int(slots[0]), int(slots[2])}
+    for i in (0, 2):
+        s = int(slots[i])
+        kq = OF.quantize(k_new[i].float().cpu().numpy(), ks[:, None])
+        vq = OF.quantize(v_new[i].float().cpu().numpy(), vs[:, None])
+        assert np.array_equal(kd[s // 16, :, s % 16, :], kq) and np.array_equal(vd[s // 16, :, s % 16, :], vq)
