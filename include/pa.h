@@ -638,9 +638,15 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  *      and copy-on-write pairs into staging_host (pinned host memory) in the
  *      layout below;
  *   2. enqueues one copy of that region to staging_dev (device memory) -- on
- *      `stream`, or, when copy_stream is given, on copy_stream, records
- *      copy_event (a hipEvent_t) there and makes `stream` wait for it, so the
- *      copy can run while earlier work of `stream` still runs -- or, when
+ *      `stream`, or, when copy_stream is given, on copy_stream, so the copy can
+ *      run while earlier work of `stream` still runs, and records copy_event (a
+ *      hipEvent_t) there.  If `stream` still has work in flight, the call then
+ *      waits on the host for copy_event before it enqueues the kernels (a wait
+ *      placed in `stream` would cost queue time between the kernels); if
+ *      `stream` is idle, it makes `stream` wait for copy_event instead.  The
+ *      host wait lasts as long as the copy and whatever copy_stream ran
+ *      before it.  PA_STEP_STREAM_WAIT=1 in the environment always takes the
+ *      stream wait -- or, when
  *      staging_dev is NULL, nothing: the kernels read staging_host in place (it
  *      must then be pinned host memory mapped for the device, as hipHostMalloc
  *      returns);
@@ -664,8 +670,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  * that take the start and end of the attention kernel itself (attached to its
  * dispatch; with more than 16 query heads per KV head, recorded before and
  * after the attention launches), NULL to skip.  info (optional) receives
- * the number of copy-on-write pairs, the longest context of the step and
- * whether it decoded as groups.
+ * the number of copy-on-write pairs, the longest context of the step,
+ * whether it decoded as groups and whether the host waited for the copy.
  * The decode reads through the caches (PA_CACHE_SHARED_BLOCKS) whenever the
  * block manager holds a block with more than one reference.
  * Every argument is checked before the block manager changes; after that only
@@ -675,6 +681,7 @@ typedef struct pa_step_info {
   int32_t num_cow;
   int32_t max_context_len;
   int32_t grouped;          /* 1: pa_decode_grouped ran, 0: pa_decode_fused */
+  int32_t host_waited;      /* 1: the host waited for the copy on copy_stream */
 } pa_step_info;
 
 size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);

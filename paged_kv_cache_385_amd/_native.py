@@ -53,7 +53,8 @@ class PaBmPrefixStats(C.Structure):
 
 
 class PaStepInfo(C.Structure):
-    _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32), ("grouped", C.c_int32)]
+    _fields_ = [("num_cow", C.c_int32), ("max_context_len", C.c_int32), ("grouped", C.c_int32),
+                ("host_waited", C.c_int32)]
 
 
 class PaError(RuntimeError):

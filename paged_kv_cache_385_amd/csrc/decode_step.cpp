@@ -7,9 +7,10 @@
 //   1. host: the block manager reserves every sequence's next slot, reporting
 //      copy-on-write pairs, and packs tables and lengths into the staging buffer;
 //   2. one host-to-device copy of the staging buffer -- on the caller's stream,
-//      or on a copy stream that the caller's stream then waits for (the copy
-//      of step i + 1 can run while step i's kernels still run) -- or none: with
-//      no device staging buffer the kernels read the pinned one in place;
+//      or on a copy stream (the copy of step i + 1 runs while step i's kernels
+//      still run; the host, or on an idle stream the stream, waits for it) --
+//      or none: with no device staging buffer the kernels read the pinned one
+//      in place;
 //   3. pa_copy_blocks for the pairs (two 16-token tiles per copied block of a
 //      32-token manager), then pa_decode_fused (the new tokens'
 //      store and the decode in one attention pass, then the merge) -- all on
@@ -54,6 +55,16 @@ bool grouped_enabled() {
   static const bool on = [] {
     const char* e = std::getenv("PA_GROUPED_DECODE");
     return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
+// PA_STEP_STREAM_WAIT=1 in the environment: a step with a copy stream always makes its
+// stream wait for the copy, never the host.
+bool stream_wait_forced() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_STEP_STREAM_WAIT");
+    return e && e[0] == '1';
   }();
   return on;
 }
@@ -126,6 +137,7 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
     info->num_cow = n_cow;
     info->max_context_len = max_ctx;
     info->grouped = plan_ints > 0 ? 1 : 0;
+    info->host_waited = 0;
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -144,8 +156,16 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
       return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
     if (copy_stream) {
       hipEvent_t ev = static_cast<hipEvent_t>(copy_event);
-      if (hipEventRecord(ev, cs) != hipSuccess || hipStreamWaitEvent(s, ev, 0) != hipSuccess)
+      // While `stream` still runs earlier work, the host waits for the copy, which lands
+      // long before that work ends, and the kernels are queued with no cross-stream
+      // wait: such a wait is a barrier packet that costs the step several microseconds
+      // of queue time even when it is already satisfied.  On an idle stream the wait
+      // goes into the stream, so the host does not block.
+      const bool host_wait = !stream_wait_forced() && hipStreamQuery(s) == hipErrorNotReady;
+      if (hipEventRecord(ev, cs) != hipSuccess ||
+          (host_wait ? hipEventSynchronize(ev) : hipStreamWaitEvent(s, ev, 0)) != hipSuccess)
         return pa::fail(PA_ERR_HIP, "pa_decode_step: copy-stream event failed");
+      if (info) info->host_waited = host_wait ? 1 : 0;
     }
   }
   if (n_cow) {

@@ -189,8 +189,10 @@ class DecodeBatch:
 
     * ``"mapped"``: they read the pinned buffer in place (no copy);
     * ``"upload"``: one copy to a device buffer on the step's stream;
-    * ``"side"``: the copy runs on a side stream and the step's stream waits
-      for it, so the copy of step i + 1 overlaps the kernels of step i.
+    * ``"side"``: the copy runs on a side stream, so the copy of step i + 1
+      overlaps the kernels of step i; while the stream is busy the host waits
+      for the copy before queueing the kernels (``last_host_waited``), else the
+      stream waits for it.
 
     The default is "side"; ``zero_copy`` is the older switch (True: "mapped",
     False: "upload"), and an explicit ``staging`` wins over it.  Two pinned buffers (and, for "side", two device
@@ -258,6 +260,7 @@ class DecodeBatch:
         self._i = 0
         self.last_max_ctx = 0
         self.last_grouped = False
+        self.last_host_waited = False
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
 
     def _staged_dev(self) -> torch.Tensor:
@@ -344,4 +347,5 @@ class DecodeBatch:
             self.last_pairs = np.zeros((0, 2), dtype=np.int32)
         self.last_max_ctx = self._info.max_context_len
         self.last_grouped = bool(self._info.grouped)
+        self.last_host_waited = bool(self._info.host_waited)
         return self.out
