@@ -34,6 +34,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 EVENT_EVERY = 5                # timed steps whose attention pass carries a timing event pair
+TIMELINE_STEPS = 5             # steps captured with per-workgroup stamps (--timeline)
+TIMELINE_HZ = 100e6            # the kernel's stamps count a constant 100 MHz clock
 FLUSH_BYTES = 1 << 30          # written before a flushed step: > 8 x 4 MB L2 + 256 MB Infinity Cache
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, AMD published (no sparsity)
@@ -91,6 +93,10 @@ def parse():
                     help="after the timed steps, this many more steps each preceded by a "
                          f"{FLUSH_BYTES >> 20} MiB write that evicts L2 and the Infinity Cache "
                          "(outside the attention events): the flushed roofline fraction")
+    ap.add_argument("--timeline", metavar="OUT_JSON",
+                    help="load libpa_timeline.so (the decode kernel stamps every workgroup), "
+                         f"capture {TIMELINE_STEPS} more single steps after the others and write "
+                         "the per-workgroup timeline summary to OUT_JSON")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read probes (the measured read ceiling)")
     ap.add_argument("--no-other-ops", action="store_true",
@@ -814,11 +820,124 @@ def run_swap(args):
     print(json.dumps(result), flush=True)
 
 
+def timeline_summary(recs, event_us):
+    """Summary of one decode launch's per-workgroup records (pa_timeline.h layout): the
+    span of the pass, how many workgroups run at once, each one's fixed start-up (item
+    known, first tile computed), wave 0's pace per tile, and where the workgroups ran."""
+    block = np.nonzero(recs[:, 0] != 0)[0]           # blockIdx.x of every written record
+    recs = recs[block]
+    t0 = recs[:, 0].min()
+    entry, plan, first, loop, out = ((recs[:, i] - t0).astype(np.float64) * (1e6 / TIMELINE_HZ)
+                                     for i in range(5))
+    has_first = recs[:, 2] != 0
+    first = np.where(has_first, first, np.nan)
+    tiles = (recs[:, 6] & 0xFFFF).astype(np.int64)
+    nw0 = ((recs[:, 6] >> 16) & 0xFFFF).astype(np.int64)
+    xcc = (recs[:, 7] >> 32).astype(np.int64)
+    hw = (recs[:, 7] & 0xFFFFFFFF).astype(np.int64)
+    # a compute unit: XCC, shader engine (HW_ID bits 15:13), array (bit 12), CU (bits 11:8)
+    cu = (xcc << 8) | (((hw >> 13) & 0x7) << 5) | (((hw >> 12) & 0x1) << 4) | ((hw >> 8) & 0xF)
+    # workgroups running over time: +1 at entry, -1 once the output is written
+    ev = np.concatenate([np.stack([entry, np.ones_like(entry)], 1),
+                         np.stack([out, -np.ones_like(out)], 1)])
+    ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]
+    active = np.cumsum(ev[:, 1])
+    span = float(out.max())
+    edges = np.arange(0.0, span + 10.0, 10.0)
+
+    def pct(x, q):
+        return round(float(np.nanpercentile(x, q)), 2)
+
+    startup = first - entry
+    late = np.argsort(entry)[-256:]                  # the last 256 workgroups to start
+    # the workgroups resident from the start (entered before any workgroup finished), per
+    # compute unit in block order: the start-up of the CU's 1st, 2nd, ... of them
+    initial = entry < out.min()
+    by_rank = {}
+    for c in np.unique(cu[initial]):
+        idx = np.nonzero(initial & (cu == c))[0]
+        for rank, i in enumerate(idx[np.argsort(block[idx])]):
+            by_rank.setdefault(rank, []).append(startup[i])
+    paced = has_first & (nw0 >= 4)
+    pace = (loop - first)[paced] / (nw0[paced] - 1)
+    r = recs.astype(np.int64)
+    ordered = ((r[:, 0] <= r[:, 1]) & (r[:, 1] <= r[:, 3]) & (r[:, 3] <= r[:, 4]) &
+               ((r[:, 2] == 0) | ((r[:, 1] <= r[:, 2]) & (r[:, 2] <= r[:, 3]))))
+    return {
+        "workgroups": int(len(recs)),
+        "misordered": int((~ordered).sum()),
+        "tiles_per_kv_head": int(tiles.sum()),
+        "span_us": round(span, 2),
+        "event_us": round(event_us, 2),
+        "max_running": int(active.max()),
+        "max_running_reached_us": round(float(ev[np.argmax(active), 0]), 2),
+        "running_per_10us": [int(((entry < hi) & (out > lo)).sum())
+                             for lo, hi in zip(edges[:-1], edges[1:])],
+        "plan_us": {"median": pct(plan - entry, 50), "p90": pct(plan - entry, 90)},
+        "first_tile_after_plan_us": {"median": pct(first - plan, 50), "p90": pct(first - plan, 90)},
+        "startup_us": {"median": pct(startup, 50), "p90": pct(startup, 90)},
+        "initial_per_cu": int(initial.sum()) / max(len(np.unique(cu[initial])), 1),
+        "initial_startup_by_block_rank_us": [
+            {"median": pct(np.array(v), 50), "p90": pct(np.array(v), 90)}
+            for _, v in sorted(by_rank.items())],
+        "last_256_start_us": [round(float(entry[late].min()), 2), round(float(entry[late].max()), 2)],
+        "last_256_startup_us": {"median": pct(startup[late], 50), "p90": pct(startup[late], 90)},
+        "wave0_us_per_tile": {"median": pct(pace, 50), "p10": pct(pace, 10), "p90": pct(pace, 90)},
+        "per_xcc": [int((xcc == x).sum()) for x in range(8)],
+        # blocks whose index leaves residue r mod 8: the XCCs they ran on (one each when
+        # the dispatcher deals blocks to the XCDs in turn)
+        "xcc_of_block_mod_8": [sorted(int(x) for x in np.unique(xcc[block % 8 == m]))
+                               for m in range(8)],
+        "compute_units": int(len(np.unique(cu))),
+    }
+
+
+def capture_timeline(path, native, batch, steps_kv, q, wl, first_step):
+    """Single decode steps with the instrumented library: clear the records, run the
+    step (attention pass between events), read every workgroup's record; the summaries
+    go to `path` as JSON."""
+    import torch
+    lib = native.lib()
+    recs = np.zeros((native.TIMELINE_MAX_WORKGROUPS, native.TIMELINE_WORDS), dtype=np.uint64)
+    launches, raw, blocks = [], [], []
+    for i, (k, v) in enumerate(steps_kv):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        native.check(lib.pa_timeline_clear(batch.stream.cuda_stream), "pa_timeline_clear")
+        batch.step(k, v, q, attn_events=(e0, e1))
+        torch.cuda.synchronize()
+        native.check(lib.pa_timeline_read(recs.ctypes.data, recs.shape[0]), "pa_timeline_read")
+        if batch.last_grouped or not (recs[:, 0] != 0).any():
+            raise SystemExit("--timeline: the step ran no decode_attn_kernel (grouped decode and "
+                             "the chunk kernels take no stamps)")
+        t = {"step": first_step + i, **timeline_summary(recs, e0.elapsed_time(e1) * 1e3)}
+        launches.append(t)
+        log(f"timeline: {t['workgroups']} workgroups, span {t['span_us']} us (events "
+            f"{t['event_us']} us), at most {t['max_running']} running "
+            f"(reached at {t['max_running_reached_us']} us), start-up median "
+            f"{t['startup_us']['median']} p90 {t['startup_us']['p90']} us, wave 0 "
+            f"{t['wave0_us_per_tile']['median']} us per tile, {t['compute_units']} CUs, "
+            f"XCC of block mod 8: {t['xcc_of_block_mod_8']}")
+        raw.append(recs[recs[:, 0] != 0].copy())
+        blocks.append(np.nonzero(recs[:, 0] != 0)[0])
+    with open(path, "w") as f:
+        json.dump({"workload": wl.cfg_id, "name": wl.name, "library": "libpa_timeline.so",
+                   "clock_hz": TIMELINE_HZ, "launches": launches}, f, indent=1)
+        f.write("\n")
+    # the raw records beside it: records_i (pa_timeline.h layout) and blocks_i (blockIdx.x)
+    np.savez_compressed(os.path.splitext(path)[0] + "_records.npz",
+                        **{f"records_{i}": r for i, r in enumerate(raw)},
+                        **{f"blocks_{i}": b for i, b in enumerate(blocks)})
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
         return
+    if args.timeline and (args.swap or args.prefix or args.chunk):
+        print("--timeline stamps the decode kernel: not with --swap, --prefix or --chunk",
+              file=sys.stderr)
+        sys.exit(2)
     if args.swap:
         if args.gpus != 1:
             print(f"bench.py measures one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -841,6 +960,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.timeline:
+        # the instrumented build of the same library (before the binding loads one)
+        os.environ["PA_LIB_PATH"] = os.path.join(ROOT, "paged_kv_cache_385_amd", "libpa_timeline.so")
     import torch
     from workloads import make_workload, new_token_kv
     import paged_kv_cache_385_amd as pa
@@ -851,7 +973,8 @@ def main():
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
     F = args.flush_steps
-    wl = make_workload(args.workload, grow=K + W + F)
+    T = TIMELINE_STEPS if args.timeline else 0
+    wl = make_workload(args.workload, grow=K + W + F + T)
     B, H, Hkv, D = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim
     log(f"workload {wl.cfg_id} ({wl.name}): B={B} H={H} Hkv={Hkv} D={D} {wl.dtype_name}, "
         f"ctx mean {wl.ctx_lens.mean():.0f} max {wl.ctx_lens.max()}, pool {wl.num_blocks} blocks")
@@ -880,11 +1003,11 @@ def main():
     segs.clear()
     sids = [op[1] for op in wl.step]
     bsz = args.block_size
-    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W + F) // bsz) * (bsz // 16)   # in 16-token tiles
+    max_blocks = -(-(int(wl.ctx_lens.max()) + K + W + F + T) // bsz) * (bsz // 16)   # 16-token tiles
     batch = pa.DecodeBatch(cache, sids, H, wl.scale, max_blocks, staging=args.staging)
     q = wl.q().to(dev)
     steps_kv = []
-    for i in range(K + W + F):
+    for i in range(K + W + F + T):
         k, v = new_token_kv(wl.seed, i, B, Hkv, D, wl.dtype)
         steps_kv.append((k.to(dev), v.to(dev)))
     torch.cuda.synchronize()
@@ -938,6 +1061,9 @@ def main():
         flushed_ms = [a.elapsed_time(b) for a, b in fev]
         del flush
 
+    if T:
+        capture_timeline(args.timeline, _native, batch, steps_kv[W + K + F:], q, wl, W + K + F)
+
     kv_read = sum(int((base_ctx + W + j).sum()) * per_tok for j in range(K))
     value = kv_read / wall / 1e9
     attn_avg_ms = float(np.mean(attn_ms))
@@ -945,7 +1071,7 @@ def main():
     # block, the most tokens any sharer keeps in it; all live sequences are the batch's,
     # and each step adds one private token per sequence.
     occupied = int(cache.bm.stats()["occupied_slots"])
-    last = W + K + F - 1                       # the step the block manager's count is taken at
+    last = W + K + F + T - 1                   # the step the block manager's count is taken at
 
     def unique_bytes(i):
         ctx = base_ctx + i

@@ -31,6 +31,8 @@ PA_SWAP_IN = 1
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
 NOALLOC_SCRATCH_BYTES = 64 << 20
+TIMELINE_WORDS = 8
+TIMELINE_MAX_WORKGROUPS = 65536
 
 
 class PaCache(C.Structure):
@@ -139,6 +141,8 @@ SIGNATURES = {
     # measurement probes (pa_probe.h)
     "pa_probe_read_contiguous": (C.c_int, [_P, C.c_size_t, _I32, _P, _P]),
     "pa_probe_read_tiles": (C.c_int, [_P, _P, C.c_size_t, _P, _P, _I32, _I32, _P, _P]),
+    "pa_timeline_clear": (C.c_int, [_P]),
+    "pa_timeline_read": (C.c_int, [_P, _I32]),
 }
 
 _lib = None

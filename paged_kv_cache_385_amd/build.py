@@ -1,4 +1,6 @@
 """Build libpa.so in-tree: HIP kernels for gfx950 plus the host block manager.
+Also builds libpa_timeline.so, the same library whose decode kernel records a
+per-workgroup timeline (pa_timeline.h).
 
     python -m paged_kv_cache_385_amd.build
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+# the same library with the decode kernel's per-workgroup timeline (pa_timeline.h)
+LIB_TIMELINE = os.path.join(PKG, "libpa_timeline.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -79,6 +83,13 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, k_o, c_o, n_o, p_o,
           gp_o, g_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    tl_o = os.path.join(BUILD, "pa_kernels_timeline.o")
+    _run([hipcc, *HIP_FLAGS, *inc, "-DPA_TIMELINE", "-c", os.path.join(CSRC, "pa_kernels.hip"),
+          "-o", tl_o], verbose)
+    tmp = LIB_TIMELINE + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bm_o, step_o, tl_o, c_o, n_o, p_o,
+          gp_o, g_o, "-o", tmp], verbose)
+    os.replace(tmp, LIB_TIMELINE)
     return LIB
 
 

@@ -36,6 +36,16 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_timeline.h"
+
+#ifdef PA_TIMELINE
+// Records of the decode kernel's workgroups (instrumented build only; layout in
+// pa_timeline.h).  TL_STAMP reads the constant 100 MHz counter.
+__device__ uint64_t g_timeline[PA_TIMELINE_MAX_WORKGROUPS * PA_TIMELINE_WORDS];
+#define TL_STAMP(v) v = __builtin_amdgcn_s_memrealtime()
+#else
+#define TL_STAMP(v) ((void)0)
+#endif
 
 namespace {
 
@@ -467,8 +477,11 @@ void decode_attn_kernel(DecodeArgs a) {
   const int32_t tid = threadIdx.x;
   const int32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t lane = tid & 63;
+  [[maybe_unused]] uint64_t t_entry = 0, t_plan = 0, t_first = 0, t_loop = 0;
+  TL_STAMP(t_entry);
   int32_t b, kg, p, ctx;
   if (!plan_item(a, lane, &b, &kg, &p, &ctx)) return;
+  TL_STAMP(t_plan);
   b = __builtin_amdgcn_readfirstlane(b);
   kg = __builtin_amdgcn_readfirstlane(kg);
   p = __builtin_amdgcn_readfirstlane(p);
@@ -785,11 +798,15 @@ void decode_attn_kernel(DecodeArgs a) {
       load_block(1, i + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute_block(0, i);
+#ifdef PA_TIMELINE
+      if (i == 0) TL_STAMP(t_first);
+#endif
       load_block(0, i + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute_block(1, i + 1);
     }
   }
+  TL_STAMP(t_loop);
 
   // ---- combine the four waves of the workgroup in LDS ----
   l_run += __shfl_xor(l_run, 16);
@@ -867,6 +884,24 @@ void decode_attn_kernel(DecodeArgs a) {
       }
     }
   }
+#ifdef PA_TIMELINE
+  if (tid == 0 && blockIdx.x < PA_TIMELINE_MAX_WORKGROUPS) {
+    uint64_t t_out;
+    TL_STAMP(t_out);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg(0x1814);   // XCC_ID, bits 3:0
+    const uint32_t hw = __builtin_amdgcn_s_getreg(0xf804);    // HW_ID, all 32 bits
+    uint64_t* r = g_timeline + static_cast<uint64_t>(blockIdx.x) * PA_TIMELINE_WORDS;
+    r[0] = t_entry;
+    r[1] = t_plan;
+    r[2] = t_first;
+    r[3] = t_loop;
+    r[4] = t_out;
+    r[5] = (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(p);
+    r[6] = (static_cast<uint64_t>(kg) << 32) | (static_cast<uint32_t>(nw) << 16) |
+           static_cast<uint32_t>(jend - p * PB);
+    r[7] = (static_cast<uint64_t>(xcc) << 32) | hw;
+  }
+#endif
   if (nparts == 1 || a.counters == nullptr) return;
 
   // Fused merge: the last of the sequence's partitions (for these KV heads) to
@@ -1565,6 +1600,41 @@ pa_status pa_decode_fused(const pa_cache* cache, const void* k_new, const void* 
                         max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
                         workspace_bytes, k_new, v_new, slot_mapping, true, true, 0, nullptr,
                         nullptr, stream);
+}
+
+// ---- timeline of the decode kernel (instrumented build) ---------------------------
+pa_status pa_timeline_clear(void* stream) {
+  pa::clear_error();
+#ifdef PA_TIMELINE
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_timeline)) != hipSuccess || !ptr)
+    return pa::fail(PA_ERR_HIP, "pa_timeline_clear: no device address for the records");
+  if (hipMemsetAsync(ptr, 0, sizeof(g_timeline), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "pa_timeline_clear: hipMemsetAsync failed");
+  return PA_OK;
+#else
+  (void)stream;
+  return pa::fail(PA_ERR_UNSUPPORTED, "pa_timeline_clear: library built without PA_TIMELINE");
+#endif
+}
+
+pa_status pa_timeline_read(uint64_t* host, int32_t num_workgroups) {
+  pa::clear_error();
+  if (!host || num_workgroups < 1 || num_workgroups > PA_TIMELINE_MAX_WORKGROUPS)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_timeline_read: host NULL or num_workgroups %d (1 .. %d)",
+                    num_workgroups, PA_TIMELINE_MAX_WORKGROUPS);
+#ifdef PA_TIMELINE
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_timeline)) != hipSuccess || !ptr)
+    return pa::fail(PA_ERR_HIP, "pa_timeline_read: no device address for the records");
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(host, ptr, sizeof(uint64_t) * PA_TIMELINE_WORDS * num_workgroups,
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return pa::fail(PA_ERR_HIP, "pa_timeline_read: copy failed");
+  return PA_OK;
+#else
+  return pa::fail(PA_ERR_UNSUPPORTED, "pa_timeline_read: library built without PA_TIMELINE");
+#endif
 }
 
 }  // extern "C"
