@@ -603,6 +603,9 @@ pa_status pa_swap_blocks(const pa_cache* device, const pa_cache* host, int32_t d
  *   block_tables, context_lens, max_context_len, max_blocks_per_seq: as pa_decode.
  *   workspace        device, >= pa_chunk_workspace_size(...) bytes, 16-byte aligned
  *                    (NULL when that size is 0).
+ *   attn_begin, attn_end  optional hipEvent_t (NULL to skip), attached to the
+ *                    dispatches: the start of the attention kernel and the end of
+ *                    the call's last kernel (the merge, when there is one).
  * One workgroup per (sequence, KV head, 16-48 (token, head) columns, key
  * partition), sequences taken longest first when there are at most 48 columns
  * and the launch gives each workgroup slot at most 4 items;
@@ -626,7 +629,8 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
                              int32_t num_heads, const int32_t* block_tables,
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t max_context_len, float scale, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, void* attn_begin, void* attn_end,
+                             void* stream);
 
 /* ===========================================================================
  * pa_decode_step -- one whole decode step of a batch, in one call.
@@ -667,9 +671,9 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  * makes copy_stream wait for the end of the step that last read staging_dev).
  * workspace: at least pa_decode_workspace_size(n, num_heads, head_dim,
  * 16 * max_blocks_per_seq) bytes.  attn_begin / attn_end: optional hipEvent_t
- * that take the start and end of the attention kernel itself (attached to its
- * dispatch; with more than 16 query heads per KV head, recorded before and
- * after the attention launches), NULL to skip.  info (optional) receives
+ * that take the start and end of the attention kernels themselves (attached to
+ * their dispatches: the start of the attention kernel, the end of the last
+ * launch of the pass), NULL to skip.  info (optional) receives
  * the number of copy-on-write pairs, the longest context of the step,
  * whether it decoded as groups and whether the host waited for the copy.
  * The decode reads through the caches (PA_CACHE_SHARED_BLOCKS) whenever the

@@ -133,7 +133,7 @@ SIGNATURES = {
     "pa_swap_blocks": (C.c_int, [C.POINTER(PaCache), C.POINTER(PaCache), _I32, _P, _P, _I32, _P]),
     "pa_chunk_workspace_size": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_chunk_attention": (C.c_int, [C.POINTER(PaCache), _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
-                                     _P, _I32, C.c_float, _P, _P, C.c_size_t, _P]),
+                                     _P, _I32, C.c_float, _P, _P, C.c_size_t, _P, _P, _P]),
     "pa_decode_step_staging_bytes": (C.c_size_t, [_I32, _I32]),
     "pa_decode_step": (C.c_int, [_P, C.POINTER(PaCache), _I32, _P, _P, _P, _P, _I32, C.c_float, _P,
                                  _P, C.c_size_t, _P, _P, C.c_size_t, _I32, _P, _P,

@@ -37,6 +37,7 @@
 // P values (tokens 4g..4g+3 of each block, g = l / 16, from the two S^T tiles)
 // as its B operand and the interleaved V rows as A.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -335,6 +336,7 @@ void chunk_attn_kernel(ChunkArgs a) {
   float m_run[NT];
   f32x4 acc[NT][MT], lsum[NT];
   const u16x4 ones = __builtin_bit_cast(u16x4, uint2{E::kOne2, E::kOne2});
+  const u32x4 ones4 = {E::kOne2, E::kOne2, E::kOne2, E::kOne2};
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_run[t] = -INFINITY;
@@ -342,7 +344,10 @@ void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  u32x4 kb[2][LW], vb[2][LW];     // 16-bit pools: the operands themselves; FP8: raw codes
+  // FP8 pools take the wave's blocks in pairs (four code buffers; below), except
+  // three tiles at three waves per SIMD, whose registers that does not fit
+  constexpr bool kPairs = kFp8 && (NT < 3 || NT * D > 192);
+  u32x4 kb[kPairs ? 4 : 2][LW], vb[kPairs ? 4 : 2][LW];   // 16-bit: the operands; FP8: codes
   // The wave's blocks go in runs of up to 64: lane i holds the id of the run's i-th.
   int32_t ids = 0, i0 = 0, cnt = 0;
 
@@ -463,6 +468,103 @@ void chunk_attn_kernel(ChunkArgs a) {
     }
   };
 
+  // FP8 pools: blocks i and i + 1 of the wave (buffers b0, b0 + 1) in one step.  The
+  // codes of the two blocks widen straight into the operands of the 32-token matrix
+  // instruction (a 16-byte operand holds 4 tokens of each), so P.V takes half the
+  // matrix instructions of two 16-token steps, and the pair shares one maximum, one
+  // rescale and one column-sum instruction.  Positions past the context get zero
+  // codes (they may hold anything, NaN codes included).
+  auto compute_pair = [&](int b0, int32_t i) {
+    int32_t t0[2], valid[2];
+    uint32_t keep[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      t0[h] = (first + kWaves * (i0 + i + h)) * kBlock;
+      valid[h] = i + h < cnt ? ctx - t0[h] : 0;
+      // code byte e of a word is token 4 g4 + e
+      const int32_t nv = min(max(valid[h] - 4 * g4, 0), 4);
+      keep[h] = nv >= 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
+    }
+    // scores: each q fragment serves both blocks
+    u32x4 K[2][KK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < LW; ++t) {
+        K[h][2 * t] = widen_fp8<E>(kb[b0 + h][t][0], kb[b0 + h][t][1]);
+        K[h][2 * t + 1] = widen_fp8<E>(kb[b0 + h][t][2], kb[b0 + h][t][3]);
+      }
+    f32x4 s[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 qv;
+        if constexpr (kQLds)
+          qv = s_q[(t * KK + kk) * 64 + lane];
+        else
+          qv = qf[t][kk];
+        s[t][0] = E::mfma_qk(K[0][kk], qv, s[t][0]);
+        s[t][1] = E::mfma_qk(K[1][kk], qv, s[t][1]);
+      }
+    }
+    // softmax of every tile first (its scores become the 4-word P operand), so the
+    // widened V operands below are not live beside the scores
+    __builtin_amdgcn_sched_barrier(0);
+    const bool diag = i + 1 >= cnt || t0[1] + kBlock - 1 > pmin;
+    const float c = score_scale;
+    u32x4 pw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float sv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) sv[r] = s[t][r >> 2][r & 3];
+      if (diag) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int32_t seen = i + h < cnt ? pos[t] - t0[h] : -1;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * g4 + r > seen) sv[4 * h + r] = -INFINITY;
+        }
+      }
+      const float bmax = col_max4_raw(max3_raw(max3_raw(sv[0], sv[1], sv[2]),
+                                               max3_raw(sv[3], sv[4], sv[5]),
+                                               max3_raw(sv[6], sv[7], sv[7])));
+      const float m_new = bmax * c > m_run[t] + kLazyMax ? bmax * c : m_run[t];
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[t] - m_use);
+      m_run[t] = m_new;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+        pw[t][w2] = E::pack2(fast_exp2(__builtin_fmaf(sv[2 * w2], c, -m_use)),
+                             fast_exp2(__builtin_fmaf(sv[2 * w2 + 1], c, -m_use)));
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[t][j] *= alpha;
+        lsum[t] *= alpha;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P.V: operand (j2, par) holds dims 64 qq + 32 hf + 2 n + par (j2 = 2 qq + hf) of the
+    // 4 tokens 4 g4 .. + 3 of block i, then the same 4 of block i + 1
+#pragma unroll
+    for (int qq = 0; qq < LW; ++qq)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          const u32x4 v2 = widen_fp8<E>(vb[b0][qq][2 * hf + par] & keep[0],
+                                        vb[b0 + 1][qq][2 * hf + par] & keep[1]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t][2 * (2 * qq + hf) + par] = E::mfma_qk(v2, pw[t], acc[t][2 * (2 * qq + hf) + par]);
+        }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) lsum[t] = E::mfma_qk(ones4, pw[t], lsum[t]);
+  };
+
   for (i0 = 0; i0 < nw; i0 += 64) {
     cnt = min(64, nw - i0);
     if (i0 == 0) {
@@ -474,14 +576,29 @@ void chunk_attn_kernel(ChunkArgs a) {
     const bool id_bad = lane < cnt && (ids < 0 || ids >= a.num_blocks);
     if (id_bad) ids = 0;
     bad_blk = bad_blk || __ballot(id_bad) != 0;
-    load_block(0, 0);
-    for (int32_t i = 0; i < cnt; i += 2) {
-      load_block(1, i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_block(0, i);
-      load_block(0, i + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_block(1, i + 1);
+    if constexpr (kPairs) {
+      load_block(0, 0);
+      load_block(1, 1);
+      for (int32_t i = 0; i < cnt; i += 4) {
+        load_block(2, i + 2);
+        load_block(3, i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_pair(0, i);
+        load_block(0, i + 4);
+        load_block(1, i + 5);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_pair(2, i + 2);
+      }
+    } else {
+      load_block(0, 0);
+      for (int32_t i = 0; i < cnt; i += 2) {
+        load_block(1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_block(0, i);
+        load_block(0, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_block(1, i + 1);
+      }
     }
   }
 
@@ -993,47 +1110,56 @@ ChunkPlan chunk_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, 
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// e0 / e1 (optional): events that take the start of the attention kernel and the end of
+// the call's last kernel, attached to the dispatches.
 template <class E, int D, bool kStream, bool kFp8>
-void launch_narrow(const ChunkArgs& a, int32_t nt, dim3 grid, hipStream_t s) {
+void launch_narrow(const ChunkArgs& a, int32_t nt, dim3 grid, hipStream_t s, hipEvent_t e0,
+                   hipEvent_t e1) {
   if (nt == 1)
-    chunk_attn_kernel<E, D, 1, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(chunk_attn_kernel<E, D, 1, kStream, kFp8>, grid, dim3(kThreads), 0, s,
+                          e0, e1, 0, a);
   else if (nt == 2)
-    chunk_attn_kernel<E, D, 2, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(chunk_attn_kernel<E, D, 2, kStream, kFp8>, grid, dim3(kThreads), 0, s,
+                          e0, e1, 0, a);
   else
-    chunk_attn_kernel<E, D, 3, kStream, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(chunk_attn_kernel<E, D, 3, kStream, kFp8>, grid, dim3(kThreads), 0, s,
+                          e0, e1, 0, a);
 }
 
 template <class E, int D, bool kFp8>
 void launch_chunk_d(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, bool stream,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(static_cast<uint32_t>(groups8 * p.tiles * p.parts));
+  hipEvent_t e1_attn = p.parts > 1 ? nullptr : e1;   // with a merge, it takes the end
   if (p.wide)
-    chunk_wide_kernel<E, D, kFp8><<<grid, dim3(kThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(chunk_wide_kernel<E, D, kFp8>, grid, dim3(kThreads), 0, s, e0, e1_attn,
+                          0, a);
   else if (stream)
-    launch_narrow<E, D, true, kFp8>(a, p.nt, grid, s);
+    launch_narrow<E, D, true, kFp8>(a, p.nt, grid, s, e0, e1_attn);
   else
-    launch_narrow<E, D, false, kFp8>(a, p.nt, grid, s);
+    launch_narrow<E, D, false, kFp8>(a, p.nt, grid, s, e0, e1_attn);
   if (p.parts > 1) {
     ChunkArgs m = a;                     // the merge works in 16-column tiles
     m.col_tiles = p.merge_tiles;
-    chunk_merge_kernel<E, D><<<dim3(static_cast<uint32_t>(groups8 * p.merge_tiles)),
-                               dim3(kThreads), 0, s>>>(m);
+    hipExtLaunchKernelGGL(chunk_merge_kernel<E, D>,
+                          dim3(static_cast<uint32_t>(groups8 * p.merge_tiles)), dim3(kThreads), 0,
+                          s, nullptr, e1, 0, m);
   }
 }
 
 template <class E>
 void launch_chunk(const ChunkArgs& a, const ChunkPlan& p, int64_t groups8, int d, bool fp8,
-                  bool stream, hipStream_t s) {
+                  bool stream, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (d == 64) {
     if (fp8)
-      launch_chunk_d<E, 64, true>(a, p, groups8, stream, s);
+      launch_chunk_d<E, 64, true>(a, p, groups8, stream, s, e0, e1);
     else
-      launch_chunk_d<E, 64, false>(a, p, groups8, stream, s);
+      launch_chunk_d<E, 64, false>(a, p, groups8, stream, s, e0, e1);
   } else {
     if (fp8)
-      launch_chunk_d<E, 128, true>(a, p, groups8, stream, s);
+      launch_chunk_d<E, 128, true>(a, p, groups8, stream, s, e0, e1);
     else
-      launch_chunk_d<E, 128, false>(a, p, groups8, stream, s);
+      launch_chunk_d<E, 128, false>(a, p, groups8, stream, s, e0, e1);
   }
 }
 
@@ -1047,7 +1173,8 @@ pa_status chunk_run(const char* fn, const pa_cache* cache, const void* q, const 
                     int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, void* ev_begin, void* ev_end,
+                    void* stream) {
   pa_status st = pa::check_cache(cache, fn);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || total_q < 0)
@@ -1114,20 +1241,22 @@ pa_status chunk_run(const char* fn, const pa_cache* cache, const void* q, const 
   // are shared between sequences
   const bool once = plan.tiles == 1 && !(cache->flags & PA_CACHE_SHARED_BLOCKS);
   const bool fp8 = (cache->flags & PA_CACHE_FP8) != 0;
+  const auto e0 = static_cast<hipEvent_t>(ev_begin), e1 = static_cast<hipEvent_t>(ev_end);
   if (cache->dtype == PA_F16)
-    launch_chunk<F16>(a, plan, groups8, cache->head_dim, fp8, once, s);
+    launch_chunk<F16>(a, plan, groups8, cache->head_dim, fp8, once, s, e0, e1);
   else
-    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, fp8, once, s);
+    launch_chunk<BF16>(a, plan, groups8, cache->head_dim, fp8, once, s, e0, e1);
   return pa::launch_status(fn);
 }
 
 pa_status chunk_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
                        int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t max_context_len, float scale,
-                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                       void* out, void* workspace, size_t workspace_bytes, void* ev_begin,
+                       void* ev_end, void* stream) {
   return chunk_run(fn, cache, q, nullptr, num_seqs, num_seqs, 1, num_heads, block_tables,
                    max_blocks_per_seq, context_lens, max_context_len, scale, out, workspace,
-                   workspace_bytes, stream);
+                   workspace_bytes, ev_begin, ev_end, stream);
 }
 
 }  // namespace pa
@@ -1153,13 +1282,14 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
                              int32_t num_heads, const int32_t* block_tables,
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t max_context_len, float scale, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* attn_begin, void* attn_end,
+                             void* stream) {
   pa::clear_error();
   if (!q_starts && num_seqs > 0 && total_q > 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_chunk_attention: q_starts is NULL");
   return pa::chunk_run("pa_chunk_attention", cache, q, q_starts, num_seqs, total_q, max_q_len,
                        num_heads, block_tables, max_blocks_per_seq, context_lens, max_context_len,
-                       scale, out, workspace, workspace_bytes, stream);
+                       scale, out, workspace, workspace_bytes, attn_begin, attn_end, stream);
 }
 
 }  // extern "C"

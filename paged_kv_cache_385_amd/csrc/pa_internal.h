@@ -63,6 +63,7 @@ pa_status decode_grouped_run(const char* fn, const pa_cache* cache, const void* 
 pa_status chunk_decode(const char* fn, const pa_cache* cache, const void* q, int32_t num_seqs,
                        int32_t num_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t max_context_len, float scale,
-                       void* out, void* workspace, size_t workspace_bytes, void* stream);
+                       void* out, void* workspace, size_t workspace_bytes, void* ev_begin,
+                       void* ev_end, void* stream);
 
 }  // namespace pa

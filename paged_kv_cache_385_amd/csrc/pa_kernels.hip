@@ -1357,14 +1357,9 @@ pa_status decode_run(const char* fn, const pa_cache* cache, const void* q, int32
     const size_t cb = ws_counter_bytes(num_seqs, num_heads);
     void* ws = workspace && workspace_bytes > cb ? static_cast<char*>(workspace) + cb : nullptr;
     const size_t wsb = ws ? workspace_bytes - cb : 0;
-    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
-      return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
-    st = chunk_decode(fn, cache, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
-                      context_lens, max_context_len, scale, out, ws, wsb, stream);
-    if (st != PA_OK) return st;
-    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
-      return pa::fail(PA_ERR_HIP, "%s: hipEventRecord failed", fn);
-    return PA_OK;
+    return chunk_decode(fn, cache, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
+                        context_lens, max_context_len, scale, out, ws, wsb, ev_begin, ev_end,
+                        stream);
   }
   const int32_t P = su.args.max_parts;
   if (merge && fuse_merge && P > 1 && P <= kMaxFusedParts && fused_merge_enabled())

@@ -329,11 +329,13 @@ def chunk_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_
 
 def chunk_attention(k_cache, v_cache, q, q_starts, block_tables, context_lens, max_q_len: int,
                     max_context_len: int, scale: float, out=None, workspace=None,
-                    stream=None, scales=None) -> torch.Tensor:
+                    stream=None, scales=None, events=None) -> torch.Tensor:
     """pa_chunk_attention: the last q_len_b tokens of each sequence (rows q_starts[b] ..
     q_starts[b+1] of the packed q [total, H, D]) attend causally over its cache.
     Returns out [total, H, D]; allocates the workspace when none is given.  FP8 pools
-    take ``scales`` = (k_scales, v_scales); q and out are then float16 or bfloat16."""
+    take ``scales`` = (k_scales, v_scales); q and out are then float16 or bfloat16.
+    ``events`` (optional): a (begin, end) pair of torch.cuda.Event, already recorded
+    once, attached to the kernels' dispatches (start of attention, end of the call)."""
     dt = _compute_dtype(k_cache, q)
     desc = cache_desc(k_cache, v_cache, scales=scales, dtype=dt)
     dev = k_cache.device
@@ -357,6 +359,9 @@ def chunk_attention(k_cache, v_cache, q, q_starts, block_tables, context_lens, m
     N.check(N.lib().pa_chunk_attention(C.byref(desc), q.data_ptr(), q_starts.data_ptr(), B, T,
                                        max_q_len, H, block_tables.data_ptr(), block_tables.shape[1],
                                        context_lens.data_ptr(), max_context_len, scale,
-                                       out.data_ptr(), ws, wsb, _stream_ptr(stream, dev)),
+                                       out.data_ptr(), ws, wsb,
+                                       events[0].cuda_event if events else None,
+                                       events[1].cuda_event if events else None,
+                                       _stream_ptr(stream, dev)),
             "pa_chunk_attention")
     return out

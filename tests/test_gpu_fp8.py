@@ -166,6 +166,7 @@ def test_fp8_chunk_speculative_verify_shape():
     ([5, 3, 6, 2], 16, 2, 128, "f16"),            # narrow, three tiles, key partitions + merge
     ([12, 10, 9, 11], 8, 2, 64, "bf16"),          # narrow, three tiles at head dim 64
     ([1, 2, 1, 2], 4, 4, 128, "bf16"),            # narrow, one tile (MHA)
+    ([4, 3, 2, 1], 16, 2, 128, "f16"),            # narrow, two tiles
 ])
 def test_fp8_chunks(q_lens, H, Hkv, D, dt):
     from workloads import custom_workload
@@ -173,6 +174,17 @@ def test_fp8_chunks(q_lens, H, Hkv, D, dt):
     wl = custom_workload(ctx, H, Hkv, D, dtype=dt, seed=H + D + q_lens[0])
     say(f"FP8 pools, chunks {q_lens} over {ctx}, H={H} Hkv={Hkv} D={D} {dt}")
     _chunk_fp8(wl, np.minimum(q_lens, ctx), range(len(ctx)), f"fp8 chunks H={H} D={D}")
+
+
+def test_fp8_chunks_over_long_contexts():
+    """Contexts whose waves walk several runs of 64 block ids (up to 9000 tokens), with
+    block counts that leave a wave an odd number of blocks: the narrow kernel on FP8
+    pools takes blocks in pairs, so a run's last pair may hold a padding step."""
+    from workloads import custom_workload
+    ctx = [9000, 4500, 4113, 70]
+    wl = custom_workload(ctx, 16, 2, 128, dtype="bf16", seed=91)
+    say(f"FP8 pools, chunks [6, 3, 5, 2] over {ctx}, H=16 Hkv=2 D=128 bf16")
+    _chunk_fp8(wl, np.minimum([6, 3, 5, 2], ctx), range(len(ctx)), "fp8 chunks, long contexts")
 
 
 def test_fp8_fused_store_contract():

@@ -90,7 +90,7 @@ def test_cache_flags_validation():
     # its missing workspace, before any launch
     c8 = _cache(flags=N.PA_CACHE_FP8, k_scales=FAKE, v_scales=FAKE)
     assert lib.pa_chunk_attention(C.byref(c8), FAKE, FAKE, 2, 12, 6, 4, FAKE, 200, FAKE, 3000, 0.1,
-                                  FAKE, None, 0, None) == N.PA_ERR_WORKSPACE
+                                  FAKE, None, 0, None, None, None) == N.PA_ERR_WORKSPACE
 
 
 @no_device
@@ -150,7 +150,8 @@ def test_chunk_call_validation():
         return lib.pa_chunk_attention(
             C.byref(c), k.get("q", FAKE), k.get("qs", FAKE), k.get("B", 2), k.get("T", 12),
             k.get("mq", 6), k.get("H", 4), FAKE, k.get("mb", 200), FAKE, k.get("mc", 3000),
-            k.get("scale", 0.1), k.get("out", FAKE), k.get("ws", None), k.get("wsb", 0), None)
+            k.get("scale", 0.1), k.get("out", FAKE), k.get("ws", None), k.get("wsb", 0), None,
+            None, None)
 
     need = lib.pa_chunk_workspace_size(2, 4, 2, 128, 12, 6, 3000)
     assert need > 0                                     # few columns: key partitions, merged
@@ -168,7 +169,7 @@ def test_chunk_call_validation():
     assert call(B=-1) == N.PA_ERR_INVALID_ARG
     assert call(B=0) == N.PA_OK and call(T=0) == N.PA_OK     # nothing to do
     assert lib.pa_chunk_attention(None, FAKE, FAKE, 2, 12, 6, 4, FAKE, 200, FAKE, 3000, 0.1, FAKE,
-                                  None, 0, None) == N.PA_ERR_INVALID_ARG
+                                  None, 0, None, None, None) == N.PA_ERR_INVALID_ARG
     # enough column tiles to fill the device: no partitions, no workspace
     assert lib.pa_chunk_workspace_size(64, 64, 8, 128, 64 * 1024, 1024, 4096) == 0
 
