@@ -311,3 +311,35 @@ def test_negative_and_zero_scales(scale_mult):
         ref = OA.chunk_batch(q, starts, lambda b: wl.seq_kv(b, segs), wl.ctx_lens, scale,
                              range(len(ctx)))
         check_close(out, ref, wl.dtype, label=f"scale {scale}, chunks {q_lens}")
+
+
+@pytest.mark.parametrize("max_q_len", [8, 8192])
+def test_events_on_the_dispatches(max_q_len):
+    """pa_chunk_attention's begin/end events are attached to its kernels: they time a
+    positive interval, and the output bits equal those of the call without events, with
+    key partitions and their merge launch (a small max_q_len) and without (a large one)."""
+    from paged_kv_cache_385_amd import chunk_attention
+    q_lens = [4, 1, 7, 2]
+    ctx = [3000, 2047, 1025, 4000]
+    wl = custom_workload(ctx, 8, 1, 128, dtype="bf16", seed=78)
+    cache, segs, tables, ctx_d = _cache_with_context(wl)
+    q = wl.chunk_q(q_lens).cuda()
+    starts = torch.from_numpy(_starts(q_lens)).cuda()
+    outs = []
+    for timed in (False, True):
+        ev = None
+        if timed:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for e in ev:
+                e.record()                      # creates the handles
+        out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=q.device)
+        chunk_attention(cache.k_cache, cache.v_cache, q, starts, tables, ctx_d, max_q_len,
+                        wl.max_context_len, wl.scale, out=out, events=ev)
+        torch.cuda.synchronize()
+        if timed:
+            us = ev[0].elapsed_time(ev[1]) * 1e3
+            say(f"max_q_len {max_q_len}: {us:.1f} us between the events")
+            assert us > 0
+        outs.append(out)
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

@@ -108,3 +108,30 @@ def test_wide_group_edge_semantics():
     assert torch.isnan(d[1]).all()
     assert torch.equal(d[0].view(torch.int16), out[0].view(torch.int16))
     assert torch.equal(d[2].view(torch.int16), out[2].view(torch.int16))
+
+
+def test_wide_group_step_events_time_the_attention():
+    """A decode step on a wide group (the several-token kernels, key partitions and their
+    merge) with attention events: they are attached to those kernels' dispatches, time a
+    positive interval, and leave the output bits as without them."""
+    from paged_kv_cache_385_amd import DecodeBatch
+    wl = custom_workload([1, 17, 600, 3000], 32, 1, 128, dtype="bf16", seed=7)
+    outs = []
+    for timed in (False, True):
+        cache, segs = build_device(wl)
+        batch = DecodeBatch(cache, [op[1] for op in wl.step], wl.num_heads, wl.scale,
+                            -(-int(wl.ctx_lens.max()) // 16))
+        ks, vs = zip(*(segs.tokens(op[2], op[3], 1) for op in wl.step))
+        ev = (torch.cuda.Event(enable_timing=True),
+              torch.cuda.Event(enable_timing=True)) if timed else None
+        out = batch.step(torch.cat(ks).cuda(), torch.cat(vs).cuda(), wl.q().cuda(),
+                         attn_events=ev)
+        torch.cuda.synchronize()
+        if timed:
+            us = ev[0].elapsed_time(ev[1]) * 1e3
+            say(f"wide group step: {us:.1f} us between the attention events")
+            assert us > 0
+        outs.append(out.clone())
+        del cache, batch
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
