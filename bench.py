@@ -67,10 +67,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3 = 70B-shaped GQA-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--staging", choices=("mapped", "upload", "side"), default="side",
+    ap.add_argument("--staging", choices=("mapped", "upload", "side"), default=None,
                     help="how the step's staged tables reach the kernels: read in place from pinned "
                          "host memory, copied on the step's stream, or copied on a side stream "
-                         "(overlapping the previous step)")
+                         "(overlapping the previous step); default: the decode batch's own choice "
+                         "(in place for batches of at most 16 MiB of K/V, else the side stream)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--kv-dtype", choices=("native", "fp8"), default="native",
                     help="KV pools in the workload's 16-bit dtype, or as FP8 (E4M3) codes with "
@@ -1144,7 +1145,7 @@ def main():
                    "head_dim": D, "block_size": bsz, "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype_name,
                    "context": CONTEXT_TEXT[wl.cfg_id],
                    "mean_context": round(float(base_ctx.mean() + W + (K - 1) / 2), 1),
-                   "num_blocks": int(cache.num_blocks)},
+                   "num_blocks": int(cache.num_blocks), "staging": batch.staging},
         "pool_waste": round(cache.bm.stats()["waste"], 4),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(B * K / wall, 1),

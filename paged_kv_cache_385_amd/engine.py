@@ -32,6 +32,10 @@ from . import ops
 from .block_manager import BlockManager
 
 _ALIGN = 256
+# Default staging of a DecodeBatch: batches whose K/V can never exceed this many bytes
+# decode in tens of microseconds, and their kernels reading the staged tables in place
+# ("mapped") beat a copy plus its wait; larger batches copy on a side stream ("side").
+_MAPPED_MAX_KV_BYTES = 16 << 20
 
 
 def _round(n: int) -> int:
@@ -194,8 +198,10 @@ class DecodeBatch:
       for the copy before queueing the kernels (``last_host_waited``), else the
       stream waits for it.
 
-    The default is "side"; ``zero_copy`` is the older switch (True: "mapped",
-    False: "upload"), and an explicit ``staging`` wins over it.  Two pinned buffers (and, for "side", two device
+    The default is "mapped" for a batch whose K/V can never pass 16 MiB (sequences x
+    max_blocks_per_seq blocks; tiny batches are bound by the step's own latency, which
+    a copy and its wait would lengthen) and "side" otherwise; ``zero_copy`` is the older
+    switch (True: "mapped", False: "upload"), and an explicit ``staging`` wins over it.  Two pinned buffers (and, for "side", two device
     buffers) alternate so the host can prepare step i + 1 while step i may
     still read its buffer.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d``
     view the last step's staged values.
@@ -214,7 +220,9 @@ class DecodeBatch:
         if staging is not None:
             mode = staging
         elif zero_copy is None:
-            mode = "side"
+            tile_bytes = 16 * cache.head_dim * (1 if cache.fp8 else cache.k_cache.element_size())
+            kv_max = 2 * B * max_blocks_per_seq * cache.num_kv_heads * tile_bytes
+            mode = "mapped" if kv_max <= _MAPPED_MAX_KV_BYTES else "side"
         else:
             mode = "mapped" if zero_copy else "upload"
         if mode not in ("mapped", "upload", "side"):
