@@ -8,7 +8,8 @@ sequences; one step is the whole hot path, done by one native call
 1. host: the block manager reserves each sequence's next slot (and reports
    copy-on-write pairs), then packs block tables and context lengths into a
    pinned staging buffer;
-2. one host-to-device copy of that buffer;
+2. one host-to-device copy of that buffer (none for a tiny batch, whose kernels
+   read it in place);
 3. ``pa_copy_blocks`` for the pairs (before any write can land in a block
    that is still shared);
 4. ``pa_cache_write`` of the new tokens' K and V;
@@ -201,9 +202,9 @@ class DecodeBatch:
     The default is "mapped" for a batch whose K/V can never pass 16 MiB (sequences x
     max_blocks_per_seq blocks; tiny batches are bound by the step's own latency, which
     a copy and its wait would lengthen) and "side" otherwise; ``zero_copy`` is the older
-    switch (True: "mapped", False: "upload"), and an explicit ``staging`` wins over it.  Two pinned buffers (and, for "side", two device
-    buffers) alternate so the host can prepare step i + 1 while step i may
-    still read its buffer.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d``
+    switch (True: "mapped", False: "upload"), and an explicit ``staging`` wins over it.
+    Two pinned buffers (and, for "side", two device buffers) alternate so the host can
+    prepare step i + 1 while step i may still read its buffer.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d``
     view the last step's staged values.
     """
 
