@@ -320,7 +320,8 @@ def _time_launches(fn, reps: int, stream) -> float:
 def read_ceiling(cache, sids, max_blocks, wl, dev, achieved_gbs, reps: int = 10):
     """Measured read ceilings (pa_probe_read_*): a contiguous 2 GiB read, and a gather of
     exactly the (block, KV head) tiles the decode pass reads, K and V, in a shuffled order
-    (the decode pass reads them in its own order).  Each at 2, 4 and 8 workgroups per
+    (the decode pass reads them in its own order), at the pool's tile size (4 KiB for a
+    16-bit pool at head dim 128, 2 KiB for an FP8 one).  Each at 2, 4 and 8 workgroups per
     compute unit; the best is reported."""
     import ctypes as C
     import torch
@@ -344,21 +345,24 @@ def read_ceiling(cache, sids, max_blocks, wl, dev, achieved_gbs, reps: int = 10)
     tiles = np.random.default_rng(385).permutation(tiles).astype(np.int32)
     tiles_d = torch.from_numpy(tiles).to(dev)
     pool_bytes = cache.k_cache.numel() * cache.k_cache.element_size()
-    tile_bytes = 2 * len(tiles) * 4096
+    one_tile = 16 * wl.head_dim * (1 if cache.fp8 else cache.k_cache.element_size())
+    tile_bytes = 2 * len(tiles) * one_tile
     gather = {}
     for wg in (2, 4, 8):
         us = _time_launches(lambda: _native.check(lib.pa_probe_read_tiles(
-            cache.k_cache.data_ptr(), cache.v_cache.data_ptr(), pool_bytes, tiles_d.data_ptr(),
-            tiles.ctypes.data, len(tiles), wg, sink.data_ptr(), sp), "pa_probe_read_tiles"),
-            reps, stream)
+            cache.k_cache.data_ptr(), cache.v_cache.data_ptr(), pool_bytes, one_tile,
+            tiles_d.data_ptr(), tiles.ctypes.data, len(tiles), wg, sink.data_ptr(), sp),
+            "pa_probe_read_tiles"), reps, stream)
         gather[wg] = tile_bytes / (us * 1e-6) / 1e9
     bc, bg = max(contiguous, key=contiguous.get), max(gather, key=gather.get)
-    log(f"read ceiling: contiguous {contiguous[bc]:.0f} GB/s ({bc} workgroups/CU), tile gather "
-        f"{gather[bg]:.0f} GB/s ({bg} workgroups/CU) over {tile_bytes / 1e6:.1f} MB")
+    log(f"read ceiling: contiguous {contiguous[bc]:.0f} GB/s ({bc} workgroups/CU), gather of "
+        f"{one_tile}-byte tiles {gather[bg]:.0f} GB/s ({bg} workgroups/CU) over "
+        f"{tile_bytes / 1e6:.1f} MB")
     return {"unit": "GB/s", "contiguous": round(contiguous[bc], 1),
             "tile_gather": round(gather[bg], 1),
             "frac_of_tile_gather": round(achieved_gbs / gather[bg], 4),
             "contiguous_bytes": 2 << 30, "tile_gather_bytes": tile_bytes,
+            "tile_bytes": one_tile,
             "workgroups_per_cu": {"contiguous": bc, "tile_gather": bg},
             "kernels": "probe_contiguous_kernel, probe_tiles_kernel (pa_probe.h)"}
 
@@ -1125,7 +1129,9 @@ def main():
                            "flush": f"{FLUSH_BYTES >> 20} MiB written before each launch"}
         log(f"flushed: {F} steps, attention pass {f_avg * 1e3:.1f} us avg (median {fm:.1f}, "
             f"p10 {f10:.1f}, p90 {f90:.1f}), frac {roof['flushed_frac']}")
-    if not fp8 and D == 128 and bsz == 16 and not args.no_ceiling:
+    # the ceilings of the pass's own tiles (16-bit or FP8), where they are enough bytes to
+    # time (not the tiny batch)
+    if bsz == 16 and not args.no_ceiling and roof_bytes >= (64 << 20):
         roof["ceiling"] = read_ceiling(cache, sids, max_blocks, wl, dev, achieved)
 
     result = {

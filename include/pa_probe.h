@@ -26,10 +26,6 @@
 extern "C" {
 #endif
 
-/* Bytes of one tile the tile probe reads: one (block, KV head) tile of a 16-bit
- * pool at head_dim 128 (16 tokens x 128 dims x 2 bytes). */
-#define PA_PROBE_TILE_BYTES 4096
-
 /* Read bytes [0, bytes) of `buf` (device, 16-byte aligned, bytes a non-zero
  * multiple of 16), front to back.  workgroups_per_cu (1 .. 64) workgroups of
  * 256 threads per compute unit stride over the buffer, four loads in flight per
@@ -38,16 +34,21 @@ pa_status pa_probe_read_contiguous(const void* buf, size_t bytes, int32_t workgr
                                    uint32_t* sink, void* stream);
 
 /* Read tiles tiles[0 .. num_tiles) of a K pool and of a V pool (device, 16-byte
- * aligned, pool_bytes each): tile i is bytes [i, i + 1) x PA_PROBE_TILE_BYTES of
- * both pools, so a list of (block * num_kv_heads + head) ids reads the tiles a
- * decode pass over those (block, head) pairs reads, in the list's order.
- * `tiles` is the device copy of the list, `tiles_host` the same list on the host,
- * where every id is checked against pool_bytes.  One workgroup (256 threads)
- * reads one tile of each pool per load instruction, two tiles in flight;
+ * aligned, pool_bytes each): tile i is bytes [i, i + 1) x tile_bytes of both pools,
+ * so a list of (block * num_kv_heads + head) ids reads the tiles a decode pass over
+ * those (block, head) pairs reads, in the list's order.  tile_bytes is one (block,
+ * KV head) tile of the pool, 16 tokens x head_dim x element bytes: 4096 for a
+ * 16-bit pool at head_dim 128, 2048 for an FP8 pool (or a 16-bit one at head_dim
+ * 64), 1024 for an FP8 pool at head_dim 64; other sizes are rejected.  `tiles` is
+ * the device copy of the list, `tiles_host` the same list on the host, where every
+ * id is checked against pool_bytes / tile_bytes.  Each tile is read by tile_bytes /
+ * 16 lanes with one 16-byte load each, so a workgroup (256 threads) covers 4096 /
+ * tile_bytes tiles of each pool per load instruction, two such steps in flight;
  * workgroups_per_cu (1 .. 64) workgroups per compute unit. */
 pa_status pa_probe_read_tiles(const void* k_base, const void* v_base, size_t pool_bytes,
-                              const int32_t* tiles, const int32_t* tiles_host, int32_t num_tiles,
-                              int32_t workgroups_per_cu, uint32_t* sink, void* stream);
+                              int32_t tile_bytes, const int32_t* tiles, const int32_t* tiles_host,
+                              int32_t num_tiles, int32_t workgroups_per_cu, uint32_t* sink,
+                              void* stream);
 
 #ifdef __cplusplus
 }

@@ -140,7 +140,7 @@ SIGNATURES = {
                                  C.POINTER(PaStepInfo), _P, _P, _P]),
     # measurement probes (pa_probe.h)
     "pa_probe_read_contiguous": (C.c_int, [_P, C.c_size_t, _I32, _P, _P]),
-    "pa_probe_read_tiles": (C.c_int, [_P, _P, C.c_size_t, _P, _P, _I32, _I32, _P, _P]),
+    "pa_probe_read_tiles": (C.c_int, [_P, _P, C.c_size_t, _I32, _P, _P, _I32, _I32, _P, _P]),
     "pa_timeline_clear": (C.c_int, [_P]),
     "pa_timeline_read": (C.c_int, [_P, _I32]),
 }

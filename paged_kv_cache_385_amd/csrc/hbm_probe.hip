@@ -46,20 +46,23 @@ __global__ __launch_bounds__(kThreads) void probe_contiguous_kernel(const u32x4*
   if (acc == kNever) sink[0] = acc;
 }
 
-// One workgroup reads a whole 4 KiB tile per load instruction (256 lanes x 16 bytes):
-// tiles t, t + grid, ... of the list, K and V, two tiles in flight.
+// Each tile is read by 2^lanes_log2 lanes of 16 bytes (64 lanes for 1 KiB, 256 for 4 KiB);
+// a workgroup reads 256 >> lanes_log2 tiles of each pool per load instruction, tiles
+// t, t + step, ... of the list (step = that count x the grid), two tiles in flight.
 __global__ __launch_bounds__(kThreads) void probe_tiles_kernel(const char* __restrict__ k_base,
                                                                const char* __restrict__ v_base,
                                                                const int32_t* __restrict__ tiles,
-                                                               int32_t num_tiles,
+                                                               int32_t num_tiles, int32_t lanes_log2,
                                                                uint32_t* __restrict__ sink) {
-  constexpr int64_t kTile = 16 * kThreads;
-  const int64_t lane_off = static_cast<int64_t>(threadIdx.x) * 16;
+  const int64_t tile_bytes = int64_t{16} << lanes_log2;
+  const int32_t per_wg = kThreads >> lanes_log2;
+  const int64_t lane_off = static_cast<int64_t>(threadIdx.x & ((1 << lanes_log2) - 1)) * 16;
+  const int32_t step = static_cast<int32_t>(gridDim.x) * per_wg;
   uint32_t acc = 0;
-  int32_t t = blockIdx.x;
-  for (; t + static_cast<int32_t>(gridDim.x) < num_tiles; t += 2 * gridDim.x) {
-    const int64_t a = static_cast<int64_t>(tiles[t]) * kTile + lane_off;
-    const int64_t b = static_cast<int64_t>(tiles[t + gridDim.x]) * kTile + lane_off;
+  int32_t t = blockIdx.x * per_wg + (threadIdx.x >> lanes_log2);
+  for (; t + step < num_tiles; t += 2 * step) {
+    const int64_t a = static_cast<int64_t>(tiles[t]) * tile_bytes + lane_off;
+    const int64_t b = static_cast<int64_t>(tiles[t + step]) * tile_bytes + lane_off;
     const u32x4 ka = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_base + a));
     const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_base + a));
     const u32x4 kb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_base + b));
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void probe_tiles_kernel(const char* __res
     acc ^= fold(ka) ^ fold(va) ^ fold(kb) ^ fold(vb);
   }
   if (t < num_tiles) {
-    const int64_t a = static_cast<int64_t>(tiles[t]) * kTile + lane_off;
+    const int64_t a = static_cast<int64_t>(tiles[t]) * tile_bytes + lane_off;
     acc ^= fold(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_base + a)));
     acc ^= fold(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_base + a)));
   }
@@ -94,16 +97,20 @@ pa_status pa_probe_read_contiguous(const void* buf, size_t bytes, int32_t workgr
 }
 
 pa_status pa_probe_read_tiles(const void* k_base, const void* v_base, size_t pool_bytes,
-                              const int32_t* tiles, const int32_t* tiles_host, int32_t num_tiles,
-                              int32_t workgroups_per_cu, uint32_t* sink, void* stream) {
+                              int32_t tile_bytes, const int32_t* tiles, const int32_t* tiles_host,
+                              int32_t num_tiles, int32_t workgroups_per_cu, uint32_t* sink,
+                              void* stream) {
   const char* fn = "pa_probe_read_tiles";
   pa::clear_error();
   if (!k_base || !v_base || !tiles || !tiles_host || !sink || num_tiles < 1 ||
       (reinterpret_cast<uintptr_t>(k_base) & 15u) || (reinterpret_cast<uintptr_t>(v_base) & 15u))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL or misaligned argument, or no tiles", fn);
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: tile_bytes %d (1024, 2048 or 4096)", fn, tile_bytes);
   if (workgroups_per_cu < 1 || workgroups_per_cu > 64)
     return pa::fail(PA_ERR_INVALID_ARG, "%s: workgroups_per_cu %d (1 .. 64)", fn, workgroups_per_cu);
-  const int64_t n_pool = static_cast<int64_t>(pool_bytes / PA_PROBE_TILE_BYTES);
+  const int32_t lanes_log2 = tile_bytes == 1024 ? 6 : tile_bytes == 2048 ? 7 : 8;
+  const int64_t n_pool = static_cast<int64_t>(pool_bytes / static_cast<size_t>(tile_bytes));
   for (int32_t i = 0; i < num_tiles; ++i)
     if (tiles_host[i] < 0 || tiles_host[i] >= n_pool)
       return pa::fail(PA_ERR_INVALID_ARG, "%s: tile %d = %d outside the pools' %lld tiles", fn, i,
@@ -111,7 +118,8 @@ pa_status pa_probe_read_tiles(const void* k_base, const void* v_base, size_t poo
   const int64_t grid = static_cast<int64_t>(pa::device_cus()) * workgroups_per_cu;
   probe_tiles_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream)>>>(
-      static_cast<const char*>(k_base), static_cast<const char*>(v_base), tiles, num_tiles, sink);
+      static_cast<const char*>(k_base), static_cast<const char*>(v_base), tiles, num_tiles,
+      lanes_log2, sink);
   return pa::launch_status(fn);
 }
 

@@ -451,3 +451,29 @@ def test_decode_step_rejects_before_the_block_manager_changes():
     assert call(cs=FAKE) == N.PA_ERR_INVALID_ARG                     # copy stream without event
     assert call(cs=FAKE, ce=FAKE, sd=None) == N.PA_ERR_INVALID_ARG   # copy stream, no device staging
     assert bm.seq_len(0) == 3 and bm.block_table(0) == [0]
+
+
+@no_device
+def test_probe_calls_check_their_arguments():
+    """The read probes reject bad arguments on the host, before any launch: a tile size
+    other than 1, 2 or 4 KiB, a tile id past the pools at the given tile size, a
+    workgroup count outside 1 .. 64, a misaligned or empty contiguous read."""
+    lib = N.lib()
+    ids = np.array([0, 5, 9], dtype=np.int32)
+    pool = 10 * 2048                                  # ten 2 KiB tiles, five 4 KiB ones
+
+    def tiles(tb, t=ids, wg=2):
+        return lib.pa_probe_read_tiles(FAKE, FAKE, pool, tb, FAKE, t.ctypes.data, len(t), wg,
+                                       FAKE, None)
+
+    for tb in (0, 512, 3000, 8192):
+        assert tiles(tb) == N.PA_ERR_INVALID_ARG
+        assert b"tile_bytes" in lib.pa_last_error()
+    assert tiles(4096) == N.PA_ERR_INVALID_ARG         # id 9 is past five 4 KiB tiles
+    assert b"outside" in lib.pa_last_error()
+    assert tiles(2048, wg=0) == N.PA_ERR_INVALID_ARG
+    assert tiles(2048, wg=65) == N.PA_ERR_INVALID_ARG
+    assert tiles(1024, t=np.array([-1], dtype=np.int32)) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_read_contiguous(FAKE + 8, 4096, 2, FAKE, None) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_read_contiguous(FAKE, 0, 2, FAKE, None) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_read_contiguous(FAKE, 4100, 2, FAKE, None) == N.PA_ERR_INVALID_ARG
