@@ -167,6 +167,8 @@ def test_fp8_chunk_speculative_verify_shape():
     ([12, 10, 9, 11], 8, 2, 64, "bf16"),          # narrow, three tiles at head dim 64
     ([1, 2, 1, 2], 4, 4, 128, "bf16"),            # narrow, one tile (MHA)
     ([4, 3, 2, 1], 16, 2, 128, "f16"),            # narrow, two tiles
+    ([8, 5, 3, 1], 8, 2, 64, "bf16"),             # narrow, two tiles at head dim 64 (pairs)
+    ([2, 1, 3, 4], 4, 4, 64, "f16"),              # narrow, one tile at head dim 64 (pairs)
 ])
 def test_fp8_chunks(q_lens, H, Hkv, D, dt):
     from workloads import custom_workload
