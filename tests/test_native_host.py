@@ -454,7 +454,7 @@ def test_decode_step_rejects_before_the_block_manager_changes():
 
 
 @no_device
-def test_probe_calls_check_their_arguments():
+def test_probe_call_validation():
     """The read probes reject bad arguments on the host, before any launch: a tile size
     other than 1, 2 or 4 KiB, a tile id past the pools at the given tile size, a
     workgroup count outside 1 .. 64, a misaligned or empty contiguous read."""
