@@ -459,9 +459,10 @@ __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_
   return false;     // not reached
 }
 
-// Three waves per SIMD: 162-163 registers at head dim 128 on 16-bit pools, 130-132 on
-// FP8 pools (no spills), and 3 x 34 KB of LDS per CU.  Held to 128 registers (four
-// waves), the FP8 form spills and its steps took 84 against 81 us.
+// Registers for three waves per SIMD: 162-163 at head dim 128 on 16-bit pools, 130-132 on
+// FP8 pools (no spills), and 34 KB of LDS per workgroup.  Held to 128 registers (four
+// waves), the FP8 form spills and its steps took 84 against 81 us.  On 16-bit pools at
+// head dim 128 the launch pads LDS so that two workgroups share a CU (launch_attn_t).
 template <class E, int D, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_attn_kernel(DecodeArgs a) {
@@ -1227,6 +1228,14 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
 // The attention launch.  Events given (hipEvent_t, may be NULL) are attached to the
 // dispatch itself: they take the kernel's own start and end times, without the queue
 // time around it that events recorded before and after the launch would include.
+// On 16-bit pools at head dim 128 the launch reserves kOccupancyPadLds bytes of LDS it
+// never uses, so that two workgroups share a compute unit instead of three.  A CU serves
+// its workgroups' loads about oldest first, so the third mostly waits for its first tile
+// while holding a slot; with two, the 70B-shaped layer's pass is ~1.3 % shorter and its
+// step ~2 % (three alternating runs), the others even.  FP8 pools, whose waves stream half
+// the bytes per tile, keep three (two were 7 % slower).
+constexpr uint32_t kOccupancyPadLds = 24 * 1024;
+
 template <class E, bool kStream, bool kFp8>
 void launch_attn_t(const DecodeSetup& su, int d, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (d == 64)
@@ -1234,7 +1243,7 @@ void launch_attn_t(const DecodeSetup& su, int d, hipStream_t s, hipEvent_t e0, h
                           0, s, e0, e1, 0, su.args);
   else
     hipExtLaunchKernelGGL(decode_attn_kernel<E, 128, kStream, kFp8>, dim3(su.grid), dim3(kThreads),
-                          0, s, e0, e1, 0, su.args);
+                          kFp8 ? 0u : kOccupancyPadLds, s, e0, e1, 0, su.args);
 }
 
 template <class E>
