@@ -1080,7 +1080,9 @@ int32_t parts_for(int32_t max_ctx, int32_t part_tokens) {
 
 // Partition length of one launch: the longest of 4096, 2048 and 1024 tokens for
 // which even the longest possible item list gives every workgroup slot of the
-// device (three per compute unit) two items, else 512 tokens.  A longer item
+// device (counted as three per compute unit, as the registers allow; 16-bit pools at
+// head dim 128 run two, for which the count asks a little more) two items, else 512
+// tokens.  A longer item
 // spends less of its time on start-up and combine per byte it reads; two items
 // per slot keep enough of them for the largest-first order to balance the slots.
 int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
