@@ -13,7 +13,8 @@ one token per step, as in real decoding.
 
 Prints one JSON line.  ``value`` is K/V bytes the steps had to read divided
 by the wall time of the timed steps (GB/s); ``roofline`` rates the attention
-kernel alone, timed with HIP events on its stream on every fifth timed step; ``cpu_baseline``
+kernel alone, timed with HIP events on its stream on about five of the timed steps
+(at most every fifth); ``cpu_baseline``
 is the CPU oracle on a bounded sample of the same workload.  Other legs:
 ``--kv-dtype fp8``, ``--block-size 32``, ``--chunk verify|prefill``, ``--prefix``, ``--swap``.
 """
@@ -33,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-EVENT_EVERY = 5                # timed steps whose attention pass carries a timing event pair
+EVENT_SAMPLES = 5              # timed steps whose attention pass carries a timing event pair
+EVENT_MIN_EVERY = 5            # ... at most one in this many
 TIMELINE_STEPS = 5             # steps captured with per-workgroup stamps (--timeline)
 TIMELINE_HZ = 100e6            # the kernel's stamps count a constant 100 MHz clock
 FLUSH_BYTES = 1 << 30          # written before a flushed step: > 8 x 4 MB L2 + 256 MB Infinity Cache
@@ -1043,11 +1045,12 @@ def main():
         batch.step(*steps_kv[i], q)
     torch.cuda.synchronize()
 
-    # The attention pass is timed with events on every EVENT_EVERY-th step: a timed event
-    # pair is two extra packets in the queue and costs about 9 us per step, which would
-    # otherwise be charged to the step.  Timing events are created (first record) before
-    # the timed region.
-    sampled = [j for j in range(K) if j % EVENT_EVERY == 0]
+    # The attention pass is timed with events on about EVENT_SAMPLES steps spread over the
+    # timed ones (every `every`-th): events attached to a dispatch delay the next kernel by
+    # about 9 us, which is charged to the step.  Timing events are created (first record)
+    # before the timed region.
+    every = max(EVENT_MIN_EVERY, K // EVENT_SAMPLES)
+    sampled = [j for j in range(K) if j % every == 0]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sampled]
     fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(F)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1058,7 +1061,7 @@ def main():
     start.record(batch.stream)
     for j in range(K):
         batch.step(*steps_kv[W + j], q,
-                   attn_events=ev[j // EVENT_EVERY] if j % EVENT_EVERY == 0 else None)
+                   attn_events=ev[j // every] if j % every == 0 else None)
     stop.record(batch.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -1103,7 +1106,7 @@ def main():
         return float(np.mean([launch_bytes(warmup + j) for j in range(0, steps, every)]))
 
     attn_bytes = float(np.mean([step_bytes(W + j) for j in sampled]))
-    roof_bytes = mean_bytes(K, W, EVENT_EVERY)
+    roof_bytes = mean_bytes(K, W, every)
     achieved = roof_bytes / (attn_avg_ms * 1e-3) / 1e9
     med, p10, p90 = (float(x) * 1e3 for x in np.percentile(attn_ms, [50, 10, 90]))
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms, attention pass "

@@ -644,13 +644,12 @@ pa_status pa_chunk_attention(const pa_cache* cache, const void* q, const int32_t
  *   2. enqueues one copy of that region to staging_dev (device memory) -- on
  *      `stream`, or, when copy_stream is given, on copy_stream, so the copy can
  *      run while earlier work of `stream` still runs, and records copy_event (a
- *      hipEvent_t) there.  If `stream` still has work in flight, the call then
- *      waits on the host for copy_event before it enqueues the kernels (a wait
- *      placed in `stream` would cost queue time between the kernels); if
- *      `stream` is idle, it makes `stream` wait for copy_event instead.  The
- *      host wait lasts as long as the copy and whatever copy_stream ran
- *      before it.  PA_STEP_STREAM_WAIT=1 in the environment always takes the
- *      stream wait -- or, when
+ *      hipEvent_t) there.  The call then waits on the host for copy_event before
+ *      it enqueues the kernels (a wait placed in `stream`, like a query of
+ *      whether `stream` is busy, would cost queue time between the kernels).
+ *      The host wait lasts as long as the copy and whatever copy_stream ran
+ *      before it.  PA_STEP_STREAM_WAIT=1 in the environment makes `stream` wait
+ *      for copy_event instead -- or, when
  *      staging_dev is NULL, nothing: the kernels read staging_host in place (it
  *      must then be pinned host memory mapped for the device, as hipHostMalloc
  *      returns);

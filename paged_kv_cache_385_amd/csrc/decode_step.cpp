@@ -59,8 +59,8 @@ bool grouped_enabled() {
   return on;
 }
 
-// PA_STEP_STREAM_WAIT=1 in the environment: a step with a copy stream always makes its
-// stream wait for the copy, never the host.
+// PA_STEP_STREAM_WAIT=1 in the environment: a step with a copy stream makes its stream
+// wait for the copy instead of the host.
 bool stream_wait_forced() {
   static const bool on = [] {
     const char* e = std::getenv("PA_STEP_STREAM_WAIT");
@@ -156,12 +156,13 @@ pa_status pa_decode_step(pa_bm* bm, const pa_cache* cache, int32_t num_seqs, con
       return pa::fail(PA_ERR_HIP, "pa_decode_step: hipMemcpyAsync failed");
     if (copy_stream) {
       hipEvent_t ev = static_cast<hipEvent_t>(copy_event);
-      // While `stream` still runs earlier work, the host waits for the copy, which lands
-      // long before that work ends, and the kernels are queued with no cross-stream
-      // wait: such a wait is a barrier packet that costs the step several microseconds
-      // of queue time even when it is already satisfied.  On an idle stream the wait
-      // goes into the stream, so the host does not block.
-      const bool host_wait = !stream_wait_forced() && hipStreamQuery(s) == hipErrorNotReady;
+      // The host waits for the copy, and the kernels are queued with nothing before
+      // them on `stream`.  A cross-stream wait is a barrier packet, and asking whether
+      // `stream` is still busy (hipStreamQuery) puts a marker behind its last kernel;
+      // either one delays the next kernel by about 5 us on gfx950 even when nothing
+      // is left to wait for.  In a loop of steps the copy ends long before the
+      // previous step's kernels do, so the host's wait costs the device nothing.
+      const bool host_wait = !stream_wait_forced();
       if (hipEventRecord(ev, cs) != hipSuccess ||
           (host_wait ? hipEventSynchronize(ev) : hipStreamWaitEvent(s, ev, 0)) != hipSuccess)
         return pa::fail(PA_ERR_HIP, "pa_decode_step: copy-stream event failed");

@@ -37,10 +37,57 @@ _ALIGN = 256
 # decode in tens of microseconds, and their kernels reading the staged tables in place
 # ("mapped") beat a copy plus its wait; larger batches copy on a side stream ("side").
 _MAPPED_MAX_KV_BYTES = 16 << 20
+# Staging slots of a DecodeBatch: up to this many, holding together at most this many
+# pinned bytes.  An event recorded on a stream between two kernels delays the second
+# by about 5.5 us on gfx950, so the step marks its completion only once per half ring.
+_RING_MAX = 16
+_RING_BYTES = 32 << 20
 
 
 def _round(n: int) -> int:
     return (n + _ALIGN - 1) // _ALIGN * _ALIGN
+
+
+def _ring_slots(staging_bytes: int) -> int:
+    """Staging slots for one step's ``staging_bytes``: even, 2 .. _RING_MAX."""
+    return max(2, min(_RING_MAX, _RING_BYTES // max(1, staging_bytes)) & ~1)
+
+
+class _CompletionMarks:
+    """Which kernels of a step ring have finished, from one event per ``every`` steps.
+
+    Step i records a mark after its kernels when i % every == every - 1 (``after``).
+    ``wait(j)`` returns once the kernels of step j (and of every step before it on the
+    stream) have finished: it waits for the first mark at or after step j, which a
+    ring of 2 * every slots always holds before the slot of step j is reused, and
+    recycles the older marks' events.  ``new_event`` makes an event and ``sync`` waits
+    for one (host side); both are plain callables so the bookkeeping runs without a
+    device.
+    """
+
+    def __init__(self, every: int, new_event: Callable, record: Callable, sync: Callable):
+        self.every = every
+        self._new, self._record, self._sync = new_event, record, sync
+        self._marks = []          # (step, event), oldest first
+        self._spare = []
+
+    def after(self, i: int) -> None:
+        if i % self.every == self.every - 1:
+            ev = self._spare.pop() if self._spare else self._new()
+            self._record(ev)
+            self._marks.append((i, ev))
+
+    def wait(self, j: int) -> None:
+        if j < 0:
+            return
+        k = 0
+        while k < len(self._marks) and self._marks[k][0] < j:
+            k += 1
+        if k == len(self._marks):
+            raise RuntimeError(f"no completion mark at or after step {j}")
+        self._spare.extend(ev for _, ev in self._marks[:k])
+        del self._marks[:k]
+        self._sync(self._marks[0][1])
 
 
 class PagedKVCache:
@@ -195,17 +242,21 @@ class DecodeBatch:
     * ``"mapped"``: they read the pinned buffer in place (no copy);
     * ``"upload"``: one copy to a device buffer on the step's stream;
     * ``"side"``: the copy runs on a side stream, so the copy of step i + 1
-      overlaps the kernels of step i; while the stream is busy the host waits
-      for the copy before queueing the kernels (``last_host_waited``), else the
-      stream waits for it.
+      overlaps the kernels of step i; the host waits for the copy before
+      queueing the kernels (``last_host_waited``), so nothing stands between
+      two steps' kernels on the stream.
 
     The default is "mapped" for a batch whose K/V can never pass 16 MiB (sequences x
     max_blocks_per_seq blocks; tiny batches are bound by the step's own latency, which
     a copy and its wait would lengthen) and "side" otherwise; ``zero_copy`` is the older
     switch (True: "mapped", False: "upload"), and an explicit ``staging`` wins over it.
-    Two pinned buffers (and, for "side", two device buffers) alternate so the host can
-    prepare step i + 1 while step i may still read its buffer.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d``
-    view the last step's staged values.
+    A ring of R pinned buffers (and, for "side", R device buffers; R even, up to 16 while
+    they take at most 32 MiB of pinned memory) lets the host prepare later steps while
+    earlier ones still read theirs.  Every R / 2 steps the step records one completion
+    event on its stream; before a slot is reused the host waits for the first such
+    event at or after the slot's last step, so no event sits between most pairs of
+    kernels.  ``slots_d``, ``ctx_d``, ``tables_d`` and ``pairs_d`` view the last step's
+    staged values.
     """
 
     def __init__(self, cache: PagedKVCache, sids: Sequence[int], num_heads: int, scale: float,
@@ -234,12 +285,15 @@ class DecodeBatch:
         lib = N.lib()
         self._lib = lib
         self._bytes = int(lib.pa_decode_step_staging_bytes(B, max_blocks_per_seq))
+        ring = _ring_slots(self._bytes)
+        self._ring = ring
         # 256-byte aligned regions carved from slightly larger allocations
         self._pinned_raw = [torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, pin_memory=True)
-                            for _ in range(2)]
+                            for _ in range(ring)]
         self._pinned = [self._aligned(t) for t in self._pinned_raw]
-        self._staged = [torch.cuda.Event() for _ in range(2)]
-        n_dev = 2 if mode == "side" else 1
+        self._marks = _CompletionMarks(ring // 2, torch.cuda.Event, lambda e: e.record(self.stream),
+                                       lambda e: e.synchronize())
+        n_dev = ring if mode == "side" else 1
         self._dev_raw = [torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, device=dev)
                          for _ in range(n_dev)]
         self._dev = [self._aligned(t) for t in self._dev_raw]
@@ -247,7 +301,7 @@ class DecodeBatch:
         self._copied = []
         if mode == "side":
             self._copy_stream = torch.cuda.Stream(dev)       # default priority
-            self._copied = [torch.cuda.Event() for _ in range(2)]
+            self._copied = [torch.cuda.Event() for _ in range(ring)]
             for e in self._copied:
                 e.record(self._copy_stream)                  # creates the handles
         off_ctx = _round(8 * B)
@@ -323,18 +377,18 @@ class DecodeBatch:
             for e in attn_events:
                 if not e.cuda_event:
                     e.record(self.stream)        # creates the handle
-        buf = self._i & 1
+        i = self._i
+        buf = i % self._ring
         self._i += 1
-        self._staged[buf].synchronize()          # the step that last used this buffer is done
+        # The slot's last reader (the kernels, or in "side" mode the copy, of step
+        # i - ring) has finished: the slot's pinned and device buffers may be rewritten.
+        self._marks.wait(i - self._ring)
         pin = self._pinned[buf]
         ev = (None, None) if attn_events is None else (attn_events[0].cuda_event,
                                                        attn_events[1].cuda_event)
         ws = self.workspace
         side = self._copy_stream is not None
         di = buf if side else 0
-        if side:
-            # the device buffer's last reader (two steps back) has finished
-            self._copy_stream.wait_event(self._staged[buf])
         N.check(self._lib.pa_decode_step(
             self.cache.bm._h, C.byref(self._desc), self.B, self._sids_ptr, k_new.data_ptr(),
             v_new.data_ptr(), q.data_ptr(), self.H, self.scale, self.out.data_ptr(),
@@ -344,7 +398,7 @@ class DecodeBatch:
             self._copy_stream.cuda_stream if side else None,
             self._copied[buf].cuda_event if side else None, self.stream.cuda_stream),
             "pa_decode_step")
-        self._staged[buf].record(self.stream)
+        self._marks.after(i)
         self._last_buf = buf
         self._last_dev = di
         self._dev_current = not self.zero_copy

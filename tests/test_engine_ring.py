@@ -1,0 +1,81 @@
+"""Host bookkeeping of DecodeBatch's staging ring (no device).
+
+The ring rule: step i uses slot i % R and, before writing it, waits until the
+kernels of step i - R (the slot's last reader) have finished; one completion mark
+is recorded every R / 2 steps.  A fake stream stands in for the device: an event
+records the last step enqueued before it, and a host wait on it completes every
+step up to that one.
+"""
+
+import pytest
+
+from paged_kv_cache_385_amd.engine import _RING_BYTES, _RING_MAX, _CompletionMarks, _ring_slots
+
+
+class _FakeStream:
+    def __init__(self):
+        self.enqueued = -1        # last step whose kernels are on the stream
+        self.finished = -1        # last step known finished on the host
+        self.records = 0
+
+    def new_event(self):
+        return {"step": None}
+
+    def record(self, ev):
+        ev["step"] = self.enqueued
+        self.records += 1
+
+    def sync(self, ev):
+        assert ev["step"] is not None, "wait on an event that was never recorded"
+        self.finished = max(self.finished, ev["step"])
+
+
+@pytest.mark.parametrize("ring", [2, 4, 8, 16])
+def test_every_reused_slot_waits_for_its_last_reader(ring):
+    st = _FakeStream()
+    marks = _CompletionMarks(ring // 2, st.new_event, st.record, st.sync)
+    steps = 10 * ring + 3
+    for i in range(steps):
+        marks.wait(i - ring)
+        if i >= ring:
+            # the slot's previous step (i - ring) is finished, and the wait asked for
+            # no step still to come or just enqueued
+            assert st.finished >= i - ring
+            assert st.finished <= i - ring // 2 - 1
+        st.enqueued = i
+        marks.after(i)
+    assert st.records == steps // (ring // 2)
+    # events are recycled: never more alive than the marks a ring needs
+    assert len(marks._marks) + len(marks._spare) <= 4
+
+
+def test_first_ring_of_steps_waits_for_nothing():
+    st = _FakeStream()
+    marks = _CompletionMarks(4, st.new_event, st.record, st.sync)
+    for i in range(8):
+        marks.wait(i - 8)
+        st.enqueued = i
+        marks.after(i)
+    assert st.finished == -1
+
+
+def test_a_wait_with_no_mark_in_range_is_an_error():
+    st = _FakeStream()
+    marks = _CompletionMarks(4, st.new_event, st.record, st.sync)
+    for i in range(3):              # no step reached i % 4 == 3
+        st.enqueued = i
+        marks.after(i)
+    with pytest.raises(RuntimeError):
+        marks.wait(0)
+
+
+def test_ring_slots():
+    assert _ring_slots(1) == _RING_MAX
+    assert _ring_slots(_RING_BYTES // 5) == 4
+    assert _ring_slots(_RING_BYTES // 3) == 2
+    assert _ring_slots(_RING_BYTES) == 2
+    assert _ring_slots(4 * _RING_BYTES) == 2
+    for b in (1000, 141_000, 3 << 20, 9 << 20, 40 << 20):
+        r = _ring_slots(b)
+        assert r % 2 == 0 and 2 <= r <= _RING_MAX
+        assert r == 2 or r * b <= _RING_BYTES

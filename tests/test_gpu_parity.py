@@ -321,9 +321,10 @@ def test_staging_modes_give_the_same_bits(cfg):
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_side_staging_with_a_busy_stream(cfg):
     """Steps queued back to back, inputs already on the device, so each call finds
-    the stream still running the previous step: the host waits for the side copy
-    and the kernels go in with no stream wait.  Outputs, pools and staged tables
-    equal those of steps that read the tables in place."""
+    the stream still running earlier steps (the staging ring lets the host run
+    several steps ahead): the host waits for the side copy and the kernels go in
+    with no stream wait.  Outputs, pools and staged tables equal those of steps
+    that read the tables in place."""
     from paged_kv_cache_385_amd import DecodeBatch
     from workloads import new_token_kv
     steps = 6
