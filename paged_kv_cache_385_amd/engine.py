@@ -71,6 +71,13 @@ class _CompletionMarks:
         self._marks = []          # (step, event), oldest first
         self._spare = []
 
+    def prime(self, n: int) -> None:
+        """Make and record ``n`` spare events now (an event's first record creates it)."""
+        for _ in range(n):
+            ev = self._new()
+            self._record(ev)
+            self._spare.append(ev)
+
     def after(self, i: int) -> None:
         if i % self.every == self.every - 1:
             ev = self._spare.pop() if self._spare else self._new()
@@ -325,6 +332,16 @@ class DecodeBatch:
         self.last_grouped = False
         self.last_host_waited = False
         self.last_pairs = np.zeros((0, 2), dtype=np.int32)
+        # First uses cost tens of microseconds each (an event's creation, a buffer's first
+        # copy); take them here rather than in the first pass over the ring.
+        self._marks.prime(3)
+        if mode != "mapped":
+            cs = self._copy_stream if mode == "side" else self.stream
+            with torch.cuda.stream(cs):
+                for i in range(ring):
+                    d = self._dev[i if mode == "side" else 0]
+                    d.copy_(self._pinned[i], non_blocking=True)
+        torch.cuda.synchronize(dev)
 
     def _staged_dev(self) -> torch.Tensor:
         """The device buffer holding the last step's staged values (copied there on

@@ -79,3 +79,21 @@ def test_ring_slots():
         r = _ring_slots(b)
         assert r % 2 == 0 and 2 <= r <= _RING_MAX
         assert r == 2 or r * b <= _RING_BYTES
+
+
+@pytest.mark.parametrize("ring", [2, 4, 16])
+def test_three_primed_events_serve_the_whole_ring(ring):
+    st = _FakeStream()
+    made = []
+
+    def new_event():
+        made.append(st.new_event())
+        return made[-1]
+
+    marks = _CompletionMarks(ring // 2, new_event, st.record, st.sync)
+    marks.prime(3)
+    for i in range(12 * ring):
+        marks.wait(i - ring)
+        st.enqueued = i
+        marks.after(i)
+    assert len(made) == 3
