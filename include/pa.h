@@ -157,8 +157,12 @@ pa_status pa_copy_blocks(const pa_cache* cache, const int32_t* pairs,
  * or 1024 tokens -- the longest for which even the longest possible list of
  * items gives every workgroup slot of the device (three per compute unit) two
  * of them -- else of PA_PARTITION_TOKENS (512) tokens; the size returned
- * covers every choice.  Layout: int32 counters[num_seqs *
- * num_heads] (padded to 256 bytes), then the states.
+ * covers every choice.  Layout: int32 counters[num_seqs * num_heads + 1]
+ * (padded to 256 bytes), then the states.  The last counter hands out the
+ * places of the attention pass's item list beyond the first round of
+ * workgroups: a workgroup that starts later takes the next unclaimed place, so
+ * the items go to whichever slots free first.  When a call is given no
+ * workspace, workgroup i takes place i.
  * The counters must be zero before a workspace's first use (allocate it
  * zero-filled); every completed call leaves them zero.  Returns 0 when
  * max_context_len <= PA_PARTITION_TOKENS (no merge) and for invalid arguments.

@@ -430,7 +430,7 @@ pa_status decode_grouped_run(const char* fn, const pa_cache* cache, const void* 
       return fail(PA_ERR_INVALID_ARG, "%s: plan item %d is malformed", fn, i);
   }
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * max_parts;
-  const size_t counters = round256(static_cast<size_t>(num_seqs) * num_heads * sizeof(int32_t));
+  const size_t counters = pa::decode_counter_bytes(num_seqs, num_heads);
   const size_t need = max_parts > 1 ? counters + round256(rows * sizeof(float2)) + rows * cache->head_dim * sizeof(float) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);

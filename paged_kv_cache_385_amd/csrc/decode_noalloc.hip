@@ -79,8 +79,9 @@ pa_status pa_decode_noalloc(const pa_cache* cache, const void* q, int32_t num_se
     st = pa::decode_check(cache, q, num_seqs, num_heads, max_blocks_per_seq, max_context_len, scale,
                           out, ws, need);
     if (st != PA_OK) return st;
-    // the merge counters start at zero (they lead the scratch, as they lead a workspace)
-    const int64_t words = static_cast<int64_t>(num_seqs) * num_heads;
+    // the merge counters and the claim counter start at zero (they lead the scratch, as
+    // they lead a workspace)
+    const int64_t words = static_cast<int64_t>(num_seqs) * num_heads + 1;
     zero_words_kernel<<<dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0,
                         static_cast<hipStream_t>(stream)>>>(static_cast<uint32_t*>(ws), words);
     st = pa::launch_status(fn);

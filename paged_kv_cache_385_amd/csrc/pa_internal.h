@@ -29,6 +29,9 @@ int32_t bm_tiles_per_block(const pa_bm* bm);
 // Argument checks of pa_decode for a call whose context lengths are at most
 // max_ctx, with a workspace of at least pa_decode_workspace_size(..., max_ctx)
 // bytes; enqueues nothing.
+// Bytes of a decode workspace's leading counter region: the merge counters int32[B][H]
+// and the claim counter after them, all zero between calls.
+size_t decode_counter_bytes(int64_t num_seqs, int64_t num_heads);
 pa_status decode_check(const pa_cache* cache, const void* q, int32_t num_seqs, int32_t num_heads,
                        int32_t max_blocks_per_seq, int32_t max_ctx, float scale, void* out,
                        void* workspace, size_t workspace_bytes);

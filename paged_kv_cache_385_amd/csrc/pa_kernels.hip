@@ -265,6 +265,8 @@ struct DecodeArgs {
   const float* k_scales;       // FP8 pools: [Hkv] scales of K and of V
   const float* v_scales;
   int32_t* counters; // [B][Hkv] partitions finished, or NULL: the merge is a separate launch
+  int32_t* claim;    // list positions handed out so far, or NULL: workgroup i takes position i
+  int32_t claim_base; // workgroups below this id take their id as position (the first round)
   float2* ws_ml;     // [B][H][P] (max in log2 units, sum)
   float* ws_acc;     // [B][H][P][D] unnormalised output
   int32_t num_seqs, num_heads, num_kv_heads, group;
@@ -348,14 +350,17 @@ __device__ __forceinline__ void load_ctx_group(const DecodeArgs& a, int32_t c0, 
 // full partitions first, ordered (KV head group, sequence, partition), then the
 // last, shorter partitions from the largest size class to the smallest, ordered
 // (KV head group, sequence) within a class -- big items start
-// first so the short ones fill the tail.  Workgroup ids are mapped to list
-// positions so that each of the 8 XCDs (which take workgroup ids round-robin)
-// gets 8 consecutive positions out of every 64.  Returns false for a workgroup
+// first so the short ones fill the tail.  Workgroup i takes list position i: the
+// 8 XCDs take workgroup ids in turn, so each XCD gets every 8th item of the
+// size-ordered list and about an eighth of the bytes.  (Giving each XCD 8
+// consecutive positions of every 64 instead left half of them 10% more bytes on
+// the 70B-shaped layer, and its pass ended with the slowest.)  Returns false for a workgroup
 // beyond the list (the launch is sized for the longest possible list).  Every
 // lane of every wave computes the same answer from the context lengths; the
 // item's context length comes back in *octx.
-__device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_t* okvh,
-                          int32_t* op, int32_t* octx) {
+template <class PosFn>
+__device__ bool plan_item(const DecodeArgs& a, int32_t lane, PosFn list_position, int32_t* ob,
+                          int32_t* okvh, int32_t* op, int32_t* octx) {
   const int32_t B = a.num_seqs, pbs = a.part_shift, hkv = a.head_groups;
   constexpr int32_t kGroup = 64 * kPlanChunks;
   int32_t cv0[kPlanChunks];            // the first group, kept for the second pass
@@ -385,9 +390,8 @@ __device__ bool plan_item(const DecodeArgs& a, int32_t lane, int32_t* ob, int32_
   }
   const int32_t n_full = nfull_tot * hkv;
   const int32_t n_items = n_full + n_part * hkv;
-  int32_t i = blockIdx.x;
+  const int32_t i = list_position();
   if (i >= n_items) return false;
-  if (i < (n_items & ~63)) i = (i & ~63) | ((i & 7) << 3) | ((i >> 3) & 7);
 
   // Second pass: find the item's sequence.  In the full-partition part the
   // target is the j-th full partition in sequence order; in the class part, the
@@ -480,8 +484,30 @@ void decode_attn_kernel(DecodeArgs a) {
   const int32_t lane = tid & 63;
   [[maybe_unused]] uint64_t t_entry = 0, t_plan = 0, t_first = 0, t_loop = 0;
   TL_STAMP(t_entry);
+  // The workgroup's place in the item list.  The first round (ids below claim_base, one
+  // per workgroup slot of the device) takes its id; a later workgroup, with a claim
+  // counter, takes the next unclaimed place after them, so that whichever slot frees
+  // first (on whichever XCD) takes the next-largest item.  The claim is issued before
+  // the plan's loads and waited for after them; the workgroup that takes the last place
+  // resets the counter.
+  __shared__ int32_t s_pos;
+  const int32_t base = a.claim_base;
+  const bool claims = a.claim != nullptr && static_cast<int32_t>(blockIdx.x) >= base;
+  int32_t claimed = 0;
+  if (claims && tid == 0)
+    claimed = __hip_atomic_fetch_add(a.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto list_position = [&]() -> int32_t {
+    if (!claims) return static_cast<int32_t>(blockIdx.x);
+    if (tid == 0) {
+      s_pos = base + claimed;
+      if (claimed == static_cast<int32_t>(gridDim.x) - base - 1)
+        __hip_atomic_store(a.claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return s_pos;
+  };
   int32_t b, kg, p, ctx;
-  if (!plan_item(a, lane, &b, &kg, &p, &ctx)) return;
+  if (!plan_item(a, lane, list_position, &b, &kg, &p, &ctx)) return;
   TL_STAMP(t_plan);
   b = __builtin_amdgcn_readfirstlane(b);
   kg = __builtin_amdgcn_readfirstlane(kg);
@@ -1016,6 +1042,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
 
 namespace pa {
 
+size_t decode_counter_bytes(int64_t num_seqs, int64_t num_heads) {
+  return ((static_cast<size_t>(num_seqs) * num_heads + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
 // Compute units of the current device (queried once per device).
 int32_t device_cus() {
   static std::atomic<int32_t> cached[64];
@@ -1116,9 +1146,10 @@ int32_t heads_shift_for(int32_t num_seqs, int32_t num_kv_heads, int32_t group, b
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t ws_ml_bytes(int64_t rows) { return round256(static_cast<size_t>(rows) * sizeof(float2)); }
-// Workspace: counters int32[B][H] (zero between calls) | (max, sum) float2[rows] | acc float[rows][D]
+// Workspace: counters int32[B][H] and the claim counter (zero between calls) |
+// (max, sum) float2[rows] | acc float[rows][D]
 size_t ws_counter_bytes(int64_t num_seqs, int64_t num_heads) {
-  return round256(static_cast<size_t>(num_seqs) * num_heads * sizeof(int32_t));
+  return pa::decode_counter_bytes(num_seqs, num_heads);
 }
 // The merge runs inside the attention pass when a sequence has at most this many partitions.
 constexpr int32_t kMaxFusedParts = 8;
@@ -1203,6 +1234,13 @@ pa_status prepare_decode(const char* fn, const pa_cache* cache, const void* q, i
   a.v_new = nullptr;
   a.new_slots = nullptr;
   a.counters = nullptr;
+  // the claim counter follows the merge counters ([B][H] words) in the counter region
+  a.claim = workspace && workspace_bytes >= ws_counter_bytes(num_seqs, num_heads)
+                ? static_cast<int32_t*>(workspace) + static_cast<int64_t>(num_seqs) * num_heads
+                : nullptr;
+  // workgroup slots of the device: two per CU on 16-bit pools at head dim 128, else three
+  const bool pad = (cache->flags & PA_CACHE_FP8) == 0 && cache->head_dim == 128;
+  a.claim_base = (pad ? 2 : 3) * device_cus();
   char* wsb = static_cast<char*>(workspace) + ws_counter_bytes(num_seqs, num_heads);
   a.ws_ml = need ? reinterpret_cast<float2*>(wsb) : nullptr;
   a.ws_acc = need ? reinterpret_cast<float*>(wsb + ws_ml_bytes(rows)) : nullptr;

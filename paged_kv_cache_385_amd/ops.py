@@ -172,8 +172,9 @@ def alloc_workspace(num_seqs, num_heads, head_dim, max_context_len, device="cuda
 
 
 def workspace_counter_bytes(num_seqs: int, num_heads: int) -> int:
-    """Bytes of the workspace's leading counter region (kept zero between calls)."""
-    return (4 * num_seqs * num_heads + 255) // 256 * 256
+    """Bytes of the workspace's leading counter region (kept zero between calls): the
+    merge counters int32[B][H] and one claim counter."""
+    return (4 * (num_seqs * num_heads + 1) + 255) // 256 * 256
 
 
 def _decode_args(k_cache, v_cache, q, block_tables, context_lens, out, workspace,
