@@ -192,15 +192,20 @@ def test_chunk_call_validation():
 
 
 def test_workspace_size():
+    from paged_kv_cache_385_amd.ops import workspace_counter_bytes
     lib = N.lib()
     assert lib.pa_decode_workspace_size(8, 32, 128, 512) == 0          # one partition: no merge
     assert lib.pa_decode_workspace_size(0, 32, 128, 4096) == 0
     for B, H, D, mc in ((8, 32, 128, 131072), (128, 64, 128, 4096), (3, 5, 64, 513)):
         P = -(-mc // 512)
         n = lib.pa_decode_workspace_size(B, H, D, mc)
-        counters = -(-4 * B * H // 256) * 256                        # zeroed counter region
-        assert n >= counters + B * H * P * (D + 2) * 4               # counters and states fit
-        assert n < counters + B * H * P * (D + 2) * 4 + 512
+        # zeroed counter region: B x H merge counters, then the claim counter
+        counters = -(-4 * (B * H + 1) // 256) * 256
+        rows = B * H * P
+        assert n == counters + -(-8 * rows // 256) * 256 + 4 * rows * D
+        assert workspace_counter_bytes(B, H) == counters >= 4 * (B * H + 1)
+    # a batch whose merge counters fill the padded region exactly still gets the claim word
+    assert workspace_counter_bytes(128, 64) == 4 * 128 * 64 + 256
 
 
 # ---- native block manager vs the oracle's -------------------------------------------------
