@@ -60,14 +60,16 @@ class _CompletionMarks:
     ``wait(j)`` returns once the kernels of step j (and of every step before it on the
     stream) have finished: it waits for the first mark at or after step j, which a
     ring of 2 * every slots always holds before the slot of step j is reused, and
-    recycles the older marks' events.  ``new_event`` makes an event and ``sync`` waits
-    for one (host side); both are plain callables so the bookkeeping runs without a
-    device.
+    recycles the older marks' events.  A step whose call failed records no mark; when
+    no mark is in range, ``wait`` drains the stream instead (``drain``).  ``new_event``
+    makes an event, ``record`` records one on the stream, ``sync`` waits for one (host
+    side); all are plain callables so the bookkeeping runs without a device.
     """
 
-    def __init__(self, every: int, new_event: Callable, record: Callable, sync: Callable):
+    def __init__(self, every: int, new_event: Callable, record: Callable, sync: Callable,
+                 drain: Callable):
         self.every = every
-        self._new, self._record, self._sync = new_event, record, sync
+        self._new, self._record, self._sync, self._drain = new_event, record, sync, drain
         self._marks = []          # (step, event), oldest first
         self._spare = []
 
@@ -90,9 +92,11 @@ class _CompletionMarks:
         k = 0
         while k < len(self._marks) and self._marks[k][0] < j:
             k += 1
-        if k == len(self._marks):
-            raise RuntimeError(f"no completion mark at or after step {j}")
         self._spare.extend(ev for _, ev in self._marks[:k])
+        if k == len(self._marks):
+            del self._marks[:]
+            self._drain()
+            return
         del self._marks[:k]
         self._sync(self._marks[0][1])
 
@@ -299,7 +303,7 @@ class DecodeBatch:
                             for _ in range(ring)]
         self._pinned = [self._aligned(t) for t in self._pinned_raw]
         self._marks = _CompletionMarks(ring // 2, torch.cuda.Event, lambda e: e.record(self.stream),
-                                       lambda e: e.synchronize())
+                                       lambda e: e.synchronize(), lambda: self.stream.synchronize())
         n_dev = ring if mode == "side" else 1
         self._dev_raw = [torch.empty(self._bytes + _ALIGN, dtype=torch.uint8, device=dev)
                          for _ in range(n_dev)]

@@ -17,6 +17,7 @@ class _FakeStream:
         self.enqueued = -1        # last step whose kernels are on the stream
         self.finished = -1        # last step known finished on the host
         self.records = 0
+        self.drains = 0
 
     def new_event(self):
         return {"step": None}
@@ -29,11 +30,15 @@ class _FakeStream:
         assert ev["step"] is not None, "wait on an event that was never recorded"
         self.finished = max(self.finished, ev["step"])
 
+    def drain(self):
+        self.drains += 1
+        self.finished = self.enqueued
+
 
 @pytest.mark.parametrize("ring", [2, 4, 8, 16])
 def test_every_reused_slot_waits_for_its_last_reader(ring):
     st = _FakeStream()
-    marks = _CompletionMarks(ring // 2, st.new_event, st.record, st.sync)
+    marks = _CompletionMarks(ring // 2, st.new_event, st.record, st.sync, st.drain)
     steps = 10 * ring + 3
     for i in range(steps):
         marks.wait(i - ring)
@@ -51,7 +56,7 @@ def test_every_reused_slot_waits_for_its_last_reader(ring):
 
 def test_first_ring_of_steps_waits_for_nothing():
     st = _FakeStream()
-    marks = _CompletionMarks(4, st.new_event, st.record, st.sync)
+    marks = _CompletionMarks(4, st.new_event, st.record, st.sync, st.drain)
     for i in range(8):
         marks.wait(i - 8)
         st.enqueued = i
@@ -59,14 +64,29 @@ def test_first_ring_of_steps_waits_for_nothing():
     assert st.finished == -1
 
 
-def test_a_wait_with_no_mark_in_range_is_an_error():
+def test_a_wait_with_no_mark_in_range_drains_the_stream():
     st = _FakeStream()
-    marks = _CompletionMarks(4, st.new_event, st.record, st.sync)
+    marks = _CompletionMarks(4, st.new_event, st.record, st.sync, st.drain)
     for i in range(3):              # no step reached i % 4 == 3
         st.enqueued = i
         marks.after(i)
-    with pytest.raises(RuntimeError):
-        marks.wait(0)
+    marks.wait(0)
+    assert st.drains == 1 and st.finished == 2
+
+
+@pytest.mark.parametrize("failed", [3, 7, 8])
+def test_a_failed_step_records_no_mark_and_the_ring_still_waits_enough(failed):
+    ring = 8
+    st = _FakeStream()
+    marks = _CompletionMarks(ring // 2, st.new_event, st.record, st.sync, st.drain)
+    for i in range(6 * ring):
+        marks.wait(i - ring)
+        if i >= ring:
+            assert st.finished >= i - ring
+        if i == failed:
+            continue                # the step's call raised: nothing queued, no mark
+        st.enqueued = i
+        marks.after(i)
 
 
 def test_ring_slots():
@@ -90,7 +110,7 @@ def test_three_primed_events_serve_the_whole_ring(ring):
         made.append(st.new_event())
         return made[-1]
 
-    marks = _CompletionMarks(ring // 2, new_event, st.record, st.sync)
+    marks = _CompletionMarks(ring // 2, new_event, st.record, st.sync, st.drain)
     marks.prime(3)
     for i in range(12 * ring):
         marks.wait(i - ring)
